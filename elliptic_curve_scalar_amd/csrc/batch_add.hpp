@@ -1,0 +1,91 @@
+// S affine additions that share one field inversion (Montgomery's trick).
+//
+// aztec-packages PR #23738 ("TL;DR") and PR #23736 ("Goal & lever") describe the
+// bucket accumulate as S affine adds per batch with one inversion, so the
+// inversion costs |inversion| / S per add. PR #23520 ("Summary") gives the three
+// passes over the S slots: a forward pass that stores each slot's prefix product,
+// one inversion, and a backward pass that peels one slot's inverse off the running
+// inverse at a time. This is that batch for one gfx950 lane:
+//
+//   forward:  d_s = denominator of slot s, pref_s = d_0 * ... * d_s
+//   invert:   inv = pref_{S-1}^{-1}
+//   backward: for s = S-1 .. 0:  1/d_s = inv * pref_{s-1} (inv itself for s = 0),
+//             then inv = inv * d_s; lambda = numerator_s / d_s; finish the add.
+//
+// Slot state lives in VGPRs: pref_s (8 words per slot) and the operands' element
+// indices; operands are re-read in the backward pass instead of being held.
+//
+// Special cases (the pages only report that x-collisions break an affine add,
+// PR #23736 "Correctness-harness fix"; the handling below is this library's):
+//   A = inf -> B;  B = inf -> A;  x_A != x_B -> chord, d = x_B - x_A;
+//   A == B -> tangent, d = 2 y_A, numerator 3 x_A^2;  A == -B -> inf.
+// Every special slot uses d = 1, so the batch product is never zero (BN254 G1 has
+// no point with y = 0).
+#pragma once
+#include "ec.hpp"
+
+namespace msmk {
+
+enum : int { ADD_CHORD = 0, ADD_A_INF = 1, ADD_B_INF = 2, ADD_TANGENT = 3, ADD_CANCEL = 4 };
+
+__device__ __forceinline__ int add_case(const aff& A, const aff& B) {
+  if (aff_is_inf(A)) return ADD_A_INF;
+  if (aff_is_inf(B)) return ADD_B_INF;
+  if (!fp_eq(A.x, B.x)) return ADD_CHORD;
+  return fp_eq(A.y, B.y) ? ADD_TANGENT : ADD_CANCEL;
+}
+
+__device__ __forceinline__ fp add_denominator(const aff& A, const aff& B, int cs) {
+  if (cs == ADD_CHORD) return fp_sub(B.x, A.x);
+  if (cs == ADD_TANGENT) return fp_dbl(A.y);
+  return fp_one();
+}
+
+// Finish slot s once 1/d is known.
+__device__ __forceinline__ aff add_finish(const aff& A, const aff& B, int cs, const fp& inv_d) {
+  if (cs == ADD_A_INF) return B;
+  if (cs == ADD_B_INF) return A;
+  if (cs == ADD_CANCEL) return aff_inf();
+  fp num;
+  if (cs == ADD_CHORD) {
+    num = fp_sub(B.y, A.y);
+  } else {
+    fp xx = fp_sqr(A.x);
+    num = fp_add(fp_dbl(xx), xx);
+  }
+  fp lam = fp_mul(num, inv_d);
+  aff r;
+  r.x = fp_sub(fp_sub(fp_sqr(lam), A.x), B.x);
+  r.y = fp_sub(fp_mul(lam, fp_sub(A.x, r.x)), A.y);
+  return r;
+}
+
+// Src supplies: aff a(int s), aff b(int s), void put(int s, const aff&).
+// Slots s >= cnt are idle (d = 1, nothing stored).
+template <int S, class Src>
+__device__ __forceinline__ void batch_affine_add(Src& src, int cnt) {
+  fp pref[S];
+  fp acc = fp_one();
+#pragma unroll
+  for (int s = 0; s < S; s++) {
+    if (s < cnt) {
+      aff A = src.a(s), B = src.b(s);
+      fp d = add_denominator(A, B, add_case(A, B));
+      acc = (s == 0) ? d : fp_mul(acc, d);
+    }
+    pref[s] = acc;
+  }
+  fp inv = fp_inv(acc);
+#pragma unroll
+  for (int s = S - 1; s >= 0; s--) {
+    if (s < cnt) {
+      fp inv_d = (s > 0) ? fp_mul(inv, pref[s - 1]) : inv;
+      aff A = src.a(s), B = src.b(s);
+      int cs = add_case(A, B);
+      inv = fp_mul(inv, add_denominator(A, B, cs));
+      src.put(s, add_finish(A, B, cs, inv_d));
+    }
+  }
+}
+
+}  // namespace msmk

@@ -1,0 +1,201 @@
+// BN254 base field F_p on gfx950: 256-bit Montgomery arithmetic on 32-bit limbs.
+//
+// The multi-scalar multiplication of aztec-packages PR #23738 / #23736 / #23520
+// ("bb/msm") spends its accumulate time in Montgomery products and a field
+// inversion per batch (PR #23520, "Measurements": compute-bound on the inverse and
+// the Montgomery products). This header is that arithmetic for CDNA4:
+//
+//   * an element is eight little-endian 32-bit limbs holding x * 2^256 mod p
+//     (Montgomery form, R = 2^256), the same bytes as the library's interchange
+//     format, always fully reduced (< p) between operations;
+//   * the product is coarsely integrated operand scanning with 32x32->64
+//     multiply-adds (v_mad_u64_u32 on gfx950); p < 2^254 keeps every partial sum
+//     inside 288 bits, and the result before the final subtraction is below 2p;
+//   * the inverse is Fermat's x^(p-2) by binary square-and-multiply.
+//
+// Everything is branch-free except where noted, so a wavefront never diverges on
+// field values.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msmk {
+
+struct fp {
+  uint32_t v[8];
+};
+
+// p = 0x30644e72e131a029b85045b68181585d97816a916871ca8d3c208c16d87cfd47 (EIP-196).
+#define MSM_P0 0xd87cfd47u
+#define MSM_P1 0x3c208c16u
+#define MSM_P2 0x6871ca8du
+#define MSM_P3 0x97816a91u
+#define MSM_P4 0x8181585du
+#define MSM_P5 0xb85045b6u
+#define MSM_P6 0xe131a029u
+#define MSM_P7 0x30644e72u
+// -p^{-1} mod 2^32
+#define MSM_PINV 0xe4866389u
+
+__device__ __forceinline__ uint32_t p_limb(int i) {
+  switch (i) {
+    case 0: return MSM_P0;
+    case 1: return MSM_P1;
+    case 2: return MSM_P2;
+    case 3: return MSM_P3;
+    case 4: return MSM_P4;
+    case 5: return MSM_P5;
+    case 6: return MSM_P6;
+    default: return MSM_P7;
+  }
+}
+
+__device__ __forceinline__ fp fp_zero() {
+  fp r;
+#pragma unroll
+  for (int i = 0; i < 8; i++) r.v[i] = 0;
+  return r;
+}
+
+// 2^256 mod p: the Montgomery form of 1.
+__device__ __forceinline__ fp fp_one() {
+  fp r;
+  r.v[0] = 0xc58f0d9du; r.v[1] = 0xd35d438du; r.v[2] = 0xf5c70b3du; r.v[3] = 0x0a78eb28u;
+  r.v[4] = 0x7879462cu; r.v[5] = 0x666ea36fu; r.v[6] = 0x9a07df2fu; r.v[7] = 0x0e0a77c1u;
+  return r;
+}
+
+// 2^512 mod p: multiplying by it converts a plain integer into Montgomery form.
+__device__ __forceinline__ fp fp_r2() {
+  fp r;
+  r.v[0] = 0x538afa89u; r.v[1] = 0xf32cfc5bu; r.v[2] = 0xd44501fbu; r.v[3] = 0xb5e71911u;
+  r.v[4] = 0x0a417ff6u; r.v[5] = 0x47ab1effu; r.v[6] = 0xcab8351fu; r.v[7] = 0x06d89f71u;
+  return r;
+}
+
+__device__ __forceinline__ bool fp_is_zero(const fp& a) {
+  uint32_t x = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) x |= a.v[i];
+  return x == 0;
+}
+
+__device__ __forceinline__ bool fp_eq(const fp& a, const fp& b) {
+  uint32_t x = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) x |= a.v[i] ^ b.v[i];
+  return x == 0;
+}
+
+// r = t - p if t >= p else t, for t < 2^256 given as 8 limbs.
+__device__ __forceinline__ fp fp_reduce_once(const fp& t) {
+  fp d;
+  uint32_t borrow = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    uint64_t s = (uint64_t)t.v[i] - p_limb(i) - borrow;
+    d.v[i] = (uint32_t)s;
+    borrow = (uint32_t)(s >> 63);
+  }
+  fp r;
+#pragma unroll
+  for (int i = 0; i < 8; i++) r.v[i] = borrow ? t.v[i] : d.v[i];
+  return r;
+}
+
+__device__ __forceinline__ fp fp_add(const fp& a, const fp& b) {
+  fp s;
+  uint32_t carry = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    uint64_t t = (uint64_t)a.v[i] + b.v[i] + carry;
+    s.v[i] = (uint32_t)t;
+    carry = (uint32_t)(t >> 32);
+  }
+  // a, b < p < 2^254: the sum is below 2^255, so no carry leaves limb 7.
+  return fp_reduce_once(s);
+}
+
+__device__ __forceinline__ fp fp_sub(const fp& a, const fp& b) {
+  fp d;
+  uint32_t borrow = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    uint64_t t = (uint64_t)a.v[i] - b.v[i] - borrow;
+    d.v[i] = (uint32_t)t;
+    borrow = (uint32_t)(t >> 63);
+  }
+  // a < b: add p back (masked, branch-free)
+  uint32_t mask = 0u - borrow;
+  uint32_t carry = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    uint64_t t = (uint64_t)d.v[i] + (p_limb(i) & mask) + carry;
+    d.v[i] = (uint32_t)t;
+    carry = (uint32_t)(t >> 32);
+  }
+  return d;
+}
+
+__device__ __forceinline__ fp fp_neg(const fp& a) { return fp_sub(fp_zero(), a); }
+
+__device__ __forceinline__ fp fp_dbl(const fp& a) { return fp_add(a, a); }
+
+// Montgomery product a * b * 2^-256 mod p (CIOS, 32-bit limbs).
+__device__ __forceinline__ fp fp_mul(const fp& a, const fp& b) {
+  uint32_t t[9];
+#pragma unroll
+  for (int j = 0; j < 9; j++) t[j] = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    uint64_t c = 0;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      c = (uint64_t)a.v[j] * b.v[i] + t[j] + (c >> 32);
+      t[j] = (uint32_t)c;
+    }
+    uint64_t top = (uint64_t)t[8] + (c >> 32);
+    t[8] = (uint32_t)top;
+    // t < 2^288 here; with p < 2^254 the running value stays below 2p * 2^32,
+    // so the word above t[8] is always zero.
+    uint32_t m = t[0] * MSM_PINV;
+    c = (uint64_t)m * p_limb(0) + t[0];
+#pragma unroll
+    for (int j = 1; j < 8; j++) {
+      c = (uint64_t)m * p_limb(j) + t[j] + (c >> 32);
+      t[j - 1] = (uint32_t)c;
+    }
+    top = (uint64_t)t[8] + (c >> 32);
+    t[7] = (uint32_t)top;
+    t[8] = (uint32_t)(top >> 32);
+  }
+  fp r;
+#pragma unroll
+  for (int j = 0; j < 8; j++) r.v[j] = t[j];
+  // inputs < p give t < 2p < 2^255, so t[8] == 0
+  return fp_reduce_once(r);
+}
+
+__device__ __forceinline__ fp fp_sqr(const fp& a) { return fp_mul(a, a); }
+
+// Small constant c (< 2^32) in Montgomery form.
+__device__ __forceinline__ fp fp_from_u32(uint32_t c) {
+  fp x = fp_zero();
+  x.v[0] = c;
+  return fp_mul(x, fp_r2());
+}
+
+// x^(p-2) mod p, the inverse of a non-zero x (0 maps to 0): left-to-right binary
+// square-and-multiply. The exponent is the same for every lane, so the multiply
+// branch is uniform across the wavefront.
+__device__ __forceinline__ fp fp_inv(const fp& x) {
+  const uint32_t e[8] = {MSM_P0 - 2u, MSM_P1, MSM_P2, MSM_P3, MSM_P4, MSM_P5, MSM_P6, MSM_P7};
+  fp acc = x;  // the exponent's top bit (bit 253) is set
+  for (int bit = 252; bit >= 0; bit--) {
+    acc = fp_sqr(acc);
+    if ((e[bit >> 5] >> (bit & 31)) & 1u) acc = fp_mul(acc, x);
+  }
+  return acc;
+}
+
+}  // namespace msmk

@@ -1,0 +1,374 @@
+// C ABI of libmsm (declared in include/msm.h): argument checks, workspace layout,
+// the host side of the pipeline, and error reporting.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <new>
+#include <vector>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/msm.h"
+#include "msm_internal.hpp"
+
+using namespace msmk;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, const char* detail = "") {
+  snprintf(g_err, sizeof g_err, fmt, detail);
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                   \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess) return fail(MSM_ERR_HIP, "HIP error: %s (" #expr ")", hipGetErrorString(e_)); \
+  } while (0)
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int num_windows(int c) { return (254 + c - 1) / c; }
+
+// Buckets per running-sum segment: enough segments to spread the reduction over the
+// chip, never fewer than 4 buckets per segment.
+uint32_t segment_length(int c, int nwin) {
+  size_t total = ((size_t)nwin) << c;
+  uint32_t g = 4;
+  while ((size_t)g * 32768 < total && g < 256) g <<= 1;
+  if (g > (1u << c)) g = 1u << c;
+  return g;
+}
+
+struct Layout {
+  size_t stats, counts, offsets, cursor, poff, block_sums, sorted_idx, lvl_a, lvl_b, bsum, seg, win;
+  size_t total;
+  uint32_t K, nwin, seg_len, nseg;
+  size_t E_max;
+};
+
+Layout plan(size_t n, int c) {
+  Layout L;
+  L.nwin = (uint32_t)num_windows(c);
+  L.K = L.nwin << c;
+  L.seg_len = segment_length(c, (int)L.nwin);
+  L.nseg = ((1u << c) + L.seg_len - 1) / L.seg_len;
+  L.E_max = n * L.nwin;
+  size_t nb = (L.K + SCAN_TILE - 1) / SCAN_TILE + 1;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align_up(off + (bytes ? bytes : 1), 256);
+    return at;
+  };
+  L.stats = take(sizeof(msm_stats));
+  L.counts = take((size_t)L.K * 4);
+  L.offsets = take(((size_t)L.K + 1) * 4);
+  L.cursor = take((size_t)L.K * 4);
+  L.poff = take(((size_t)L.K + 1) * 4);
+  L.block_sums = take((nb + 1) * 4);
+  L.sorted_idx = take(L.E_max * 4);
+  L.lvl_a = take(L.E_max * sizeof(g1a));
+  L.lvl_b = take(L.E_max * sizeof(g1a));
+  L.bsum = take((size_t)L.K * sizeof(g1a));
+  L.seg = take((size_t)L.nwin * L.nseg * sizeof(xyzz_st));
+  L.win = take((size_t)L.nwin * sizeof(xyzz_st));
+  L.total = off;
+  return L;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_run_args(const msm_g1_affine* pts, const uint32_t* sc, size_t n, int c, int S,
+                   const msm_g1_affine* out) {
+  if (c < 1 || c > 16) return fail(MSM_ERR_ARG, "window c must be in 1..16%s");
+  if (S != 4 && S != 8 && S != 16 && S != 32) return fail(MSM_ERR_ARG, "S must be 4, 8, 16 or 32%s");
+  if (n > MSM_MAX_N) return fail(MSM_ERR_ARG, "n exceeds MSM_MAX_N%s");
+  if (!out) return fail(MSM_ERR_ARG, "d_out is NULL%s");
+  if (n && (!pts || !sc)) return fail(MSM_ERR_ARG, "points or scalars pointer is NULL%s");
+  if (!aligned(pts, 16) || !aligned(sc, 16) || !aligned(out, 16))
+    return fail(MSM_ERR_ARG, "points, scalars and d_out must be 16-byte aligned%s");
+  return MSM_OK;
+}
+
+}  // namespace
+
+enum Phase { PH_SORT = 0, PH_ACCUM = 1, PH_LEVEL = 2, PH_REDUCE = 3, PH_FINAL = 4 };
+
+struct Span {
+  int phase;
+  size_t e0, e1;
+};
+
+struct msm_ctx {
+  int device = 0;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  msm_stats* host_stats = nullptr;  // pinned
+  // phase timing
+  bool timing = false;
+  std::vector<hipEvent_t> events;
+  size_t ev_used = 0;
+  std::vector<Span> spans;
+  int runs = 0, level_launches = 0;
+  uint64_t level_pairs = 0, level_lanes = 0;
+};
+
+namespace {
+
+// Record an event on the stream; returns its index, or SIZE_MAX on failure.
+size_t mark(msm_ctx* ctx, hipStream_t st) {
+  if (ctx->ev_used == ctx->events.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return SIZE_MAX;
+    ctx->events.push_back(e);
+  }
+  size_t i = ctx->ev_used++;
+  if (hipEventRecord(ctx->events[i], st) != hipSuccess) return SIZE_MAX;
+  return i;
+}
+
+struct PhaseMark {
+  msm_ctx* ctx;
+  hipStream_t st;
+  int phase;
+  size_t e0 = SIZE_MAX;
+  PhaseMark(msm_ctx* c, hipStream_t s, int ph) : ctx(c), st(s), phase(ph) {
+    if (ctx->timing) e0 = mark(ctx, st);
+  }
+  void end() {
+    if (ctx->timing && e0 != SIZE_MAX) {
+      size_t e1 = mark(ctx, st);
+      if (e1 != SIZE_MAX) ctx->spans.push_back({phase, e0, e1});
+    }
+    e0 = SIZE_MAX;
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+int msm_version(void) { return 100; }
+
+const char* msm_last_error(void) { return g_err; }
+
+size_t msm_workspace_bytes(size_t n, int c, int S) {
+  (void)S;
+  if (c < 1 || c > 16 || n > MSM_MAX_N) return 0;
+  return plan(n, c).total;
+}
+
+int msm_ctx_create(int device, msm_ctx** out) {
+  if (!out) return fail(MSM_ERR_ARG, "out is NULL%s");
+  *out = nullptr;
+  int ndev = 0;
+  HIP_TRY(hipGetDeviceCount(&ndev));
+  if (device < 0 || device >= ndev) return fail(MSM_ERR_ARG, "no such device%s");
+  msm_ctx* ctx = new (std::nothrow) msm_ctx;
+  if (!ctx) return fail(MSM_ERR_OOM, "host allocation failed%s");
+  ctx->device = device;
+  HIP_TRY(hipSetDevice(device));
+  if (hipHostMalloc((void**)&ctx->host_stats, sizeof(msm_stats), hipHostMallocDefault) != hipSuccess) {
+    delete ctx;
+    return fail(MSM_ERR_OOM, "pinned host allocation failed%s");
+  }
+  *out = ctx;
+  return MSM_OK;
+}
+
+void msm_ctx_destroy(msm_ctx* ctx) {
+  if (!ctx) return;
+  (void)hipSetDevice(ctx->device);
+  for (hipEvent_t e : ctx->events) (void)hipEventDestroy(e);
+  if (ctx->ws) (void)hipFree(ctx->ws);
+  if (ctx->host_stats) (void)hipHostFree(ctx->host_stats);
+  delete ctx;
+}
+
+int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scalars, size_t n,
+            int c, int S, void* d_workspace, size_t workspace_bytes, void* stream,
+            msm_g1_affine* d_out) {
+  if (!ctx) return fail(MSM_ERR_ARG, "ctx is NULL%s");
+  int rc = check_run_args(d_points, d_scalars, n, c, S, d_out);
+  if (rc) return rc;
+  Layout L = plan(n, c);
+  if (d_workspace && (workspace_bytes < L.total || !aligned(d_workspace, 256)))
+    return fail(MSM_ERR_ARG, "workspace smaller than msm_workspace_bytes() or not 256-byte aligned%s");
+  hipStream_t st = (hipStream_t)stream;
+  HIP_TRY(hipSetDevice(ctx->device));
+  if (n == 0) {
+    HIP_TRY(hipMemsetAsync(d_out, 0, sizeof(msm_g1_affine), st));
+    return MSM_OK;
+  }
+  char* ws = (char*)d_workspace;
+  if (!ws) {
+    if (ctx->ws_bytes < L.total) {
+      if (ctx->ws) {
+        HIP_TRY(hipStreamSynchronize(st));
+        HIP_TRY(hipFree(ctx->ws));
+        ctx->ws = nullptr;
+        ctx->ws_bytes = 0;
+      }
+      if (hipMalloc(&ctx->ws, L.total) != hipSuccess) {
+        ctx->ws = nullptr;
+        return fail(MSM_ERR_OOM, "workspace allocation failed%s");
+      }
+      ctx->ws_bytes = L.total;
+    }
+    ws = (char*)ctx->ws;
+  }
+  msm_stats* stats = (msm_stats*)(ws + L.stats);
+  uint32_t* counts = (uint32_t*)(ws + L.counts);
+  uint32_t* offsets = (uint32_t*)(ws + L.offsets);
+  uint32_t* cursor = (uint32_t*)(ws + L.cursor);
+  uint32_t* poff = (uint32_t*)(ws + L.poff);
+  uint32_t* block_sums = (uint32_t*)(ws + L.block_sums);
+  uint32_t* sorted_idx = (uint32_t*)(ws + L.sorted_idx);
+  g1a* lvl[2] = {(g1a*)(ws + L.lvl_a), (g1a*)(ws + L.lvl_b)};
+  g1a* bsum = (g1a*)(ws + L.bsum);
+  xyzz_st* seg = (xyzz_st*)(ws + L.seg);
+  xyzz_st* win = (xyzz_st*)(ws + L.win);
+  const g1a* pts = (const g1a*)d_points;
+  uint32_t n32 = (uint32_t)n, c32 = (uint32_t)c;
+
+  // decompose + count, offsets, plan, scatter
+  PhaseMark ph_sort(ctx, st, PH_SORT);
+  HIP_TRY(launch_fill((uint32_t*)stats, sizeof(msm_stats) / 4, 0, st));
+  HIP_TRY(launch_fill(counts, L.K, 0, st));
+  HIP_TRY(launch_hist(d_scalars, n32, c32, L.nwin, counts, stats, st));
+  HIP_TRY(launch_scan(counts, L.K, -1, block_sums, offsets, cursor, st));
+  HIP_TRY(launch_stats(counts, L.K, stats, st));
+  HIP_TRY(launch_scatter(d_scalars, n32, c32, L.nwin, cursor, sorted_idx, st));
+  HIP_TRY(hipMemcpyAsync(ctx->host_stats, stats, sizeof(msm_stats), hipMemcpyDeviceToHost, st));
+  ph_sort.end();
+  HIP_TRY(hipStreamSynchronize(st));
+  const msm_stats hs = *ctx->host_stats;
+  if (hs.range_flag) return fail(MSM_ERR_RANGE, "a scalar has a bit at or above W*c set%s");
+
+  // accumulate: pair-tree levels until every bucket holds one point
+  PhaseMark ph_acc(ctx, st, PH_ACCUM);
+  HIP_TRY(launch_bucket_init(counts, offsets, L.K, sorted_idx, pts, bsum, st));
+  int levels = 0;
+  while (levels < MAX_LEVELS && ((uint64_t)1 << levels) < hs.max_count) levels++;
+  for (int l = 0; l < levels; l++) {
+    uint32_t np = hs.pairs[l];
+    if (np == 0) continue;
+    HIP_TRY(launch_scan(counts, L.K, l, block_sums, poff, nullptr, st));
+    const g1a* in = (l == 0) ? pts : lvl[(l - 1) & 1];
+    const uint32_t* idx = (l == 0) ? sorted_idx : nullptr;
+    PhaseMark ph_lvl(ctx, st, PH_LEVEL);
+    HIP_TRY(launch_level(S, in, idx, lvl[l & 1], bsum, counts, offsets, poff, L.K, np, l, st));
+    ph_lvl.end();
+    if (ctx->timing) {
+      ctx->level_launches++;
+      ctx->level_pairs += np;
+      ctx->level_lanes += (np + S - 1) / S;
+    }
+  }
+  ph_acc.end();
+
+  // running sum per window, window combine
+  PhaseMark ph_red(ctx, st, PH_REDUCE);
+  HIP_TRY(launch_reduce(bsum, c32, L.nwin, L.seg_len, L.nseg, seg, win, st));
+  ph_red.end();
+  PhaseMark ph_fin(ctx, st, PH_FINAL);
+  HIP_TRY(launch_final(win, L.nwin, c32, (g1a*)d_out, st));
+  ph_fin.end();
+  if (ctx->timing) ctx->runs++;
+  return MSM_OK;
+}
+
+int msm_ctx_set_timing(msm_ctx* ctx, int enable) {
+  if (!ctx) return fail(MSM_ERR_ARG, "ctx is NULL%s");
+  ctx->timing = enable != 0;
+  return MSM_OK;
+}
+
+int msm_ctx_timing_read(msm_ctx* ctx, msm_timing* out) {
+  if (!ctx || !out) return fail(MSM_ERR_ARG, "NULL argument%s");
+  memset(out, 0, sizeof *out);
+  HIP_TRY(hipSetDevice(ctx->device));
+  double* slot[5] = {&out->sort_ms, &out->accumulate_ms, &out->level_kernel_ms, &out->reduce_ms,
+                     &out->final_ms};
+  for (const Span& sp : ctx->spans) {
+    HIP_TRY(hipEventSynchronize(ctx->events[sp.e1]));
+    float ms = 0.f;
+    HIP_TRY(hipEventElapsedTime(&ms, ctx->events[sp.e0], ctx->events[sp.e1]));
+    *slot[sp.phase] += ms;
+  }
+  out->runs = ctx->runs;
+  out->level_launches = ctx->level_launches;
+  out->level_pairs = ctx->level_pairs;
+  out->level_lanes = ctx->level_lanes;
+  ctx->spans.clear();
+  ctx->ev_used = 0;
+  ctx->runs = ctx->level_launches = 0;
+  ctx->level_pairs = ctx->level_lanes = 0;
+  return MSM_OK;
+}
+
+int msm(const msm_g1_affine* d_points, const uint32_t* d_scalars, size_t n, int c,
+        msm_g1_affine* h_out) {
+  if (!h_out) return fail(MSM_ERR_ARG, "h_out is NULL%s");
+  int rc = check_run_args(d_points, d_scalars, n, c, 8, (const msm_g1_affine*)16);
+  if (rc) return rc;
+  static std::mutex mu;
+  static msm_ctx* ctxs[64] = {};
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return fail(MSM_ERR_ARG, "device index out of range%s");
+  msm_ctx* ctx;
+  {
+    std::lock_guard<std::mutex> g(mu);
+    if (!ctxs[dev]) {
+      rc = msm_ctx_create(dev, &ctxs[dev]);
+      if (rc) return rc;
+    }
+    ctx = ctxs[dev];
+  }
+  msm_g1_affine* d_out = nullptr;
+  if (hipMalloc(&d_out, sizeof(msm_g1_affine)) != hipSuccess) return fail(MSM_ERR_OOM, "allocation failed%s");
+  std::lock_guard<std::mutex> g(mu);
+  rc = msm_run(ctx, d_points, d_scalars, n, c, 8, nullptr, 0, nullptr, d_out);
+  if (rc == MSM_OK) {
+    hipError_t e = hipMemcpy(h_out, d_out, sizeof(msm_g1_affine), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) rc = fail(MSM_ERR_HIP, "HIP error: %s (copy result)", hipGetErrorString(e));
+  }
+  (void)hipFree(d_out);
+  return rc;
+}
+
+int msm_g1_from_scalars(const uint32_t* d_k, size_t n, msm_g1_affine* d_out, void* stream) {
+  if (n > MSM_MAX_N) return fail(MSM_ERR_ARG, "n exceeds MSM_MAX_N%s");
+  if (n && (!d_k || !d_out)) return fail(MSM_ERR_ARG, "NULL pointer%s");
+  if (!aligned(d_k, 16) || !aligned(d_out, 16)) return fail(MSM_ERR_ARG, "pointers must be 16-byte aligned%s");
+  HIP_TRY(launch_from_scalars(d_k, (uint32_t)n, (g1a*)d_out, (hipStream_t)stream));
+  return MSM_OK;
+}
+
+int msm_test_fp(int op, const uint32_t* d_a, const uint32_t* d_b, uint32_t* d_out, size_t n,
+                void* stream) {
+  if (op < 0 || op > 6) return fail(MSM_ERR_ARG, "op must be in 0..6%s");
+  if (n > MSM_MAX_N) return fail(MSM_ERR_ARG, "n exceeds MSM_MAX_N%s");
+  bool binary = (op <= 2);
+  if (n && (!d_a || !d_out || (binary && !d_b))) return fail(MSM_ERR_ARG, "NULL pointer%s");
+  HIP_TRY(launch_test_fp(op, d_a, binary ? d_b : nullptr, d_out, (uint32_t)n, (hipStream_t)stream));
+  return MSM_OK;
+}
+
+int msm_test_pair_add(const msm_g1_affine* d_a, const msm_g1_affine* d_b, msm_g1_affine* d_out,
+                      size_t n, int S, void* stream) {
+  if (S != 4 && S != 8 && S != 16 && S != 32) return fail(MSM_ERR_ARG, "S must be 4, 8, 16 or 32%s");
+  if (n > MSM_MAX_N) return fail(MSM_ERR_ARG, "n exceeds MSM_MAX_N%s");
+  if (n && (!d_a || !d_b || !d_out)) return fail(MSM_ERR_ARG, "NULL pointer%s");
+  if (!aligned(d_a, 16) || !aligned(d_b, 16) || !aligned(d_out, 16))
+    return fail(MSM_ERR_ARG, "pointers must be 16-byte aligned%s");
+  HIP_TRY(launch_test_pair_add(S, (const g1a*)d_a, (const g1a*)d_b, (g1a*)d_out, (uint32_t)n,
+                               (hipStream_t)stream));
+  return MSM_OK;
+}
+
+}  // extern "C"

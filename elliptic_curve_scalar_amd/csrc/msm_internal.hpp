@@ -1,0 +1,56 @@
+// Internal declarations shared by the kernels and the C-ABI layer of libmsm.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ec.hpp"
+
+namespace msmk {
+
+constexpr int SCAN_ITEMS = 4;                        // counts per thread in a scan tile
+constexpr uint32_t SCAN_TILE = 256 * SCAN_ITEMS;     // counts per scan block
+constexpr int SCAN_TOP_ITEMS = 16;                   // block sums per thread in the top scan
+constexpr uint32_t SCAN_MAX_BLOCKS = 256 * SCAN_TOP_ITEMS;
+constexpr int MAX_LEVELS = 32;                       // pair-tree levels tracked
+constexpr unsigned LEVEL_BLOCK = 128;                // lanes per block in k_level
+constexpr int SEARCH_STEPS = 22;                     // bucket searches cover K < 2^22
+
+// Plan read back to the host after the sort (one 16 + 4 * MAX_LEVELS byte copy).
+struct msm_stats {
+  uint32_t range_flag;          // some scalar has a bit >= W c
+  uint32_t max_count;           // largest bucket
+  uint32_t total;               // bucket entries E (non-zero digits)
+  uint32_t pad;
+  uint32_t pairs[MAX_LEVELS];   // pair adds at pair-tree level l
+};
+
+// XYZZ point as stored in device memory (X, Y, ZZ, ZZZ; 128 bytes).
+struct xyzz_st {
+  uint32_t w[32];
+};
+
+hipError_t launch_fill(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
+hipError_t launch_hist(const uint32_t* scalars, uint32_t n, uint32_t c, uint32_t nwin,
+                       uint32_t* counts, msm_stats* st, hipStream_t s);
+hipError_t launch_scatter(const uint32_t* scalars, uint32_t n, uint32_t c, uint32_t nwin,
+                          uint32_t* cursor, uint32_t* sorted_idx, hipStream_t s);
+hipError_t launch_scan(const uint32_t* counts, uint32_t n, int level, uint32_t* block_sums,
+                       uint32_t* out, uint32_t* out2, hipStream_t s);
+hipError_t launch_stats(const uint32_t* counts, uint32_t K, msm_stats* st, hipStream_t s);
+hipError_t launch_bucket_init(const uint32_t* counts, const uint32_t* offsets, uint32_t K,
+                              const uint32_t* sorted_idx, const g1a* points, g1a* bsum,
+                              hipStream_t s);
+hipError_t launch_level(int S, const g1a* in, const uint32_t* idx, g1a* out, g1a* bsum,
+                        const uint32_t* counts, const uint32_t* offsets, const uint32_t* poff,
+                        uint32_t K, uint32_t npairs, int level, hipStream_t s);
+hipError_t launch_reduce(const g1a* bsum, uint32_t c, uint32_t nwin, uint32_t seg_len,
+                         uint32_t nseg, xyzz_st* seg, xyzz_st* win, hipStream_t s);
+hipError_t launch_final(const xyzz_st* win, uint32_t nwin, uint32_t c, g1a* out, hipStream_t s);
+hipError_t launch_from_scalars(const uint32_t* ks, uint32_t n, g1a* out, hipStream_t s);
+hipError_t launch_test_fp(int op, const uint32_t* a, const uint32_t* b, uint32_t* out, uint32_t n,
+                          hipStream_t s);
+hipError_t launch_test_pair_add(int S, const g1a* a, const g1a* b, g1a* out, uint32_t n,
+                                hipStream_t s);
+
+}  // namespace msmk

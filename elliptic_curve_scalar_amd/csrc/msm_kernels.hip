@@ -1,0 +1,572 @@
+// Device kernels of the BN254 G1 bucket MSM for gfx950, and their launchers.
+//
+// Pipeline (one stream; W = ceil(254 / c) windows, 2^c buckets per window, digit 0
+// dropped since it adds nothing):
+//   k_hist        scalar -> W window digits, per-(window, digit) counts (global atomics)
+//   k_scan_*      exclusive scan of the counts -> bucket offsets (and scatter cursors)
+//   k_stats       largest bucket, number of pair adds at every pair-tree level
+//   k_scatter     point indices into per-bucket lists (sorted_idx)
+//   -- host reads the stats back (one sync) --
+//   k_bucket_init buckets of size 0 / 1 are final at once
+//   k_level<S>    pair-tree level l: pair (2m, 2m+1) of every bucket -> element m,
+//                 S pairs per lane with one inversion (batch_add.hpp)
+//   k_rsum_seg    per window, segments of buckets: sum_b b * B_b by a running sum
+//   k_rsum_win    per window: tree over its segments -> W_j
+//   k_final       Q = sum_j 2^(c j) W_j by doubling (Horner), then affine
+//
+// The method is aztec-packages PR #23738 / #23736 / #23520 ("bb/msm"); its WebGPU
+// kernels are prior art only: the level kernel takes S pairs per lane the way the
+// pages' pair-tree accumulate takes S adds per invocation (PR #23520 "Summary").
+#include <hip/hip_runtime.h>
+
+#include "batch_add.hpp"
+#include "msm_internal.hpp"
+
+namespace msmk {
+
+// ------------------------------------------------------------------ scalars
+struct sc256 {
+  uint32_t w[8];
+};
+
+__device__ __forceinline__ sc256 load_scalar(const uint32_t* s, uint32_t i) {
+  const uint4* q = reinterpret_cast<const uint4*>(s + 8 * (size_t)i);
+  uint4 a = q[0], b = q[1];
+  sc256 r;
+  r.w[0] = a.x; r.w[1] = a.y; r.w[2] = a.z; r.w[3] = a.w;
+  r.w[4] = b.x; r.w[5] = b.y; r.w[6] = b.z; r.w[7] = b.w;
+  return r;
+}
+
+// Bits [bit, bit + c) of s (c <= 16, bit < 256); bits past 255 read as 0.
+__device__ __forceinline__ uint32_t window_digit(const sc256& s, uint32_t bit, uint32_t c) {
+  uint32_t w = bit >> 5, sh = bit & 31u;
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (uint32_t k = 0; k < 8; k++) {
+    lo = (k == w) ? s.w[k] : lo;
+    hi = (k == w + 1) ? s.w[k] : hi;
+  }
+  uint64_t v = ((uint64_t)hi << 32) | lo;
+  return (uint32_t)(v >> sh) & ((1u << c) - 1u);
+}
+
+// Any bit at or above `top` set?
+__device__ __forceinline__ bool above_bits(const sc256& s, uint32_t top) {
+  if (top >= 256) return false;
+  uint32_t acc = 0;
+#pragma unroll
+  for (uint32_t k = 0; k < 8; k++) {
+    uint32_t lo_bit = 32 * k;
+    uint32_t m = (top <= lo_bit) ? 0xffffffffu : (top >= lo_bit + 32 ? 0u : (0xffffffffu << (top - lo_bit)));
+    acc |= s.w[k] & m;
+  }
+  return acc != 0;
+}
+
+__global__ void k_fill_u32(uint32_t* p, size_t n, uint32_t v) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__global__ void __launch_bounds__(256) k_hist(const uint32_t* __restrict__ scalars, uint32_t n,
+                                              uint32_t c, uint32_t nwin,
+                                              uint32_t* __restrict__ counts, msm_stats* st) {
+  uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  sc256 s = load_scalar(scalars, i);
+  if (above_bits(s, nwin * c)) atomicOr(&st->range_flag, 1u);
+  for (uint32_t j = 0; j < nwin; j++) {
+    uint32_t d = window_digit(s, j * c, c);
+    if (d) atomicAdd(&counts[(j << c) | d], 1u);
+  }
+}
+
+__global__ void __launch_bounds__(256) k_scatter(const uint32_t* __restrict__ scalars, uint32_t n,
+                                                 uint32_t c, uint32_t nwin,
+                                                 uint32_t* __restrict__ cursor,
+                                                 uint32_t* __restrict__ sorted_idx) {
+  uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  sc256 s = load_scalar(scalars, i);
+  for (uint32_t j = 0; j < nwin; j++) {
+    uint32_t d = window_digit(s, j * c, c);
+    if (d) {
+      uint32_t pos = atomicAdd(&cursor[(j << c) | d], 1u);
+      sorted_idx[pos] = i;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ scan
+// Value scanned for bucket k: its count (level < 0), or the number of pair adds
+// it has at pair-tree level `level`: floor(ceil(count / 2^level) / 2).
+__device__ __forceinline__ uint32_t level_count(uint32_t cnt, int level) {
+  return (uint32_t)(((uint64_t)cnt + (1ull << level) - 1) >> level);
+}
+
+__device__ __forceinline__ uint32_t scan_value(const uint32_t* counts, uint32_t k, uint32_t n,
+                                               int level) {
+  if (k >= n) return 0;
+  uint32_t c = counts[k];
+  return level < 0 ? c : (level_count(c, level) >> 1);
+}
+
+// Exclusive scan of 256 per-thread values in a block; returns this thread's prefix,
+// *total gets the block sum.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* lds, uint32_t* total) {
+  uint32_t t = threadIdx.x;
+  lds[t] = v;
+  __syncthreads();
+  for (uint32_t off = 1; off < 256; off <<= 1) {
+    uint32_t add = (t >= off) ? lds[t - off] : 0u;
+    __syncthreads();
+    lds[t] += add;
+    __syncthreads();
+  }
+  uint32_t incl = lds[t];
+  *total = lds[255];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ void __launch_bounds__(256) k_scan_reduce(const uint32_t* __restrict__ counts, uint32_t n,
+                                                     int level, uint32_t* __restrict__ block_sums) {
+  __shared__ uint32_t lds[256];
+  uint32_t base = blockIdx.x * SCAN_TILE + threadIdx.x * SCAN_ITEMS;
+  uint32_t sum = 0;
+#pragma unroll
+  for (int e = 0; e < SCAN_ITEMS; e++) sum += scan_value(counts, base + e, n, level);
+  uint32_t total;
+  block_exclusive_scan(sum, lds, &total);
+  if (threadIdx.x == 0) block_sums[blockIdx.x] = total;
+}
+
+// One block of 256 threads scans up to 256 * SCAN_TOP_ITEMS block sums in place
+// (exclusive) and stores the grand total at block_sums[nb].
+__global__ void __launch_bounds__(256) k_scan_top(uint32_t* block_sums, uint32_t nb) {
+  __shared__ uint32_t lds[256];
+  uint32_t base = threadIdx.x * SCAN_TOP_ITEMS;
+  uint32_t v[SCAN_TOP_ITEMS];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int e = 0; e < SCAN_TOP_ITEMS; e++) {
+    v[e] = (base + e < nb) ? block_sums[base + e] : 0u;
+    sum += v[e];
+  }
+  uint32_t total;
+  uint32_t run = block_exclusive_scan(sum, lds, &total);
+#pragma unroll
+  for (int e = 0; e < SCAN_TOP_ITEMS; e++) {
+    if (base + e < nb) block_sums[base + e] = run;
+    run += v[e];
+  }
+  if (threadIdx.x == 0) block_sums[nb] = total;
+}
+
+__global__ void __launch_bounds__(256) k_scan_down(const uint32_t* __restrict__ counts, uint32_t n,
+                                                   int level, const uint32_t* __restrict__ block_sums,
+                                                   uint32_t nb, uint32_t* __restrict__ out,
+                                                   uint32_t* __restrict__ out2) {
+  __shared__ uint32_t lds[256];
+  uint32_t base = blockIdx.x * SCAN_TILE + threadIdx.x * SCAN_ITEMS;
+  uint32_t v[SCAN_ITEMS];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int e = 0; e < SCAN_ITEMS; e++) {
+    v[e] = scan_value(counts, base + e, n, level);
+    sum += v[e];
+  }
+  uint32_t total;
+  uint32_t run = block_exclusive_scan(sum, lds, &total) + block_sums[blockIdx.x];
+#pragma unroll
+  for (int e = 0; e < SCAN_ITEMS; e++) {
+    if (base + e < n) {
+      out[base + e] = run;
+      if (out2) out2[base + e] = run;
+    }
+    run += v[e];
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) out[n] = block_sums[nb];
+}
+
+// ------------------------------------------------------------------ stats
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor(v, off, 64));
+  return v;
+}
+
+__global__ void __launch_bounds__(256) k_stats(const uint32_t* __restrict__ counts, uint32_t K,
+                                               msm_stats* st) {
+  uint32_t mx = 0, tot = 0;
+  uint32_t pt[MAX_LEVELS];
+#pragma unroll
+  for (int l = 0; l < MAX_LEVELS; l++) pt[l] = 0;
+  for (uint32_t k = blockIdx.x * blockDim.x + threadIdx.x; k < K; k += gridDim.x * blockDim.x) {
+    uint32_t c = counts[k];
+    mx = max(mx, c);
+    tot += c;
+#pragma unroll
+    for (int l = 0; l < MAX_LEVELS; l++) pt[l] += level_count(c, l) >> 1;
+  }
+  mx = wave_max(mx);
+  tot = wave_sum(tot);
+  bool lead = (threadIdx.x & 63) == 0;
+  if (lead) {
+    atomicMax(&st->max_count, mx);
+    atomicAdd(&st->total, tot);
+  }
+#pragma unroll
+  for (int l = 0; l < MAX_LEVELS; l++) {
+    uint32_t s = wave_sum(pt[l]);
+    if (lead && s) atomicAdd(&st->pairs[l], s);
+  }
+}
+
+// ------------------------------------------------------------------ buckets
+__global__ void __launch_bounds__(256) k_bucket_init(const uint32_t* __restrict__ counts,
+                                                     const uint32_t* __restrict__ offsets, uint32_t K,
+                                                     const uint32_t* __restrict__ sorted_idx,
+                                                     const g1a* __restrict__ points,
+                                                     g1a* __restrict__ bsum) {
+  uint32_t k = blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= K) return;
+  uint32_t c = counts[k];
+  if (c == 0) {
+    aff_store(bsum + k, aff_inf());
+  } else if (c == 1) {
+    aff_store(bsum + k, aff_load(points + sorted_idx[offsets[k]]));
+  }
+}
+
+// Largest k in [0, n) with a[k] <= x, for a non-decreasing a with a[0] <= x: a
+// branch-free binary search with a fixed trip count (n <= 2^SEARCH_STEPS), so it can
+// sit inside fully unrolled slot loops.
+__device__ __forceinline__ uint32_t last_le(const uint32_t* a, uint32_t n, uint32_t x) {
+  uint32_t k = 0;
+#pragma unroll
+  for (int b = SEARCH_STEPS - 1; b >= 0; b--) {
+    uint32_t t = k + (1u << b);
+    k = (t < n && a[t] <= x) ? t : k;
+  }
+  return k;
+}
+
+// Operands of pair-tree level `level`: pair m of bucket k adds elements 2m and 2m+1
+// of the bucket's list at this level. Level 0 reads the points through sorted_idx;
+// later levels read the previous level's buffer, where bucket k's elements sit at
+// offsets[k] + i. Output m goes to offsets[k] + m, or straight to the bucket sum
+// when the bucket has exactly two elements left; the last pair of an odd list also
+// moves the unpaired element along.
+template <int S>
+struct LevelSrc {
+  const g1a* in;
+  const uint32_t* idx;
+  g1a* out;
+  g1a* bsum;
+  const uint32_t* counts;
+  const uint32_t* offsets;
+  int level;
+  uint32_t ea[S], eb[S], kb[S], mm[S];
+
+  __device__ __forceinline__ uint32_t elem(uint32_t pos) const { return idx ? idx[pos] : pos; }
+  __device__ __forceinline__ aff a(int s) const { return aff_load(in + ea[s]); }
+  __device__ __forceinline__ aff b(int s) const { return aff_load(in + eb[s]); }
+  __device__ __forceinline__ void put(int s, const aff& r) const {
+    uint32_t k = kb[s], m = mm[s];
+    uint32_t cl = level_count(counts[k], level);
+    uint32_t off = offsets[k];
+    if (cl == 2) {
+      aff_store(bsum + k, r);
+      return;
+    }
+    aff_store(out + off + m, r);
+    uint32_t np = cl >> 1;
+    if ((cl & 1u) && m == np - 1) aff_store(out + off + np, aff_load(in + elem(off + cl - 1)));
+  }
+};
+
+template <int S>
+__global__ void __launch_bounds__(256) k_level(const g1a* __restrict__ in,
+                                               const uint32_t* __restrict__ idx, g1a* out, g1a* bsum,
+                                               const uint32_t* __restrict__ counts,
+                                               const uint32_t* __restrict__ offsets,
+                                               const uint32_t* __restrict__ poff, uint32_t K,
+                                               uint32_t npairs, int level) {
+  uint64_t p0 = (uint64_t)(blockIdx.x * blockDim.x + threadIdx.x) * S;
+  if (p0 >= npairs) return;
+  int cnt = (int)min((uint64_t)S, (uint64_t)npairs - p0);
+  LevelSrc<S> src{in, idx, out, bsum, counts, offsets, level, {}, {}, {}, {}};
+  // bucket of the first pair; later pairs stay in it or move to a later bucket
+  uint32_t k = last_le(poff, K, (uint32_t)p0);
+#pragma unroll
+  for (int s = 0; s < S; s++) {
+    if (s < cnt) {
+      uint32_t p = (uint32_t)p0 + s;
+      if (p >= poff[k + 1]) k = last_le(poff, K, p);
+      uint32_t m = p - poff[k];
+      src.kb[s] = k;
+      src.mm[s] = m;
+      uint32_t pos = offsets[k] + 2 * m;
+      src.ea[s] = src.elem(pos);
+      src.eb[s] = src.elem(pos + 1);
+    }
+  }
+  batch_affine_add<S>(src, cnt);
+}
+
+// ------------------------------------------------------------------ reduction
+__device__ __forceinline__ void xyzz_store(xyzz_st* p, const xyzz& a) {
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    p->w[i] = a.X.v[i];
+    p->w[8 + i] = a.Y.v[i];
+    p->w[16 + i] = a.ZZ.v[i];
+    p->w[24 + i] = a.ZZZ.v[i];
+  }
+}
+
+__device__ __forceinline__ xyzz xyzz_load(const xyzz_st* p) {
+  xyzz a;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    a.X.v[i] = p->w[i];
+    a.Y.v[i] = p->w[8 + i];
+    a.ZZ.v[i] = p->w[16 + i];
+    a.ZZZ.v[i] = p->w[24 + i];
+  }
+  return a;
+}
+
+// Segment s of window j covers buckets [lo, hi). With T = sum of the segment's
+// buckets and R = sum_b (b - lo + 1) B_b (a running sum from the top bucket down),
+// the segment's share of W_j = sum_b b B_b is R + (lo - 1) T.
+__global__ void __launch_bounds__(128) k_rsum_seg(const g1a* __restrict__ bsum, uint32_t c,
+                                                  uint32_t nwin, uint32_t seg_len, uint32_t nseg,
+                                                  xyzz_st* __restrict__ seg_out) {
+  uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= nwin * nseg) return;
+  uint32_t j = t / nseg, s = t % nseg;
+  uint32_t lo = max(1u, s * seg_len), hi = min(1u << c, (s + 1) * seg_len);
+  xyzz T = xyzz_inf(), R = xyzz_inf();
+  for (uint32_t b = hi; b-- > lo;) {
+    T = xyzz_add_aff(T, aff_load(bsum + ((size_t)j << c) + b));
+    R = xyzz_add(R, T);
+  }
+  xyzz_store(seg_out + t, xyzz_add(R, xyzz_mul_small(T, lo - 1)));
+}
+
+__global__ void __launch_bounds__(256) k_rsum_win(const xyzz_st* __restrict__ seg, uint32_t nseg,
+                                                  xyzz_st* __restrict__ win) {
+  __shared__ xyzz_st lds[256];
+  uint32_t j = blockIdx.x, t = threadIdx.x;
+  xyzz acc = xyzz_inf();
+  for (uint32_t s = t; s < nseg; s += 256) acc = xyzz_add(acc, xyzz_load(seg + (size_t)j * nseg + s));
+  xyzz_store(&lds[t], acc);
+  __syncthreads();
+  for (uint32_t stride = 128; stride > 0; stride >>= 1) {
+    if (t < stride) {
+      acc = xyzz_add(acc, xyzz_load(&lds[t + stride]));
+      xyzz_store(&lds[t], acc);
+    }
+    __syncthreads();
+  }
+  if (t == 0) xyzz_store(win + j, acc);
+}
+
+// Q = sum_j 2^(c j) W_j by Horner from the top window, then to affine.
+__global__ void k_final(const xyzz_st* __restrict__ win, uint32_t nwin, uint32_t c, g1a* out) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  xyzz q = xyzz_load(win + nwin - 1);
+  for (int j = (int)nwin - 2; j >= 0; j--) {
+    for (uint32_t b = 0; b < c; b++) q = xyzz_dbl(q);
+    q = xyzz_add(q, xyzz_load(win + j));
+  }
+  aff_store(out, xyzz_to_aff(q));
+}
+
+// ------------------------------------------------------------------ generator
+__global__ void __launch_bounds__(128) k_from_scalars(const uint32_t* __restrict__ ks, uint32_t n,
+                                                      g1a* __restrict__ out) {
+  uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  sc256 k = load_scalar(ks, i);
+  aff g;
+  g.x = fp_from_u32(1);
+  g.y = fp_from_u32(2);
+  xyzz acc = xyzz_inf();
+  for (int w = 7; w >= 0; w--) {
+    uint32_t word = k.w[w];
+    for (int b = 31; b >= 0; b--) {
+      acc = xyzz_dbl(acc);
+      if ((word >> b) & 1u) acc = xyzz_add_aff(acc, g);
+    }
+  }
+  aff_store(out + i, xyzz_to_aff(acc));
+}
+
+// ------------------------------------------------------------------ test hooks
+__device__ __forceinline__ fp fp_load_words(const uint32_t* p) {
+  fp r;
+#pragma unroll
+  for (int i = 0; i < 8; i++) r.v[i] = p[i];
+  return r;
+}
+
+__global__ void k_test_fp(int op, const uint32_t* a, const uint32_t* b, uint32_t* out, uint32_t n) {
+  uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  fp x = fp_load_words(a + 8 * (size_t)i), y = fp_zero(), r;
+  if (b) y = fp_load_words(b + 8 * (size_t)i);
+  switch (op) {
+    case 0: r = fp_mul(x, y); break;
+    case 1: r = fp_add(x, y); break;
+    case 2: r = fp_sub(x, y); break;
+    case 3: r = fp_sqr(x); break;
+    case 4: r = fp_is_zero(x) ? fp_zero() : fp_inv(x); break;
+    case 5: r = fp_mul(x, fp_r2()); break;
+    default: {
+      fp one = fp_zero();
+      one.v[0] = 1;
+      r = fp_mul(x, one);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 8; k++) out[8 * (size_t)i + k] = r.v[k];
+}
+
+template <int S>
+struct PairSrc {
+  const g1a* a_;
+  const g1a* b_;
+  g1a* out;
+  uint32_t base;
+  __device__ __forceinline__ aff a(int s) const { return aff_load(a_ + base + s); }
+  __device__ __forceinline__ aff b(int s) const { return aff_load(b_ + base + s); }
+  __device__ __forceinline__ void put(int s, const aff& r) const { aff_store(out + base + s, r); }
+};
+
+template <int S>
+__global__ void __launch_bounds__(256) k_test_pair_add(const g1a* a, const g1a* b, g1a* out,
+                                                       uint32_t n) {
+  uint64_t p0 = (uint64_t)(blockIdx.x * blockDim.x + threadIdx.x) * S;
+  if (p0 >= n) return;
+  int cnt = (int)min((uint64_t)S, (uint64_t)n - p0);
+  PairSrc<S> src{a, b, out, (uint32_t)p0};
+  batch_affine_add<S>(src, cnt);
+}
+
+// ------------------------------------------------------------------ launchers
+static inline unsigned grid_for(size_t n, unsigned block) { return (unsigned)((n + block - 1) / block); }
+
+hipError_t launch_fill(uint32_t* p, size_t n, uint32_t v, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  k_fill_u32<<<grid_for(n, 256), 256, 0, st>>>(p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_hist(const uint32_t* scalars, uint32_t n, uint32_t c, uint32_t nwin,
+                       uint32_t* counts, msm_stats* st, hipStream_t s) {
+  k_hist<<<grid_for(n, 256), 256, 0, s>>>(scalars, n, c, nwin, counts, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(const uint32_t* scalars, uint32_t n, uint32_t c, uint32_t nwin,
+                          uint32_t* cursor, uint32_t* sorted_idx, hipStream_t s) {
+  k_scatter<<<grid_for(n, 256), 256, 0, s>>>(scalars, n, c, nwin, cursor, sorted_idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(const uint32_t* counts, uint32_t n, int level, uint32_t* block_sums,
+                       uint32_t* out, uint32_t* out2, hipStream_t s) {
+  uint32_t nb = (n + SCAN_TILE - 1) / SCAN_TILE;
+  if (nb == 0) nb = 1;
+  k_scan_reduce<<<nb, 256, 0, s>>>(counts, n, level, block_sums);
+  k_scan_top<<<1, 256, 0, s>>>(block_sums, nb);
+  k_scan_down<<<nb, 256, 0, s>>>(counts, n, level, block_sums, nb, out, out2);
+  return hipGetLastError();
+}
+
+hipError_t launch_stats(const uint32_t* counts, uint32_t K, msm_stats* st, hipStream_t s) {
+  unsigned g = grid_for(K, 256);
+  if (g > 1024) g = 1024;
+  k_stats<<<g, 256, 0, s>>>(counts, K, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_bucket_init(const uint32_t* counts, const uint32_t* offsets, uint32_t K,
+                              const uint32_t* sorted_idx, const g1a* points, g1a* bsum,
+                              hipStream_t s) {
+  k_bucket_init<<<grid_for(K, 256), 256, 0, s>>>(counts, offsets, K, sorted_idx, points, bsum);
+  return hipGetLastError();
+}
+
+template <int S>
+static hipError_t level_S(const g1a* in, const uint32_t* idx, g1a* out, g1a* bsum,
+                          const uint32_t* counts, const uint32_t* offsets, const uint32_t* poff,
+                          uint32_t K, uint32_t npairs, int level, hipStream_t s) {
+  size_t threads = (npairs + S - 1) / S;
+  k_level<S><<<grid_for(threads, LEVEL_BLOCK), LEVEL_BLOCK, 0, s>>>(in, idx, out, bsum, counts,
+                                                                    offsets, poff, K, npairs, level);
+  return hipGetLastError();
+}
+
+hipError_t launch_level(int S, const g1a* in, const uint32_t* idx, g1a* out, g1a* bsum,
+                        const uint32_t* counts, const uint32_t* offsets, const uint32_t* poff,
+                        uint32_t K, uint32_t npairs, int level, hipStream_t s) {
+  switch (S) {
+    case 4: return level_S<4>(in, idx, out, bsum, counts, offsets, poff, K, npairs, level, s);
+    case 8: return level_S<8>(in, idx, out, bsum, counts, offsets, poff, K, npairs, level, s);
+    case 16: return level_S<16>(in, idx, out, bsum, counts, offsets, poff, K, npairs, level, s);
+    case 32: return level_S<32>(in, idx, out, bsum, counts, offsets, poff, K, npairs, level, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_reduce(const g1a* bsum, uint32_t c, uint32_t nwin, uint32_t seg_len,
+                         uint32_t nseg, xyzz_st* seg, xyzz_st* win, hipStream_t s) {
+  k_rsum_seg<<<grid_for((size_t)nwin * nseg, 128), 128, 0, s>>>(bsum, c, nwin, seg_len, nseg, seg);
+  k_rsum_win<<<nwin, 256, 0, s>>>(seg, nseg, win);
+  return hipGetLastError();
+}
+
+hipError_t launch_final(const xyzz_st* win, uint32_t nwin, uint32_t c, g1a* out, hipStream_t s) {
+  k_final<<<1, 64, 0, s>>>(win, nwin, c, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_from_scalars(const uint32_t* ks, uint32_t n, g1a* out, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  k_from_scalars<<<grid_for(n, 128), 128, 0, s>>>(ks, n, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_test_fp(int op, const uint32_t* a, const uint32_t* b, uint32_t* out, uint32_t n,
+                          hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  k_test_fp<<<grid_for(n, 128), 128, 0, s>>>(op, a, b, out, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_test_pair_add(int S, const g1a* a, const g1a* b, g1a* out, uint32_t n,
+                                hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  size_t threads;
+  switch (S) {
+    case 4: threads = (n + 3) / 4; k_test_pair_add<4><<<grid_for(threads, 256), 256, 0, s>>>(a, b, out, n); break;
+    case 8: threads = (n + 7) / 8; k_test_pair_add<8><<<grid_for(threads, 256), 256, 0, s>>>(a, b, out, n); break;
+    case 16: threads = (n + 15) / 16; k_test_pair_add<16><<<grid_for(threads, 256), 256, 0, s>>>(a, b, out, n); break;
+    case 32: threads = (n + 31) / 32; k_test_pair_add<32><<<grid_for(threads, 256), 256, 0, s>>>(a, b, out, n); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace msmk

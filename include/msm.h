@@ -1,0 +1,158 @@
+/*
+ * msm.h - C ABI of libmsm, an MI355X (gfx950) multi-scalar multiplication over
+ * BN254 G1:
+ *
+ *     Q = sum_{i < n} s_i * P_i
+ *
+ * The method is the bucket (Pippenger) MSM of aztec-packages PR #23738 / #23736 /
+ * #23520 ("bb/msm"): scalars are cut into c-bit windows (c = 13 at n = 2^16 in
+ * PR #23520, "Measurements"), (bucket, point) pairs are sorted into per-bucket lists
+ * (the sorted_bucket_list / sorted_count_list of PR #23738, "What would actually
+ * win"), each bucket is summed with affine additions in batches of S that share one
+ * field inversion (PR #23738 "TL;DR", PR #23736 "Goal & lever"; S = 8 is the pages'
+ * default, PR #23738 "What landed here"), the pairs of each bucket are reduced level
+ * by level (the pair-tree of PR #23520, "Summary"), and the bucket sums are combined
+ * per window by a running sum and across windows by doubling. The curve is the one
+ * barretenberg uses; the pages do not name it, so its constants are EIP-196's.
+ *
+ * Data formats (all little-endian):
+ *   - a field element is eight 32-bit words holding x * 2^256 mod p (Montgomery
+ *     form), fully reduced (< p);
+ *   - a point is msm_g1_affine {x, y}, 64 bytes; the point at infinity is (0, 0);
+ *   - a scalar is eight 32-bit words holding an integer below 2^256 (not Montgomery).
+ *
+ * Every call validates its arguments before touching the GPU. Return codes are the
+ * MSM_* values below; msm_last_error() gives the calling thread's last message.
+ * Device pointers are the caller's; the library never frees them.
+ */
+#ifndef MSM_H
+#define MSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct msm_g1_affine {
+  uint32_t x[8];
+  uint32_t y[8];
+} msm_g1_affine;
+
+typedef struct msm_ctx msm_ctx;
+
+enum {
+  MSM_OK = 0,
+  MSM_ERR_ARG = -1,   /* bad pointer, alignment, size, c or S; workspace too small */
+  MSM_ERR_HIP = -2,   /* a HIP runtime call or kernel launch failed */
+  MSM_ERR_OOM = -3,   /* device or pinned host allocation failed */
+  MSM_ERR_RANGE = -4  /* some scalar is >= 2^(W*c), W = ceil(254 / c) windows */
+};
+
+/* Largest n accepted (bucket lists are indexed with 32-bit offsets). */
+#define MSM_MAX_N ((size_t)1 << 26)
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int msm_version(void);
+
+/* Message describing the calling thread's most recent error ("" if none). */
+const char* msm_last_error(void);
+
+/*
+ * Context: binds a device and owns a growable workspace and a pinned host buffer
+ * for the one mid-pipeline read-back. One context per host thread; calls on one
+ * context must not overlap. Returns MSM_ERR_ARG for a bad device or NULL out.
+ */
+int msm_ctx_create(int device, msm_ctx** out);
+void msm_ctx_destroy(msm_ctx* ctx);
+
+/*
+ * Device workspace bytes msm_run needs for n points with window c (the analogue of
+ * the pages' estimateMem, PR #23520 "Summary"). S does not change the size.
+ * Returns 0 for invalid n or c.
+ */
+size_t msm_workspace_bytes(size_t n, int c, int S);
+
+/*
+ * Q = sum_i s_i * P_i on `stream` (a hipStream_t; NULL is the null stream).
+ *   d_points   device, n msm_g1_affine, 16-byte aligned; every point on the curve or
+ *              (0, 0); the library does not check curve membership.
+ *   d_scalars  device, n * 8 uint32 words, 16-byte aligned.
+ *   n          0 .. MSM_MAX_N; n = 0 gives the point at infinity.
+ *   c          window width in bits, 1 .. 16; W = ceil(254 / c) windows.
+ *   S          affine additions sharing one inversion: 4, 8, 16 or 32.
+ *   d_workspace device scratch of msm_workspace_bytes(n, c, S) bytes (256-byte
+ *              aligned), or NULL to use the context's own (grown on demand).
+ *   d_out      device, one msm_g1_affine: Q in affine Montgomery form, (0, 0) if
+ *              Q is the point at infinity.
+ * The call enqueues the decompose/count/sort kernels, then blocks once on `stream`
+ * to read back a small plan (largest bucket, scalar range flag), then enqueues the
+ * accumulate, reduction and combine kernels and returns; d_out is valid once the
+ * stream reaches that point. Scalars s with r <= s < 2^(W*c) are treated as the
+ * integers they are (s * P = (s mod r) * P). MSM_ERR_RANGE if any scalar has a bit
+ * at or above W*c set (nothing further is enqueued).
+ */
+int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scalars, size_t n,
+            int c, int S, void* d_workspace, size_t workspace_bytes, void* stream,
+            msm_g1_affine* d_out);
+
+/*
+ * Synchronous convenience form, the shape msm(points_affine, scalars, n, c) -> point:
+ * device inputs, result written to host memory h_out. Uses a per-device default
+ * context, S = 8 and the null stream.
+ */
+int msm(const msm_g1_affine* d_points, const uint32_t* d_scalars, size_t n, int c,
+        msm_g1_affine* h_out);
+
+/*
+ * d_out[i] = k_i * G for the BN254 generator G = (1, 2), in the point format above.
+ * d_k: device, n * 8 uint32 words (any 256-bit integers). Asynchronous on `stream`.
+ * Builds synthetic inputs of the pages' kind: independent points r_i * G
+ * (PR #23736, "Correctness-harness fix").
+ */
+int msm_g1_from_scalars(const uint32_t* d_k, size_t n, msm_g1_affine* d_out, void* stream);
+
+/*
+ * Phase timing. When enabled on a context, msm_run records HIP events on its stream
+ * around each phase: sort (count, scan, scatter), accumulate (pair-tree levels, with
+ * every level kernel launch bracketed on its own), reduce (running sums) and final
+ * (window combine). msm_ctx_timing_read waits for the events recorded since the last
+ * read, sums them into *out and resets. Events are reused; enabling costs a few
+ * microseconds per call. Returns MSM_ERR_ARG for NULL arguments.
+ */
+typedef struct msm_timing {
+  double sort_ms;          /* decompose, histogram, scans, scatter (incl. the read-back) */
+  double accumulate_ms;    /* bucket init + all pair-tree levels (scans included) */
+  double level_kernel_ms;  /* the pair-tree level kernels alone */
+  double reduce_ms;        /* running-sum segments + per-window trees */
+  double final_ms;         /* window combine and conversion to affine */
+  int runs;                /* msm_run calls summed */
+  int level_launches;      /* level kernel launches summed */
+  uint64_t level_pairs;    /* affine additions done by those launches */
+  uint64_t level_lanes;    /* lanes that ran them (one inversion each) */
+} msm_timing;
+
+int msm_ctx_set_timing(msm_ctx* ctx, int enable);
+int msm_ctx_timing_read(msm_ctx* ctx, msm_timing* out);
+
+/*
+ * Test hooks (the same device code as the MSM, exposed for unit tests).
+ *
+ * msm_test_fp: element-wise F_p operation on n Montgomery-form elements (8 words
+ * each, device pointers; d_b unused for unary ops): op 0 a*b, 1 a+b, 2 a-b, 3 a^2,
+ * 4 a^-1 (0 -> 0), 5 to Montgomery (a * 2^256), 6 from Montgomery (a * 2^-256).
+ *
+ * msm_test_pair_add: d_out[i] = d_a[i] + d_b[i] for n affine points, computed by
+ * the batched-affine adder with S slots per lane (one inversion per S sums).
+ */
+int msm_test_fp(int op, const uint32_t* d_a, const uint32_t* d_b, uint32_t* d_out, size_t n,
+                void* stream);
+int msm_test_pair_add(const msm_g1_affine* d_a, const msm_g1_affine* d_b, msm_g1_affine* d_out,
+                      size_t n, int S, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSM_H */

@@ -1,0 +1,83 @@
+"""C-ABI checks that need no GPU: libmsm.so loads, exports every function that
+include/msm.h declares, sizes its workspace, and rejects bad arguments before any
+HIP call is made."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from elliptic_curve_scalar_amd import msm as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msm.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(msm\w*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_expected_entry_points():
+    names = _declared_functions()
+    for want in ("msm", "msm_run", "msm_ctx_create", "msm_ctx_destroy", "msm_workspace_bytes",
+                 "msm_last_error", "msm_g1_from_scalars", "msm_test_fp", "msm_test_pair_add",
+                 "msm_version"):
+        assert want in names
+    assert set(names) == set(M.SYMBOLS), "binding and header disagree"
+
+
+def test_library_exports_every_declared_symbol():
+    L = M.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+    assert L.msm_version() >= 100
+
+
+def test_workspace_bytes():
+    assert M.workspace_bytes(1 << 16, 13) > 0
+    assert M.workspace_bytes(1 << 16, 13) % 256 == 0
+    assert M.workspace_bytes(1 << 16, 0) == 0
+    assert M.workspace_bytes(1 << 16, 17) == 0
+    assert M.workspace_bytes(M.MSM_MAX_N + 1, 8) == 0
+    assert M.workspace_bytes(1 << 20, 16) > M.workspace_bytes(1 << 16, 16)
+    assert M.workspace_bytes(1 << 16, 13, 4) == M.workspace_bytes(1 << 16, 13, 32)
+
+
+def _err(L):
+    return L.msm_last_error().decode()
+
+
+def test_argument_errors_without_gpu():
+    L = M.lib()
+    out = ctypes.c_void_p(256)
+    p = ctypes.c_void_p(512)
+    # NULL context
+    assert L.msm_run(None, p, p, 16, 13, 8, None, 0, None, out) == M.MSM_ERR_ARG
+    assert "ctx" in _err(L)
+    # NULL h_out / bad c / bad S / misaligned pointers on the synchronous form
+    assert L.msm(p, p, 16, 13, None) == M.MSM_ERR_ARG
+    assert L.msm(p, p, 16, 0, out) == M.MSM_ERR_ARG
+    assert "1..16" in _err(L)
+    assert L.msm(p, p, 16, 17, out) == M.MSM_ERR_ARG
+    assert L.msm(ctypes.c_void_p(513), p, 16, 13, out) == M.MSM_ERR_ARG
+    assert "aligned" in _err(L)
+    assert L.msm(None, p, 16, 13, out) == M.MSM_ERR_ARG
+    assert L.msm(p, p, M.MSM_MAX_N + 1, 13, out) == M.MSM_ERR_ARG
+    # generator and test hooks
+    assert L.msm_g1_from_scalars(None, 4, p, None) == M.MSM_ERR_ARG
+    assert L.msm_g1_from_scalars(ctypes.c_void_p(4), 4, p, None) == M.MSM_ERR_ARG
+    assert L.msm_test_fp(7, p, p, p, 4, None) == M.MSM_ERR_ARG
+    assert L.msm_test_fp(0, p, None, p, 4, None) == M.MSM_ERR_ARG
+    assert L.msm_test_pair_add(p, p, p, 4, 5, None) == M.MSM_ERR_ARG
+    # context creation with a NULL out pointer
+    assert L.msm_ctx_create(0, None) == M.MSM_ERR_ARG
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    pts = torch.zeros((4, 16), dtype=torch.int32)
+    with pytest.raises(ValueError):
+        M._dev_ptr(pts, 16, "points")

@@ -1,0 +1,174 @@
+"""End-to-end MSM parity on the GPU through the C ABI, bit-exact against the oracle:
+
+* every workload recipe at reduced sizes (several tiles, ragged n);
+* the full-size workloads, against the oracle's Pippenger on the oracle's own points
+  and against the linearity closed form (sum_i s_i r_i mod r) * G;
+* knob invariance: the same bits for every S and several c;
+* edge cases: n = 0, 1, 2, all-zero scalars, {P, P}, {P, -P}, infinity inputs,
+  the arithmetic-progression point set, one giant bucket, and the range error.
+"""
+import random
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import ref
+from elliptic_curve_scalar_amd import workloads as wl
+
+from gpu_util import DEV, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _msm():
+    from elliptic_curve_scalar_amd import msm as M
+    return M
+
+
+def _gpu_msm(pts, sc, c, S=8):
+    M = _msm()
+    return to_host(M.msm(to_dev(pts), to_dev(sc), c, S))
+
+
+@pytest.mark.parametrize("name,n", [("n256_c8", 256), ("n256_c8", 1000), ("n65536_c13", 4097),
+                                    ("n262144_c13_edge", 6000), ("n1048576_c16", 3001),
+                                    ("n4194304_c16_skew", 5000)])
+def test_reduced_sizes_bit_exact(name, n):
+    w = wl.generate(name, n=n)
+    pts = oracle.g1_from_scalars(w["dlogs"])
+    want = oracle.msm_pippenger(pts, w["scalars"], w["c"])
+    for S in (w["S"],):
+        say(name, "n", n, "c", w["c"], "S", S)
+        got = _gpu_msm(pts, w["scalars"], w["c"], S)
+        assert np.array_equal(got, want)
+    assert ref.decode_point(want) == ref.msm_linear(wl.to_ints(w["dlogs"]), wl.to_ints(w["scalars"]))
+
+
+@pytest.mark.parametrize("name", ["n256_c8", "n65536_c13", "n262144_c13_edge", "n1048576_c16",
+                                  "n4194304_c16_skew"])
+def test_full_size_workloads(name):
+    """Full-size inputs: GPU-generated points must equal the oracle's, and the GPU MSM
+    must equal the oracle's Pippenger and the closed form."""
+    M = _msm()
+    w = wl.generate(name)
+    say(name, "generate points n", w["n"])
+    k = to_dev(w["dlogs"])
+    pts_gpu = M.g1_from_scalars(k)
+    pts = oracle.g1_from_scalars(w["dlogs"])
+    assert np.array_equal(to_host(pts_gpu), pts)
+    sweep = wl.CONFIGS[name].get("S_sweep", (w["S"],))
+    want = oracle.msm_pippenger(pts, w["scalars"], w["c"])
+    sc = to_dev(w["scalars"])
+    for S in sweep:
+        say(name, "msm c", w["c"], "S", S)
+        got = to_host(M.msm(pts_gpu, sc, w["c"], S))
+        assert np.array_equal(got, want), S
+    if w["n"] <= (1 << 20):
+        lin = ref.msm_linear(wl.to_ints(w["dlogs"]), wl.to_ints(w["scalars"]))
+        assert ref.decode_point(want) == lin
+
+
+def test_knob_invariance():
+    """Same inputs, every S and several c: one answer (the sum is unique)."""
+    w = wl.generate("n65536_c13", n=3000)
+    pts = oracle.g1_from_scalars(w["dlogs"])
+    want = oracle.msm_pippenger(pts, w["scalars"], 13)
+    for c in (1, 5, 8, 11, 13, 16):
+        for S in (4, 8, 16, 32):
+            say("knobs c", c, "S", S)
+            assert np.array_equal(_gpu_msm(pts, w["scalars"], c, S), want), (c, S)
+
+
+def test_sync_entry_point():
+    M = _msm()
+    w = wl.generate("n256_c8")
+    pts = oracle.g1_from_scalars(w["dlogs"])
+    say("msm() sync n 256")
+    got = M.msm_sync(to_dev(pts), to_dev(w["scalars"]), 8)
+    assert got == list(oracle.msm_pippenger(pts, w["scalars"], 8))
+
+
+def _pts(dl):
+    return oracle.g1_from_scalars(wl.from_ints(dl))
+
+
+def test_edge_cases():
+    rng = random.Random(99)
+    dl = [rng.randrange(1, ref.R) for _ in range(8)]
+    pts = _pts(dl)
+    negp = _pts([ref.R - dl[0]])
+    inf = np.zeros((1, 16), np.uint32)
+    cases = {
+        "n1": (pts[:1], [12345]),
+        "n2": (pts[:2], [ref.R - 1, 1]),
+        "zero_scalars": (pts, [0] * 8),
+        "dup_pair": (np.vstack([pts[:1], pts[:1]]), [77, 77]),
+        "neg_pair": (np.vstack([pts[:1], negp]), [77, 77]),
+        "p_p_m2p": (np.vstack([pts[:1], pts[:1], _pts([(ref.R - 2 * dl[0]) % ref.R])]), [5, 5, 5]),
+        "inf_inputs": (np.vstack([inf, pts[:2], inf]), [3, 4, 5, 6]),
+        "all_ones": (pts, [1] * 8),
+        "r_minus_1": (pts, [ref.R - 1] * 8),
+        "high_scalar": (pts[:2], [ref.R + 7, (1 << 254) - 1]),
+    }
+    for name, (p, s) in cases.items():
+        sc = wl.from_ints(s)
+        want = oracle.msm_pippenger(p, sc, 13)
+        for c, S in ((13, 8), (4, 4), (16, 32)):
+            say("edge", name, "c", c, "S", S)
+            assert np.array_equal(_gpu_msm(p, sc, c, S), want), (name, c, S)
+
+
+def test_empty_input():
+    M = _msm()
+    import torch
+    say("n = 0")
+    out = M.msm(torch.zeros((0, 16), dtype=torch.uint32, device=DEV),
+                torch.zeros((0, 8), dtype=torch.uint32, device=DEV), 13)
+    assert not to_host(out).any()
+
+
+def test_equal_points_equal_scalars():
+    """Every pair-tree add is a doubling: n copies of one point with one scalar."""
+    dl = [123456789]
+    p = np.repeat(_pts(dl), 1000, axis=0)
+    sc = wl.from_ints([ref.R - 3] * 1000)
+    want = oracle.msm_pippenger(p, sc, 13)
+    say("all equal n 1000")
+    assert np.array_equal(_gpu_msm(p, sc, 13, 8), want)
+
+
+def test_arithmetic_progression_points():
+    """The point set the pages report breaks affine partial sums (PR #23736)."""
+    dl = wl.arithmetic_progression(4096, a=1234567, d=89)
+    pts = oracle.g1_from_scalars(dl)
+    sc = wl.generate("n65536_c13", n=4096)["scalars"]
+    want = oracle.msm_pippenger(pts, sc, 13)
+    for S in (4, 8, 32):
+        say("AP set S", S)
+        assert np.array_equal(_gpu_msm(pts, sc, 13, S), want)
+    assert ref.decode_point(want) == ref.msm_linear(wl.to_ints(dl), wl.to_ints(sc))
+
+
+def test_giant_bucket():
+    """One bucket per window holds ~half of all entries (deep pair-tree)."""
+    w = wl.generate("n65536_c13", n=6000)
+    sc = w["scalars"].copy()
+    sc[::2] = wl.from_ints([ref.R - 1])[0]
+    pts = oracle.g1_from_scalars(w["dlogs"])
+    want = oracle.msm_pippenger(pts, sc, 13)
+    say("giant bucket n 6000")
+    assert np.array_equal(_gpu_msm(pts, sc, 13, 8), want)
+
+
+def test_range_error():
+    M = _msm()
+    pts = _pts([5])
+    sc = wl.from_ints([1 << 255])
+    say("range error c 15")
+    with pytest.raises(M.MsmError) as e:
+        M.msm(to_dev(pts), to_dev(sc), 15)
+    assert e.value.code == M.MSM_ERR_RANGE
+    # the same scalar is in range for c = 16 (W c = 256)
+    want = oracle.msm_pippenger(pts, sc, 16)
+    assert np.array_equal(_gpu_msm(pts, sc, 16), want)
