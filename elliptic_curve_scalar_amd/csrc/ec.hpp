@@ -13,7 +13,7 @@
 // The point at infinity is (0, 0) in affine storage (not on the curve, since
 // 0 != 0^3 + 3) and ZZ = ZZZ = 0 in XYZZ.
 #pragma once
-#include "fp.hpp"
+#include "inv.hpp"
 
 namespace msmk {
 
