@@ -49,6 +49,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="n65536_c13")
     ap.add_argument("--S", type=int, default=None, help="override the workload's S")
+    ap.add_argument("--affine-levels", type=int, default=None,
+                    help="pair-tree levels done with batched affine adds (-1: all)")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0,
                     help="CPU seconds for the oracle baseline (0 disables it)")
     args = ap.parse_args()
@@ -76,6 +78,8 @@ def main() -> int:
     del k
 
     ctx = M.context(dev)
+    if args.affine_levels is not None:
+        ctx.set_affine_levels(args.affine_levels)
     out = torch.empty(16, dtype=torch.uint32, device=dev)
     for _ in range(args.warmup):
         ctx.run(points, scalars, c, S, out=out)
@@ -119,7 +123,7 @@ def main() -> int:
         "algorithmic_ops_per_launch": mads / launches,
     }
     phases = {kk: tm[kk] / runs for kk in ("sort_ms", "accumulate_ms", "level_kernel_ms",
-                                            "reduce_ms", "final_ms")}
+                                            "xyzz_level_ms", "reduce_ms", "final_ms")}
 
     cpu = None
     verified = None

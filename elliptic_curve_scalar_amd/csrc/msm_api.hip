@@ -43,10 +43,11 @@ uint32_t segment_length(int c, int nwin) {
 }
 
 struct Layout {
-  size_t stats, counts, offsets, cursor, poff, block_sums, sorted_idx, lvl_a, lvl_b, bsum, seg, win;
+  size_t stats, counts, offsets, cursor, poff, block_sums, sorted_idx, aff_a, aff_b, xz_a, xz_b,
+      bsum, seg, win;
   size_t total;
   uint32_t K, nwin, seg_len, nseg;
-  size_t E_max;
+  size_t E_max, half;
 };
 
 Layout plan(size_t n, int c) {
@@ -56,6 +57,7 @@ Layout plan(size_t n, int c) {
   L.seg_len = segment_length(c, (int)L.nwin);
   L.nseg = ((1u << c) + L.seg_len - 1) / L.seg_len;
   L.E_max = n * L.nwin;
+  L.half = (L.E_max + L.K) / 2 + 1;  // elements of a level >= 1 buffer
   size_t nb = (L.K + SCAN_TILE - 1) / SCAN_TILE + 1;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -70,9 +72,11 @@ Layout plan(size_t n, int c) {
   L.poff = take(((size_t)L.K + 1) * 4);
   L.block_sums = take((nb + 1) * 4);
   L.sorted_idx = take(L.E_max * 4);
-  L.lvl_a = take(L.E_max * sizeof(g1a));
-  L.lvl_b = take(L.E_max * sizeof(g1a));
-  L.bsum = take((size_t)L.K * sizeof(g1a));
+  L.aff_a = take(L.half * sizeof(g1a));
+  L.aff_b = take(L.half * sizeof(g1a));
+  L.xz_a = take(L.half * sizeof(xyzz_st));
+  L.xz_b = take(L.half * sizeof(xyzz_st));
+  L.bsum = take((size_t)L.K * sizeof(xyzz_st));
   L.seg = take((size_t)L.nwin * L.nseg * sizeof(xyzz_st));
   L.win = take((size_t)L.nwin * sizeof(xyzz_st));
   L.total = off;
@@ -95,7 +99,7 @@ int check_run_args(const msm_g1_affine* pts, const uint32_t* sc, size_t n, int c
 
 }  // namespace
 
-enum Phase { PH_SORT = 0, PH_ACCUM = 1, PH_LEVEL = 2, PH_REDUCE = 3, PH_FINAL = 4 };
+enum Phase { PH_SORT = 0, PH_ACCUM = 1, PH_LEVEL = 2, PH_REDUCE = 3, PH_FINAL = 4, PH_XYZZ = 5 };
 
 struct Span {
   int phase;
@@ -104,6 +108,7 @@ struct Span {
 
 struct msm_ctx {
   int device = 0;
+  int affine_levels = 1;  // leading pair-tree levels done with batched affine adds
   void* ws = nullptr;
   size_t ws_bytes = 0;
   msm_stats* host_stats = nullptr;  // pinned
@@ -227,8 +232,9 @@ int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scala
   uint32_t* poff = (uint32_t*)(ws + L.poff);
   uint32_t* block_sums = (uint32_t*)(ws + L.block_sums);
   uint32_t* sorted_idx = (uint32_t*)(ws + L.sorted_idx);
-  g1a* lvl[2] = {(g1a*)(ws + L.lvl_a), (g1a*)(ws + L.lvl_b)};
-  g1a* bsum = (g1a*)(ws + L.bsum);
+  g1a* aff[2] = {(g1a*)(ws + L.aff_a), (g1a*)(ws + L.aff_b)};
+  xyzz_st* xz[2] = {(xyzz_st*)(ws + L.xz_a), (xyzz_st*)(ws + L.xz_b)};
+  xyzz_st* bsum = (xyzz_st*)(ws + L.bsum);
   xyzz_st* seg = (xyzz_st*)(ws + L.seg);
   xyzz_st* win = (xyzz_st*)(ws + L.win);
   const g1a* pts = (const g1a*)d_points;
@@ -257,15 +263,28 @@ int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scala
     uint32_t np = hs.pairs[l];
     if (np == 0) continue;
     HIP_TRY(launch_scan(counts, L.K, l, block_sums, poff, nullptr, st));
-    const g1a* in = (l == 0) ? pts : lvl[(l - 1) & 1];
     const uint32_t* idx = (l == 0) ? sorted_idx : nullptr;
-    PhaseMark ph_lvl(ctx, st, PH_LEVEL);
-    HIP_TRY(launch_level(S, in, idx, lvl[l & 1], bsum, counts, offsets, poff, L.K, np, l, st));
-    ph_lvl.end();
-    if (ctx->timing) {
-      ctx->level_launches++;
-      ctx->level_pairs += np;
-      ctx->level_lanes += (np + S - 1) / S;
+    const int La = ctx->affine_levels < 0 ? MAX_LEVELS : ctx->affine_levels;
+    if (l < La) {
+      // batched affine adds, S per lane sharing one inversion
+      const g1a* in = (l == 0) ? pts : aff[(l - 1) & 1];
+      PhaseMark ph_lvl(ctx, st, PH_LEVEL);
+      HIP_TRY(launch_level(S, in, idx, aff[l & 1], bsum, counts, offsets, poff, L.K, np, l, st));
+      ph_lvl.end();
+      if (ctx->timing) {
+        ctx->level_launches++;
+        ctx->level_pairs += np;
+        ctx->level_lanes += (np + S - 1) / S;
+      }
+    } else {
+      // XYZZ adds, one pair per lane; the first such level reads affine input
+      const bool in_aff = (l == La) || l == 0;
+      const void* in = (l == 0) ? (const void*)pts
+                       : in_aff ? (const void*)aff[(l - 1) & 1] : (const void*)xz[(l - 1) & 1];
+      PhaseMark ph_lvl(ctx, st, PH_XYZZ);
+      HIP_TRY(launch_level_xyzz(in_aff, in, idx, xz[l & 1], bsum, counts, offsets, poff, L.K, np,
+                                l, st));
+      ph_lvl.end();
     }
   }
   ph_acc.end();
@@ -281,6 +300,13 @@ int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scala
   return MSM_OK;
 }
 
+int msm_ctx_set_affine_levels(msm_ctx* ctx, int levels) {
+  if (!ctx) return fail(MSM_ERR_ARG, "ctx is NULL%s");
+  if (levels < -1 || levels > MAX_LEVELS) return fail(MSM_ERR_ARG, "levels must be -1 .. 32%s");
+  ctx->affine_levels = levels;
+  return MSM_OK;
+}
+
 int msm_ctx_set_timing(msm_ctx* ctx, int enable) {
   if (!ctx) return fail(MSM_ERR_ARG, "ctx is NULL%s");
   ctx->timing = enable != 0;
@@ -291,8 +317,8 @@ int msm_ctx_timing_read(msm_ctx* ctx, msm_timing* out) {
   if (!ctx || !out) return fail(MSM_ERR_ARG, "NULL argument%s");
   memset(out, 0, sizeof *out);
   HIP_TRY(hipSetDevice(ctx->device));
-  double* slot[5] = {&out->sort_ms, &out->accumulate_ms, &out->level_kernel_ms, &out->reduce_ms,
-                     &out->final_ms};
+  double* slot[6] = {&out->sort_ms, &out->accumulate_ms, &out->level_kernel_ms, &out->reduce_ms,
+                     &out->final_ms, &out->xyzz_level_ms};
   for (const Span& sp : ctx->spans) {
     HIP_TRY(hipEventSynchronize(ctx->events[sp.e1]));
     float ms = 0.f;

@@ -39,12 +39,16 @@ hipError_t launch_scan(const uint32_t* counts, uint32_t n, int level, uint32_t* 
                        uint32_t* out, uint32_t* out2, hipStream_t s);
 hipError_t launch_stats(const uint32_t* counts, uint32_t K, msm_stats* st, hipStream_t s);
 hipError_t launch_bucket_init(const uint32_t* counts, const uint32_t* offsets, uint32_t K,
-                              const uint32_t* sorted_idx, const g1a* points, g1a* bsum,
+                              const uint32_t* sorted_idx, const g1a* points, xyzz_st* bsum,
                               hipStream_t s);
-hipError_t launch_level(int S, const g1a* in, const uint32_t* idx, g1a* out, g1a* bsum,
+hipError_t launch_level(int S, const g1a* in, const uint32_t* idx, g1a* out, xyzz_st* bsum,
                         const uint32_t* counts, const uint32_t* offsets, const uint32_t* poff,
                         uint32_t K, uint32_t npairs, int level, hipStream_t s);
-hipError_t launch_reduce(const g1a* bsum, uint32_t c, uint32_t nwin, uint32_t seg_len,
+hipError_t launch_level_xyzz(bool in_aff, const void* in, const uint32_t* idx, xyzz_st* out,
+                             xyzz_st* bsum, const uint32_t* counts, const uint32_t* offsets,
+                             const uint32_t* poff, uint32_t K, uint32_t npairs, int level,
+                             hipStream_t s);
+hipError_t launch_reduce(const xyzz_st* bsum, uint32_t c, uint32_t nwin, uint32_t seg_len,
                          uint32_t nseg, xyzz_st* seg, xyzz_st* win, hipStream_t s);
 hipError_t launch_final(const xyzz_st* win, uint32_t nwin, uint32_t c, g1a* out, hipStream_t s);
 hipError_t launch_from_scalars(const uint32_t* ks, uint32_t n, g1a* out, hipStream_t s);

@@ -205,6 +205,7 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 
 __global__ void __launch_bounds__(256) k_stats(const uint32_t* __restrict__ counts, uint32_t K,
                                                msm_stats* st) {
+  __shared__ uint32_t red[4][MAX_LEVELS + 2];
   uint32_t mx = 0, tot = 0;
   uint32_t pt[MAX_LEVELS];
 #pragma unroll
@@ -216,113 +217,34 @@ __global__ void __launch_bounds__(256) k_stats(const uint32_t* __restrict__ coun
 #pragma unroll
     for (int l = 0; l < MAX_LEVELS; l++) pt[l] += level_count(c, l) >> 1;
   }
+  // wave reductions, then the block's four waves through LDS, then one atomic each
+  const uint32_t wave = threadIdx.x >> 6;
+  const bool lead = (threadIdx.x & 63) == 0;
   mx = wave_max(mx);
   tot = wave_sum(tot);
-  bool lead = (threadIdx.x & 63) == 0;
   if (lead) {
-    atomicMax(&st->max_count, mx);
-    atomicAdd(&st->total, tot);
+    red[wave][MAX_LEVELS] = mx;
+    red[wave][MAX_LEVELS + 1] = tot;
   }
 #pragma unroll
   for (int l = 0; l < MAX_LEVELS; l++) {
-    uint32_t s = wave_sum(pt[l]);
-    if (lead && s) atomicAdd(&st->pairs[l], s);
+    uint32_t v = wave_sum(pt[l]);
+    if (lead) red[wave][l] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < MAX_LEVELS + 2) {
+    const uint32_t i = threadIdx.x;
+    uint32_t a = red[0][i], b = red[1][i], c = red[2][i], d = red[3][i];
+    if (i == MAX_LEVELS) {
+      atomicMax(&st->max_count, max(max(a, b), max(c, d)));
+    } else {
+      uint32_t v = a + b + c + d;
+      if (v) atomicAdd(i == MAX_LEVELS + 1 ? &st->total : &st->pairs[i], v);
+    }
   }
 }
 
 // ------------------------------------------------------------------ buckets
-__global__ void __launch_bounds__(256) k_bucket_init(const uint32_t* __restrict__ counts,
-                                                     const uint32_t* __restrict__ offsets, uint32_t K,
-                                                     const uint32_t* __restrict__ sorted_idx,
-                                                     const g1a* __restrict__ points,
-                                                     g1a* __restrict__ bsum) {
-  uint32_t k = blockIdx.x * blockDim.x + threadIdx.x;
-  if (k >= K) return;
-  uint32_t c = counts[k];
-  if (c == 0) {
-    aff_store(bsum + k, aff_inf());
-  } else if (c == 1) {
-    aff_store(bsum + k, aff_load(points + sorted_idx[offsets[k]]));
-  }
-}
-
-// Largest k in [0, n) with a[k] <= x, for a non-decreasing a with a[0] <= x: a
-// branch-free binary search with a fixed trip count (n <= 2^SEARCH_STEPS), so it can
-// sit inside fully unrolled slot loops.
-__device__ __forceinline__ uint32_t last_le(const uint32_t* a, uint32_t n, uint32_t x) {
-  uint32_t k = 0;
-#pragma unroll
-  for (int b = SEARCH_STEPS - 1; b >= 0; b--) {
-    uint32_t t = k + (1u << b);
-    k = (t < n && a[t] <= x) ? t : k;
-  }
-  return k;
-}
-
-// Operands of pair-tree level `level`: pair m of bucket k adds elements 2m and 2m+1
-// of the bucket's list at this level. Level 0 reads the points through sorted_idx;
-// later levels read the previous level's buffer, where bucket k's elements sit at
-// offsets[k] + i. Output m goes to offsets[k] + m, or straight to the bucket sum
-// when the bucket has exactly two elements left; the last pair of an odd list also
-// moves the unpaired element along.
-template <int S>
-struct LevelSrc {
-  const g1a* in;
-  const uint32_t* idx;
-  g1a* out;
-  g1a* bsum;
-  const uint32_t* counts;
-  const uint32_t* offsets;
-  int level;
-  uint32_t ea[S], eb[S], kb[S], mm[S];
-
-  __device__ __forceinline__ uint32_t elem(uint32_t pos) const { return idx ? idx[pos] : pos; }
-  __device__ __forceinline__ aff a(int s) const { return aff_load(in + ea[s]); }
-  __device__ __forceinline__ aff b(int s) const { return aff_load(in + eb[s]); }
-  __device__ __forceinline__ void put(int s, const aff& r) const {
-    uint32_t k = kb[s], m = mm[s];
-    uint32_t cl = level_count(counts[k], level);
-    uint32_t off = offsets[k];
-    if (cl == 2) {
-      aff_store(bsum + k, r);
-      return;
-    }
-    aff_store(out + off + m, r);
-    uint32_t np = cl >> 1;
-    if ((cl & 1u) && m == np - 1) aff_store(out + off + np, aff_load(in + elem(off + cl - 1)));
-  }
-};
-
-template <int S>
-__global__ void __launch_bounds__(256) k_level(const g1a* __restrict__ in,
-                                               const uint32_t* __restrict__ idx, g1a* out, g1a* bsum,
-                                               const uint32_t* __restrict__ counts,
-                                               const uint32_t* __restrict__ offsets,
-                                               const uint32_t* __restrict__ poff, uint32_t K,
-                                               uint32_t npairs, int level) {
-  uint64_t p0 = (uint64_t)(blockIdx.x * blockDim.x + threadIdx.x) * S;
-  if (p0 >= npairs) return;
-  int cnt = (int)min((uint64_t)S, (uint64_t)npairs - p0);
-  LevelSrc<S> src{in, idx, out, bsum, counts, offsets, level, {}, {}, {}, {}};
-  // bucket of the first pair; later pairs stay in it or move to a later bucket
-  uint32_t k = last_le(poff, K, (uint32_t)p0);
-#pragma unroll
-  for (int s = 0; s < S; s++) {
-    if (s < cnt) {
-      uint32_t p = (uint32_t)p0 + s;
-      if (p >= poff[k + 1]) k = last_le(poff, K, p);
-      uint32_t m = p - poff[k];
-      src.kb[s] = k;
-      src.mm[s] = m;
-      uint32_t pos = offsets[k] + 2 * m;
-      src.ea[s] = src.elem(pos);
-      src.eb[s] = src.elem(pos + 1);
-    }
-  }
-  batch_affine_add<S>(src, cnt);
-}
-
-// ------------------------------------------------------------------ reduction
 __device__ __forceinline__ void xyzz_store(xyzz_st* p, const xyzz& a) {
 #pragma unroll
   for (int i = 0; i < 8; i++) {
@@ -345,10 +267,156 @@ __device__ __forceinline__ xyzz xyzz_load(const xyzz_st* p) {
   return a;
 }
 
+__global__ void __launch_bounds__(256) k_bucket_init(const uint32_t* __restrict__ counts,
+                                                     const uint32_t* __restrict__ offsets, uint32_t K,
+                                                     const uint32_t* __restrict__ sorted_idx,
+                                                     const g1a* __restrict__ points,
+                                                     xyzz_st* __restrict__ bsum) {
+  uint32_t k = blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= K) return;
+  uint32_t c = counts[k];
+  if (c == 0) {
+    xyzz_store(bsum + k, xyzz_inf());
+  } else if (c == 1) {
+    xyzz_store(bsum + k, xyzz_from_aff(aff_load(points + sorted_idx[offsets[k]])));
+  }
+}
+
+// Start of bucket k's elements in the buffers of pair-tree levels >= 1: a level-l
+// bucket holds at most ceil(count / 2) elements, and (offset + k) / 2 leaves exactly
+// that much room before the next bucket.
+__device__ __forceinline__ uint32_t half_base(uint32_t off, uint32_t k) { return (off + k) >> 1; }
+
+// Largest k in [0, n) with a[k] <= x, for a non-decreasing a with a[0] <= x: a
+// branch-free binary search with a fixed trip count (n <= 2^SEARCH_STEPS), so it can
+// sit inside fully unrolled slot loops.
+__device__ __forceinline__ uint32_t last_le(const uint32_t* a, uint32_t n, uint32_t x) {
+  uint32_t k = 0;
+#pragma unroll
+  for (int b = SEARCH_STEPS - 1; b >= 0; b--) {
+    uint32_t t = k + (1u << b);
+    k = (t < n && a[t] <= x) ? t : k;
+  }
+  return k;
+}
+
+// Operands of pair-tree level `level`: pair m of bucket k adds elements 2m and 2m+1
+// of the bucket's list at this level. Level 0 reads the points through sorted_idx
+// (bucket k's entries at offsets[k] + i); later levels read the previous level's
+// buffer (entries at half_base(offsets[k], k) + i). Output m goes to
+// half_base + m, or straight to the bucket sum when the bucket has exactly two
+// elements left; the last pair of an odd list also moves the unpaired element along.
+template <int S>
+struct LevelSrc {
+  const g1a* in;
+  const uint32_t* idx;
+  g1a* out;
+  xyzz_st* bsum;
+  const uint32_t* counts;
+  const uint32_t* offsets;
+  int level;
+  uint32_t ea[S], eb[S], kb[S], mm[S];
+
+  __device__ __forceinline__ uint32_t base(uint32_t k) const {
+    return idx ? offsets[k] : half_base(offsets[k], k);
+  }
+  __device__ __forceinline__ uint32_t elem(uint32_t pos) const { return idx ? idx[pos] : pos; }
+  __device__ __forceinline__ aff a(int s) const { return aff_load(in + ea[s]); }
+  __device__ __forceinline__ aff b(int s) const { return aff_load(in + eb[s]); }
+  __device__ __forceinline__ void put(int s, const aff& r) const {
+    uint32_t k = kb[s], m = mm[s];
+    uint32_t cl = level_count(counts[k], level);
+    if (cl == 2) {
+      xyzz_store(bsum + k, xyzz_from_aff(r));
+      return;
+    }
+    uint32_t ob = half_base(offsets[k], k);
+    aff_store(out + ob + m, r);
+    uint32_t np = cl >> 1;
+    if ((cl & 1u) && m == np - 1) aff_store(out + ob + np, aff_load(in + elem(base(k) + cl - 1)));
+  }
+};
+
+template <int S>
+__global__ void __launch_bounds__(256) k_level(const g1a* __restrict__ in,
+                                               const uint32_t* __restrict__ idx, g1a* out, xyzz_st* bsum,
+                                               const uint32_t* __restrict__ counts,
+                                               const uint32_t* __restrict__ offsets,
+                                               const uint32_t* __restrict__ poff, uint32_t K,
+                                               uint32_t npairs, int level) {
+  uint64_t p0 = (uint64_t)(blockIdx.x * blockDim.x + threadIdx.x) * S;
+  if (p0 >= npairs) return;
+  int cnt = (int)min((uint64_t)S, (uint64_t)npairs - p0);
+  LevelSrc<S> src{in, idx, out, bsum, counts, offsets, level, {}, {}, {}, {}};
+  // bucket of the first pair; later pairs stay in it or move to a later bucket
+  uint32_t k = last_le(poff, K, (uint32_t)p0);
+#pragma unroll
+  for (int s = 0; s < S; s++) {
+    if (s < cnt) {
+      uint32_t p = (uint32_t)p0 + s;
+      if (p >= poff[k + 1]) k = last_le(poff, K, p);
+      uint32_t m = p - poff[k];
+      src.kb[s] = k;
+      src.mm[s] = m;
+      uint32_t pos = src.base(k) + 2 * m;
+      src.ea[s] = src.elem(pos);
+      src.eb[s] = src.elem(pos + 1);
+    }
+  }
+  batch_affine_add<S>(src, cnt);
+}
+
+
+// Pair-tree level in XYZZ coordinates, one pair per lane and no inversion: the
+// deep levels have few pairs, so their time is one addition's latency rather than an
+// inversion's. Inputs are affine (IN_AFF, the output of a batched-affine level, or
+// the points themselves through sorted_idx at level 0) or XYZZ; outputs are XYZZ.
+template <bool IN_AFF>
+__global__ void __launch_bounds__(128) k_level_xyzz(const void* __restrict__ in_,
+                                                    const uint32_t* __restrict__ idx,
+                                                    xyzz_st* __restrict__ out, xyzz_st* bsum,
+                                                    const uint32_t* __restrict__ counts,
+                                                    const uint32_t* __restrict__ offsets,
+                                                    const uint32_t* __restrict__ poff, uint32_t K,
+                                                    uint32_t npairs, int level) {
+  uint32_t p = blockIdx.x * blockDim.x + threadIdx.x;
+  if (p >= npairs) return;
+  uint32_t k = last_le(poff, K, p);
+  uint32_t m = p - poff[k];
+  uint32_t off = offsets[k];
+  uint32_t base = idx ? off : half_base(off, k);
+  uint32_t cl = level_count(counts[k], level);
+  auto load = [&](uint32_t pos) -> xyzz {
+    if (IN_AFF) {
+      const g1a* in = reinterpret_cast<const g1a*>(in_);
+      return xyzz_from_aff(aff_load(in + (idx ? idx[pos] : pos)));
+    }
+    return xyzz_load(reinterpret_cast<const xyzz_st*>(in_) + pos);
+  };
+  xyzz r;
+  if (IN_AFF) {
+    const g1a* in = reinterpret_cast<const g1a*>(in_);
+    uint32_t ia = base + 2 * m;
+    r = xyzz_add_aff(xyzz_from_aff(aff_load(in + (idx ? idx[ia] : ia))),
+                     aff_load(in + (idx ? idx[ia + 1] : ia + 1)));
+  } else {
+    r = xyzz_add(load(base + 2 * m), load(base + 2 * m + 1));
+  }
+  if (cl == 2) {
+    xyzz_store(bsum + k, r);
+    return;
+  }
+  uint32_t ob = half_base(off, k);
+  xyzz_store(out + ob + m, r);
+  uint32_t np = cl >> 1;
+  if ((cl & 1u) && m == np - 1) xyzz_store(out + ob + np, load(base + cl - 1));
+}
+
+// ------------------------------------------------------------------ reduction
 // Segment s of window j covers buckets [lo, hi). With T = sum of the segment's
 // buckets and R = sum_b (b - lo + 1) B_b (a running sum from the top bucket down),
 // the segment's share of W_j = sum_b b B_b is R + (lo - 1) T.
-__global__ void __launch_bounds__(128) k_rsum_seg(const g1a* __restrict__ bsum, uint32_t c,
+__global__ void __launch_bounds__(128) k_rsum_seg(const xyzz_st* __restrict__ bsum, uint32_t c,
                                                   uint32_t nwin, uint32_t seg_len, uint32_t nseg,
                                                   xyzz_st* __restrict__ seg_out) {
   uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
@@ -357,7 +425,7 @@ __global__ void __launch_bounds__(128) k_rsum_seg(const g1a* __restrict__ bsum, 
   uint32_t lo = max(1u, s * seg_len), hi = min(1u << c, (s + 1) * seg_len);
   xyzz T = xyzz_inf(), R = xyzz_inf();
   for (uint32_t b = hi; b-- > lo;) {
-    T = xyzz_add_aff(T, aff_load(bsum + ((size_t)j << c) + b));
+    T = xyzz_add(T, xyzz_load(bsum + ((size_t)j << c) + b));
     R = xyzz_add(R, T);
   }
   xyzz_store(seg_out + t, xyzz_add(R, xyzz_mul_small(T, lo - 1)));
@@ -381,15 +449,110 @@ __global__ void __launch_bounds__(256) k_rsum_win(const xyzz_st* __restrict__ se
   if (t == 0) xyzz_store(win + j, acc);
 }
 
-// Q = sum_j 2^(c j) W_j by Horner from the top window, then to affine.
-__global__ void k_final(const xyzz_st* __restrict__ win, uint32_t nwin, uint32_t c, g1a* out) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+// ---- window combine: one wave, independent products spread over its lanes ----
+// The combine is one long chain (c (W - 1) doublings), so its time is latency, not
+// throughput. Each XYZZ doubling has 9 products but only 3 dependent rounds, and an
+// addition 12 products in 4 rounds; lane i computes product i of a round and every
+// lane reads all results back with v_readlane, so a step costs 3 (or 4) product
+// latencies instead of 9 (or 12). All lanes hold the same point, so every branch is
+// uniform.
+
+__device__ __forceinline__ fp fp_from_lane(const fp& v, int src) {
+  fp r;
+#pragma unroll
+  for (int i = 0; i < 8; i++) r.v[i] = __builtin_amdgcn_readlane(v.v[i], src);
+  return r;
+}
+
+// Operand k for this lane (lanes beyond the list take the last entry).
+template <int N>
+__device__ __forceinline__ fp fp_pick(int lane, const fp (&opt)[N]) {
+  fp r = opt[N - 1];
+#pragma unroll
+  for (int k = N - 2; k >= 0; k--) {
+    const bool hit = (lane == k);
+#pragma unroll
+    for (int i = 0; i < 8; i++) r.v[i] = hit ? opt[k].v[i] : r.v[i];
+  }
+  return r;
+}
+
+__device__ __forceinline__ xyzz wave_dbl(const xyzz& p, int lane) {
+  const fp U = fp_dbl(p.Y);
+  fp r;
+  {  // V = U^2, XX = X^2
+    const fp a[2] = {U, p.X};
+    const fp x = fp_pick(lane, a);
+    r = fp_mul(x, x);
+  }
+  const fp V = fp_from_lane(r, 0), XX = fp_from_lane(r, 1);
+  const fp M = fp_add(fp_dbl(XX), XX);
+  {  // W = U V, S = X V, MM = M^2, ZZ3 = V ZZ
+    const fp a[4] = {U, p.X, M, V}, b[4] = {V, V, M, p.ZZ};
+    r = fp_mul(fp_pick(lane, a), fp_pick(lane, b));
+  }
+  const fp W = fp_from_lane(r, 0), S = fp_from_lane(r, 1), MM = fp_from_lane(r, 2);
+  xyzz q;
+  q.ZZ = fp_from_lane(r, 3);
+  q.X = fp_sub(fp_sub(MM, S), S);
+  {  // ZZZ3 = W ZZZ, WY = W Y, T = M (S - X3)
+    const fp a[3] = {W, W, M}, b[3] = {p.ZZZ, p.Y, fp_sub(S, q.X)};
+    r = fp_mul(fp_pick(lane, a), fp_pick(lane, b));
+  }
+  q.ZZZ = fp_from_lane(r, 0);
+  q.Y = fp_sub(fp_from_lane(r, 2), fp_from_lane(r, 1));
+  return q;
+}
+
+__device__ __forceinline__ xyzz wave_add(const xyzz& p, const xyzz& q, int lane) {
+  if (xyzz_is_inf(q)) return p;
+  if (xyzz_is_inf(p)) return q;
+  fp r;
+  {  // U1, U2, S1, S2, ZZ1 ZZ2, ZZZ1 ZZZ2
+    const fp a[6] = {p.X, q.X, p.Y, q.Y, p.ZZ, p.ZZZ}, b[6] = {q.ZZ, p.ZZ, q.ZZZ, p.ZZZ, q.ZZ, q.ZZZ};
+    r = fp_mul(fp_pick(lane, a), fp_pick(lane, b));
+  }
+  const fp U1 = fp_from_lane(r, 0), U2 = fp_from_lane(r, 1), S1 = fp_from_lane(r, 2);
+  const fp S2 = fp_from_lane(r, 3), ZZ12 = fp_from_lane(r, 4), ZZZ12 = fp_from_lane(r, 5);
+  const fp P = fp_sub(U2, U1), R = fp_sub(S2, S1);
+  if (fp_is_zero(P)) {
+    if (fp_is_zero(R)) return wave_dbl(p, lane);
+    return xyzz_inf();
+  }
+  {  // PP = P^2, RR = R^2
+    const fp a[2] = {P, R};
+    const fp x = fp_pick(lane, a);
+    r = fp_mul(x, x);
+  }
+  const fp PP = fp_from_lane(r, 0), RR = fp_from_lane(r, 1);
+  {  // PPP = P PP, Q = U1 PP, ZZ3 = ZZ12 PP
+    const fp a[3] = {P, U1, ZZ12};
+    r = fp_mul(fp_pick(lane, a), PP);
+  }
+  const fp PPP = fp_from_lane(r, 0), Q = fp_from_lane(r, 1);
+  xyzz o;
+  o.ZZ = fp_from_lane(r, 2);
+  o.X = fp_sub(fp_sub(fp_sub(RR, PPP), Q), Q);
+  {  // ZZZ3 = ZZZ12 PPP, S1 PPP, R (Q - X3)
+    const fp a[3] = {ZZZ12, S1, R}, b[3] = {PPP, PPP, fp_sub(Q, o.X)};
+    r = fp_mul(fp_pick(lane, a), fp_pick(lane, b));
+  }
+  o.ZZZ = fp_from_lane(r, 0);
+  o.Y = fp_sub(fp_from_lane(r, 2), fp_from_lane(r, 1));
+  return o;
+}
+
+// Q = sum_j 2^(c j) W_j by Horner from the top window, then to affine. One wave.
+__global__ void __launch_bounds__(64) k_final(const xyzz_st* __restrict__ win, uint32_t nwin,
+                                              uint32_t c, g1a* out) {
+  const int lane = threadIdx.x;
   xyzz q = xyzz_load(win + nwin - 1);
   for (int j = (int)nwin - 2; j >= 0; j--) {
-    for (uint32_t b = 0; b < c; b++) q = xyzz_dbl(q);
-    q = xyzz_add(q, xyzz_load(win + j));
+    for (uint32_t b = 0; b < c; b++) q = wave_dbl(q, lane);
+    q = wave_add(q, xyzz_load(win + j), lane);
   }
-  aff_store(out, xyzz_to_aff(q));
+  const aff a = xyzz_to_aff(q);
+  if (lane == 0) aff_store(out, a);
 }
 
 // ------------------------------------------------------------------ generator
@@ -502,14 +665,14 @@ hipError_t launch_stats(const uint32_t* counts, uint32_t K, msm_stats* st, hipSt
 }
 
 hipError_t launch_bucket_init(const uint32_t* counts, const uint32_t* offsets, uint32_t K,
-                              const uint32_t* sorted_idx, const g1a* points, g1a* bsum,
+                              const uint32_t* sorted_idx, const g1a* points, xyzz_st* bsum,
                               hipStream_t s) {
   k_bucket_init<<<grid_for(K, 256), 256, 0, s>>>(counts, offsets, K, sorted_idx, points, bsum);
   return hipGetLastError();
 }
 
 template <int S>
-static hipError_t level_S(const g1a* in, const uint32_t* idx, g1a* out, g1a* bsum,
+static hipError_t level_S(const g1a* in, const uint32_t* idx, g1a* out, xyzz_st* bsum,
                           const uint32_t* counts, const uint32_t* offsets, const uint32_t* poff,
                           uint32_t K, uint32_t npairs, int level, hipStream_t s) {
   size_t threads = (npairs + S - 1) / S;
@@ -518,7 +681,7 @@ static hipError_t level_S(const g1a* in, const uint32_t* idx, g1a* out, g1a* bsu
   return hipGetLastError();
 }
 
-hipError_t launch_level(int S, const g1a* in, const uint32_t* idx, g1a* out, g1a* bsum,
+hipError_t launch_level(int S, const g1a* in, const uint32_t* idx, g1a* out, xyzz_st* bsum,
                         const uint32_t* counts, const uint32_t* offsets, const uint32_t* poff,
                         uint32_t K, uint32_t npairs, int level, hipStream_t s) {
   switch (S) {
@@ -530,7 +693,19 @@ hipError_t launch_level(int S, const g1a* in, const uint32_t* idx, g1a* out, g1a
   }
 }
 
-hipError_t launch_reduce(const g1a* bsum, uint32_t c, uint32_t nwin, uint32_t seg_len,
+hipError_t launch_level_xyzz(bool in_aff, const void* in, const uint32_t* idx, xyzz_st* out,
+                             xyzz_st* bsum, const uint32_t* counts, const uint32_t* offsets,
+                             const uint32_t* poff, uint32_t K, uint32_t npairs, int level,
+                             hipStream_t s) {
+  unsigned g = grid_for(npairs, 128);
+  if (in_aff)
+    k_level_xyzz<true><<<g, 128, 0, s>>>(in, idx, out, bsum, counts, offsets, poff, K, npairs, level);
+  else
+    k_level_xyzz<false><<<g, 128, 0, s>>>(in, idx, out, bsum, counts, offsets, poff, K, npairs, level);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce(const xyzz_st* bsum, uint32_t c, uint32_t nwin, uint32_t seg_len,
                          uint32_t nseg, xyzz_st* seg, xyzz_st* win, hipStream_t s) {
   k_rsum_seg<<<grid_for((size_t)nwin * nseg, 128), 128, 0, s>>>(bsum, c, nwin, seg_len, nseg, seg);
   k_rsum_win<<<nwin, 256, 0, s>>>(seg, nseg, win);

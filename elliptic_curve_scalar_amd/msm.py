@@ -31,6 +31,7 @@ SYMBOLS = {
     "msm_run": (_I, [_P, _P, _P, _S, _I, _I, _P, _S, _P, _P]),
     "msm": (_I, [_P, _P, _S, _I, _P]),
     "msm_g1_from_scalars": (_I, [_P, _S, _P, _P]),
+    "msm_ctx_set_affine_levels": (_I, [_P, _I]),
     "msm_ctx_set_timing": (_I, [_P, _I]),
     "msm_ctx_timing_read": (_I, [_P, _P]),
     "msm_test_fp": (_I, [_I, _P, _P, _P, _S, _P]),
@@ -46,7 +47,7 @@ class Timing(ctypes.Structure):
                 ("level_kernel_ms", ctypes.c_double), ("reduce_ms", ctypes.c_double),
                 ("final_ms", ctypes.c_double), ("runs", ctypes.c_int),
                 ("level_launches", ctypes.c_int), ("level_pairs", ctypes.c_uint64),
-                ("level_lanes", ctypes.c_uint64)]
+                ("level_lanes", ctypes.c_uint64), ("xyzz_level_ms", ctypes.c_double)]
 
 
 class MsmError(RuntimeError):
@@ -120,6 +121,10 @@ class Context:
             self.close()
         except Exception:
             pass
+
+    def set_affine_levels(self, levels: int):
+        """Leading pair-tree levels done with batched affine adds (-1: all)."""
+        _check(lib().msm_ctx_set_affine_levels(self._h, int(levels)))
 
     def set_timing(self, enable: bool = True):
         _check(lib().msm_ctx_set_timing(self._h, int(bool(enable))))

@@ -114,6 +114,15 @@ int msm(const msm_g1_affine* d_points, const uint32_t* d_scalars, size_t n, int 
 int msm_g1_from_scalars(const uint32_t* d_k, size_t n, msm_g1_affine* d_out, void* stream);
 
 /*
+ * Pair-tree schedule: the first `levels` levels of every bucket's pair tree use the
+ * batched affine adder (S adds per lane share one inversion); the remaining levels
+ * use XYZZ coordinates, one addition per lane and no inversion, which shortens the
+ * deep levels where few pairs are left. -1 makes every level affine. Default 1.
+ * Returns MSM_ERR_ARG for a NULL ctx or levels outside -1 .. 32.
+ */
+int msm_ctx_set_affine_levels(msm_ctx* ctx, int levels);
+
+/*
  * Phase timing. When enabled on a context, msm_run records HIP events on its stream
  * around each phase: sort (count, scan, scatter), accumulate (pair-tree levels, with
  * every level kernel launch bracketed on its own), reduce (running sums) and final
@@ -131,6 +140,7 @@ typedef struct msm_timing {
   int level_launches;      /* level kernel launches summed */
   uint64_t level_pairs;    /* affine additions done by those launches */
   uint64_t level_lanes;    /* lanes that ran them (one inversion each) */
+  double xyzz_level_ms;    /* pair-tree levels done in XYZZ coordinates */
 } msm_timing;
 
 int msm_ctx_set_timing(msm_ctx* ctx, int enable);

@@ -80,6 +80,24 @@ def test_knob_invariance():
             assert np.array_equal(_gpu_msm(pts, w["scalars"], c, S), want), (c, S)
 
 
+def test_pair_tree_schedule_invariance():
+    """Batched-affine levels vs XYZZ levels: every split gives the same bits."""
+    from elliptic_curve_scalar_amd import msm as M
+    w = wl.generate("n262144_c13_edge", n=8000)
+    pts = oracle.g1_from_scalars(w["dlogs"])
+    want = oracle.msm_pippenger(pts, w["scalars"], 13)
+    ctx = M.Context(0)
+    try:
+        for levels in (-1, 0, 1, 2, 5):
+            ctx.set_affine_levels(levels)
+            for S in (4, 32):
+                say("affine levels", levels, "S", S)
+                got = to_host(ctx.run(to_dev(pts), to_dev(w["scalars"]), 13, S))
+                assert np.array_equal(got, want), (levels, S)
+    finally:
+        ctx.close()
+
+
 def test_sync_entry_point():
     M = _msm()
     w = wl.generate("n256_c8")
