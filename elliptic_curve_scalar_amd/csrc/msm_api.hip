@@ -30,15 +30,16 @@ int fail(int code, const char* fmt, const char* detail = "") {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-int num_windows(int c) { return (254 + c - 1) / c; }
+// Signed c-bit digits of scalars below 2^254 need W c >= 255.
+int num_windows(int c) { return (255 + c - 1) / c; }
 
 // Buckets per running-sum segment: enough segments to spread the reduction over the
 // chip, never fewer than 4 buckets per segment.
 uint32_t segment_length(int c, int nwin) {
-  size_t total = ((size_t)nwin) << c;
+  size_t total = ((size_t)nwin) << (c - 1);
   uint32_t g = 4;
   while ((size_t)g * 32768 < total && g < 256) g <<= 1;
-  if (g > (1u << c)) g = 1u << c;
+  if (g > (1u << (c - 1))) g = 1u << (c - 1);
   return g;
 }
 
@@ -53,9 +54,9 @@ struct Layout {
 Layout plan(size_t n, int c) {
   Layout L;
   L.nwin = (uint32_t)num_windows(c);
-  L.K = L.nwin << c;
+  L.K = L.nwin << (c - 1);  // 2^(c-1) bucket slots per window (signed digits)
   L.seg_len = segment_length(c, (int)L.nwin);
-  L.nseg = ((1u << c) + L.seg_len - 1) / L.seg_len;
+  L.nseg = ((1u << (c - 1)) + L.seg_len - 1) / L.seg_len;
   L.E_max = n * L.nwin;
   L.half = (L.E_max + L.K) / 2 + 1;  // elements of a level >= 1 buffer
   size_t nb = (L.K + SCAN_TILE - 1) / SCAN_TILE + 1;
@@ -252,7 +253,7 @@ int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scala
   ph_sort.end();
   HIP_TRY(hipStreamSynchronize(st));
   const msm_stats hs = *ctx->host_stats;
-  if (hs.range_flag) return fail(MSM_ERR_RANGE, "a scalar has a bit at or above W*c set%s");
+  if (hs.range_flag) return fail(MSM_ERR_RANGE, "a scalar is not below 2^(W*c-1)%s");
 
   // accumulate: pair-tree levels until every bucket holds one point
   PhaseMark ph_acc(ctx, st, PH_ACCUM);

@@ -69,19 +69,40 @@ __global__ void k_fill_u32(uint32_t* p, size_t n, uint32_t v) {
   if (i < n) p[i] = v;
 }
 
+// Signed window digits: s = sum_j d_j 2^(c j) with d_j in [-2^(c-1), 2^(c-1)], found
+// from the least significant window up with a carry (a window above 2^(c-1) becomes
+// d - 2^c and carries 1); the top window is not recoded, which is why scalars must be
+// below 2^(W c - 1). -P is free in affine coordinates, so a window needs only 2^(c-1)
+// buckets, one per |d|. Calls f(j, slot, negative) for every non-zero digit, with
+// slot = |d| - 1.
+template <class F>
+__device__ __forceinline__ void for_each_signed_digit(const sc256& s, uint32_t c, uint32_t nwin,
+                                                      F&& f) {
+  const uint32_t half = 1u << (c - 1);
+  uint32_t carry = 0;
+  for (uint32_t j = 0; j < nwin; j++) {
+    const uint32_t raw = window_digit(s, j * c, c) + carry;
+    const bool neg = (j + 1 < nwin) && raw > half;
+    carry = neg ? 1u : 0u;
+    const uint32_t mag = neg ? (1u << c) - raw : raw;
+    if (mag) f(j, mag - 1, neg);
+  }
+}
+
 __global__ void __launch_bounds__(256) k_hist(const uint32_t* __restrict__ scalars, uint32_t n,
                                               uint32_t c, uint32_t nwin,
                                               uint32_t* __restrict__ counts, msm_stats* st) {
   uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   sc256 s = load_scalar(scalars, i);
-  if (above_bits(s, nwin * c)) atomicOr(&st->range_flag, 1u);
-  for (uint32_t j = 0; j < nwin; j++) {
-    uint32_t d = window_digit(s, j * c, c);
-    if (d) atomicAdd(&counts[(j << c) | d], 1u);
-  }
+  if (above_bits(s, nwin * c - 1)) atomicOr(&st->range_flag, 1u);
+  const uint32_t sh = c - 1;
+  for_each_signed_digit(s, c, nwin, [&](uint32_t j, uint32_t slot, bool) {
+    atomicAdd(&counts[(j << sh) | slot], 1u);
+  });
 }
 
+// Bucket lists hold point indices with the digit's sign in bit 31.
 __global__ void __launch_bounds__(256) k_scatter(const uint32_t* __restrict__ scalars, uint32_t n,
                                                  uint32_t c, uint32_t nwin,
                                                  uint32_t* __restrict__ cursor,
@@ -89,13 +110,11 @@ __global__ void __launch_bounds__(256) k_scatter(const uint32_t* __restrict__ sc
   uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   sc256 s = load_scalar(scalars, i);
-  for (uint32_t j = 0; j < nwin; j++) {
-    uint32_t d = window_digit(s, j * c, c);
-    if (d) {
-      uint32_t pos = atomicAdd(&cursor[(j << c) | d], 1u);
-      sorted_idx[pos] = i;
-    }
-  }
+  const uint32_t sh = c - 1;
+  for_each_signed_digit(s, c, nwin, [&](uint32_t j, uint32_t slot, bool neg) {
+    uint32_t pos = atomicAdd(&cursor[(j << sh) | slot], 1u);
+    sorted_idx[pos] = i | (neg ? 0x80000000u : 0u);
+  });
 }
 
 // ------------------------------------------------------------------ scan
@@ -245,6 +264,14 @@ __global__ void __launch_bounds__(256) k_stats(const uint32_t* __restrict__ coun
 }
 
 // ------------------------------------------------------------------ buckets
+// Point named by a bucket-list entry: index in bits 0..30, negated when bit 31 is set
+// (the negative of (x, y) is (x, -y); the infinity encoding (0, 0) stays put).
+__device__ __forceinline__ aff load_entry(const g1a* points, uint32_t e) {
+  aff a = aff_load(points + (e & 0x7fffffffu));
+  if (e >> 31) a.y = fp_neg(a.y);
+  return a;
+}
+
 __device__ __forceinline__ void xyzz_store(xyzz_st* p, const xyzz& a) {
 #pragma unroll
   for (int i = 0; i < 8; i++) {
@@ -278,7 +305,7 @@ __global__ void __launch_bounds__(256) k_bucket_init(const uint32_t* __restrict_
   if (c == 0) {
     xyzz_store(bsum + k, xyzz_inf());
   } else if (c == 1) {
-    xyzz_store(bsum + k, xyzz_from_aff(aff_load(points + sorted_idx[offsets[k]])));
+    xyzz_store(bsum + k, xyzz_from_aff(load_entry(points, sorted_idx[offsets[k]])));
   }
 }
 
@@ -321,8 +348,9 @@ struct LevelSrc {
     return idx ? offsets[k] : half_base(offsets[k], k);
   }
   __device__ __forceinline__ uint32_t elem(uint32_t pos) const { return idx ? idx[pos] : pos; }
-  __device__ __forceinline__ aff a(int s) const { return aff_load(in + ea[s]); }
-  __device__ __forceinline__ aff b(int s) const { return aff_load(in + eb[s]); }
+  __device__ __forceinline__ aff get(uint32_t e) const { return idx ? load_entry(in, e) : aff_load(in + e); }
+  __device__ __forceinline__ aff a(int s) const { return get(ea[s]); }
+  __device__ __forceinline__ aff b(int s) const { return get(eb[s]); }
   __device__ __forceinline__ void put(int s, const aff& r) const {
     uint32_t k = kb[s], m = mm[s];
     uint32_t cl = level_count(counts[k], level);
@@ -333,7 +361,7 @@ struct LevelSrc {
     uint32_t ob = half_base(offsets[k], k);
     aff_store(out + ob + m, r);
     uint32_t np = cl >> 1;
-    if ((cl & 1u) && m == np - 1) aff_store(out + ob + np, aff_load(in + elem(base(k) + cl - 1)));
+    if ((cl & 1u) && m == np - 1) aff_store(out + ob + np, get(elem(base(k) + cl - 1)));
   }
 };
 
@@ -386,19 +414,18 @@ __global__ void __launch_bounds__(128) k_level_xyzz(const void* __restrict__ in_
   uint32_t off = offsets[k];
   uint32_t base = idx ? off : half_base(off, k);
   uint32_t cl = level_count(counts[k], level);
+  auto load_aff = [&](uint32_t pos) -> aff {
+    const g1a* in = reinterpret_cast<const g1a*>(in_);
+    return idx ? load_entry(in, idx[pos]) : aff_load(in + pos);
+  };
   auto load = [&](uint32_t pos) -> xyzz {
-    if (IN_AFF) {
-      const g1a* in = reinterpret_cast<const g1a*>(in_);
-      return xyzz_from_aff(aff_load(in + (idx ? idx[pos] : pos)));
-    }
+    if (IN_AFF) return xyzz_from_aff(load_aff(pos));
     return xyzz_load(reinterpret_cast<const xyzz_st*>(in_) + pos);
   };
   xyzz r;
   if (IN_AFF) {
-    const g1a* in = reinterpret_cast<const g1a*>(in_);
     uint32_t ia = base + 2 * m;
-    r = xyzz_add_aff(xyzz_from_aff(aff_load(in + (idx ? idx[ia] : ia))),
-                     aff_load(in + (idx ? idx[ia + 1] : ia + 1)));
+    r = xyzz_add_aff(xyzz_from_aff(load_aff(ia)), load_aff(ia + 1));
   } else {
     r = xyzz_add(load(base + 2 * m), load(base + 2 * m + 1));
   }
@@ -413,22 +440,24 @@ __global__ void __launch_bounds__(128) k_level_xyzz(const void* __restrict__ in_
 }
 
 // ------------------------------------------------------------------ reduction
-// Segment s of window j covers buckets [lo, hi). With T = sum of the segment's
-// buckets and R = sum_b (b - lo + 1) B_b (a running sum from the top bucket down),
-// the segment's share of W_j = sum_b b B_b is R + (lo - 1) T.
+// Window j has 2^(c-1) bucket slots; slot b holds the points whose digit has
+// magnitude b + 1, so W_j = sum_b (b + 1) B_b. Segment s covers slots [lo, hi): with
+// T = sum of its slots and R = sum_b (b - lo + 1) B_b (a running sum from the top slot
+// down), its share of W_j is R + lo T.
 __global__ void __launch_bounds__(128) k_rsum_seg(const xyzz_st* __restrict__ bsum, uint32_t c,
                                                   uint32_t nwin, uint32_t seg_len, uint32_t nseg,
                                                   xyzz_st* __restrict__ seg_out) {
   uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= nwin * nseg) return;
+  const uint32_t nb = 1u << (c - 1);
   uint32_t j = t / nseg, s = t % nseg;
-  uint32_t lo = max(1u, s * seg_len), hi = min(1u << c, (s + 1) * seg_len);
+  uint32_t lo = s * seg_len, hi = min(nb, (s + 1) * seg_len);
   xyzz T = xyzz_inf(), R = xyzz_inf();
   for (uint32_t b = hi; b-- > lo;) {
-    T = xyzz_add(T, xyzz_load(bsum + ((size_t)j << c) + b));
+    T = xyzz_add(T, xyzz_load(bsum + (size_t)j * nb + b));
     R = xyzz_add(R, T);
   }
-  xyzz_store(seg_out + t, xyzz_add(R, xyzz_mul_small(T, lo - 1)));
+  xyzz_store(seg_out + t, xyzz_add(R, xyzz_mul_small(T, lo)));
 }
 
 __global__ void __launch_bounds__(256) k_rsum_win(const xyzz_st* __restrict__ seg, uint32_t nseg,

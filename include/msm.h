@@ -47,7 +47,7 @@ enum {
   MSM_ERR_ARG = -1,   /* bad pointer, alignment, size, c or S; workspace too small */
   MSM_ERR_HIP = -2,   /* a HIP runtime call or kernel launch failed */
   MSM_ERR_OOM = -3,   /* device or pinned host allocation failed */
-  MSM_ERR_RANGE = -4  /* some scalar is >= 2^(W*c), W = ceil(254 / c) windows */
+  MSM_ERR_RANGE = -4  /* some scalar is >= 2^(W*c - 1), W = ceil(255 / c) windows */
 };
 
 /* Largest n accepted (bucket lists are indexed with 32-bit offsets). */
@@ -80,7 +80,8 @@ size_t msm_workspace_bytes(size_t n, int c, int S);
  *              (0, 0); the library does not check curve membership.
  *   d_scalars  device, n * 8 uint32 words, 16-byte aligned.
  *   n          0 .. MSM_MAX_N; n = 0 gives the point at infinity.
- *   c          window width in bits, 1 .. 16; W = ceil(254 / c) windows.
+ *   c          window width in bits, 1 .. 16; W = ceil(255 / c) windows of signed
+ *              digits in [-2^(c-1), 2^(c-1)] (2^(c-1) buckets per window, -P is free).
  *   S          affine additions sharing one inversion: 4, 8, 16 or 32.
  *   d_workspace device scratch of msm_workspace_bytes(n, c, S) bytes (256-byte
  *              aligned), or NULL to use the context's own (grown on demand).
@@ -89,9 +90,10 @@ size_t msm_workspace_bytes(size_t n, int c, int S);
  * The call enqueues the decompose/count/sort kernels, then blocks once on `stream`
  * to read back a small plan (largest bucket, scalar range flag), then enqueues the
  * accumulate, reduction and combine kernels and returns; d_out is valid once the
- * stream reaches that point. Scalars s with r <= s < 2^(W*c) are treated as the
- * integers they are (s * P = (s mod r) * P). MSM_ERR_RANGE if any scalar has a bit
- * at or above W*c set (nothing further is enqueued).
+ * stream reaches that point. Scalars s with r <= s < 2^(W*c - 1) are treated as the
+ * integers they are (s * P = (s mod r) * P); every scalar below 2^254 (so every
+ * canonical one, s < r) is in range for every c. MSM_ERR_RANGE if some scalar is at
+ * or above 2^(W*c - 1) (nothing further is enqueued).
  */
 int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scalars, size_t n,
             int c, int S, void* d_workspace, size_t workspace_bytes, void* stream,

@@ -180,13 +180,15 @@ def test_giant_bucket():
 
 
 def test_range_error():
+    """Signed digits with W = ceil(255 / c) windows cover scalars below 2^(W c - 1)."""
     M = _msm()
     pts = _pts([5])
     sc = wl.from_ints([1 << 255])
-    say("range error c 15")
-    with pytest.raises(M.MsmError) as e:
-        M.msm(to_dev(pts), to_dev(sc), 15)
-    assert e.value.code == M.MSM_ERR_RANGE
-    # the same scalar is in range for c = 16 (W c = 256)
-    want = oracle.msm_pippenger(pts, sc, 16)
-    assert np.array_equal(_gpu_msm(pts, sc, 16), want)
+    for c in (15, 16):  # W c - 1 = 254 and 255
+        say("range error c", c)
+        with pytest.raises(M.MsmError) as e:
+            M.msm(to_dev(pts), to_dev(sc), c)
+        assert e.value.code == M.MSM_ERR_RANGE
+    # the same scalar is in range for c = 13 (W c - 1 = 259)
+    want = oracle.msm_pippenger(pts, sc, 13)
+    assert np.array_equal(_gpu_msm(pts, sc, 13), want)
