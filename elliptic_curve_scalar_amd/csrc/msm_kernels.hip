@@ -21,6 +21,7 @@
 
 #include "batch_add.hpp"
 #include "msm_internal.hpp"
+#include "quad.hpp"
 
 namespace msmk {
 
@@ -439,6 +440,44 @@ __global__ void __launch_bounds__(128) k_level_xyzz(const void* __restrict__ in_
   if ((cl & 1u) && m == np - 1) xyzz_store(out + ob + np, load(base + cl - 1));
 }
 
+// The same level with one pair per quad (quad.hpp): for small levels, whose time is
+// one addition's latency, four lanes share each addition.
+template <bool IN_AFF>
+__global__ void __launch_bounds__(128) k_level_xyzz_q(const void* __restrict__ in_,
+                                                      const uint32_t* __restrict__ idx,
+                                                      xyzz_st* __restrict__ out, xyzz_st* bsum,
+                                                      const uint32_t* __restrict__ counts,
+                                                      const uint32_t* __restrict__ offsets,
+                                                      const uint32_t* __restrict__ poff,
+                                                      uint32_t K, uint32_t npairs, int level) {
+  const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint32_t p = gid >> 2;
+  const int q = (int)(gid & 3u);
+  if (p >= npairs) return;
+  uint32_t k = last_le(poff, K, p);
+  uint32_t m = p - poff[k];
+  uint32_t off = offsets[k];
+  uint32_t base = idx ? off : half_base(off, k);
+  uint32_t cl = level_count(counts[k], level);
+  auto load = [&](uint32_t pos) -> xyzz {
+    if (IN_AFF) {
+      const g1a* in = reinterpret_cast<const g1a*>(in_);
+      return xyzz_from_aff(idx ? load_entry(in, idx[pos]) : aff_load(in + pos));
+    }
+    return xyzz_load(reinterpret_cast<const xyzz_st*>(in_) + pos);
+  };
+  const xyzz r = quad_add(load(base + 2 * m), load(base + 2 * m + 1), q);
+  if (q != 0) return;
+  if (cl == 2) {
+    xyzz_store(bsum + k, r);
+    return;
+  }
+  uint32_t ob = half_base(off, k);
+  xyzz_store(out + ob + m, r);
+  uint32_t np = cl >> 1;
+  if ((cl & 1u) && m == np - 1) xyzz_store(out + ob + np, load(base + cl - 1));
+}
+
 // ------------------------------------------------------------------ reduction
 // Window j has 2^(c-1) bucket slots; slot b holds the points whose digit has
 // magnitude b + 1, so W_j = sum_b (b + 1) B_b. Segment s covers slots [lo, hi): with
@@ -447,35 +486,42 @@ __global__ void __launch_bounds__(128) k_level_xyzz(const void* __restrict__ in_
 __global__ void __launch_bounds__(128) k_rsum_seg(const xyzz_st* __restrict__ bsum, uint32_t c,
                                                   uint32_t nwin, uint32_t seg_len, uint32_t nseg,
                                                   xyzz_st* __restrict__ seg_out) {
-  uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
+  // one segment per quad (quad.hpp)
+  const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint32_t t = gid >> 2;
+  const int q = (int)(gid & 3u);
   if (t >= nwin * nseg) return;
   const uint32_t nb = 1u << (c - 1);
   uint32_t j = t / nseg, s = t % nseg;
   uint32_t lo = s * seg_len, hi = min(nb, (s + 1) * seg_len);
   xyzz T = xyzz_inf(), R = xyzz_inf();
   for (uint32_t b = hi; b-- > lo;) {
-    T = xyzz_add(T, xyzz_load(bsum + (size_t)j * nb + b));
-    R = xyzz_add(R, T);
+    T = quad_add(T, xyzz_load(bsum + (size_t)j * nb + b), q);
+    R = quad_add(R, T, q);
   }
-  xyzz_store(seg_out + t, xyzz_add(R, xyzz_mul_small(T, lo)));
+  const xyzz res = quad_add(R, quad_mul_small(T, lo, q), q);
+  if (q == 0) xyzz_store(seg_out + t, res);
 }
 
+// One block per window: 64 quads sum strided segments, then a tree through LDS.
 __global__ void __launch_bounds__(256) k_rsum_win(const xyzz_st* __restrict__ seg, uint32_t nseg,
                                                   xyzz_st* __restrict__ win) {
-  __shared__ xyzz_st lds[256];
-  uint32_t j = blockIdx.x, t = threadIdx.x;
+  __shared__ xyzz_st lds[64];
+  const uint32_t j = blockIdx.x, quad = threadIdx.x >> 2;
+  const int q = (int)(threadIdx.x & 3u);
   xyzz acc = xyzz_inf();
-  for (uint32_t s = t; s < nseg; s += 256) acc = xyzz_add(acc, xyzz_load(seg + (size_t)j * nseg + s));
-  xyzz_store(&lds[t], acc);
+  for (uint32_t s = quad; s < nseg; s += 64)
+    acc = quad_add(acc, xyzz_load(seg + (size_t)j * nseg + s), q);
+  if (q == 0) xyzz_store(&lds[quad], acc);
   __syncthreads();
-  for (uint32_t stride = 128; stride > 0; stride >>= 1) {
-    if (t < stride) {
-      acc = xyzz_add(acc, xyzz_load(&lds[t + stride]));
-      xyzz_store(&lds[t], acc);
+  for (uint32_t stride = 32; stride > 0; stride >>= 1) {
+    if (quad < stride) {
+      acc = quad_add(acc, xyzz_load(&lds[quad + stride]), q);
+      if (q == 0) xyzz_store(&lds[quad], acc);
     }
     __syncthreads();
   }
-  if (t == 0) xyzz_store(win + j, acc);
+  if (threadIdx.x == 0) xyzz_store(win + j, acc);
 }
 
 // ---- window combine: one wave, independent products spread over its lanes ----
@@ -726,6 +772,14 @@ hipError_t launch_level_xyzz(bool in_aff, const void* in, const uint32_t* idx, x
                              xyzz_st* bsum, const uint32_t* counts, const uint32_t* offsets,
                              const uint32_t* poff, uint32_t K, uint32_t npairs, int level,
                              hipStream_t s) {
+  if (npairs <= XYZZ_QUAD_MAX_PAIRS) {  // small level: four lanes per addition
+    unsigned g = grid_for((size_t)npairs * 4, 128);
+    if (in_aff)
+      k_level_xyzz_q<true><<<g, 128, 0, s>>>(in, idx, out, bsum, counts, offsets, poff, K, npairs, level);
+    else
+      k_level_xyzz_q<false><<<g, 128, 0, s>>>(in, idx, out, bsum, counts, offsets, poff, K, npairs, level);
+    return hipGetLastError();
+  }
   unsigned g = grid_for(npairs, 128);
   if (in_aff)
     k_level_xyzz<true><<<g, 128, 0, s>>>(in, idx, out, bsum, counts, offsets, poff, K, npairs, level);
@@ -736,7 +790,7 @@ hipError_t launch_level_xyzz(bool in_aff, const void* in, const uint32_t* idx, x
 
 hipError_t launch_reduce(const xyzz_st* bsum, uint32_t c, uint32_t nwin, uint32_t seg_len,
                          uint32_t nseg, xyzz_st* seg, xyzz_st* win, hipStream_t s) {
-  k_rsum_seg<<<grid_for((size_t)nwin * nseg, 128), 128, 0, s>>>(bsum, c, nwin, seg_len, nseg, seg);
+  k_rsum_seg<<<grid_for((size_t)nwin * nseg * 4, 128), 128, 0, s>>>(bsum, c, nwin, seg_len, nseg, seg);
   k_rsum_win<<<nwin, 256, 0, s>>>(seg, nseg, win);
   return hipGetLastError();
 }

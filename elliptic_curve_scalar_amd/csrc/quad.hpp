@@ -1,0 +1,94 @@
+// XYZZ point arithmetic shared by the four lanes of a quad.
+//
+// The running sum, the per-window trees and the deep pair-tree levels have too
+// little parallel work to fill the chip, so their time is the latency of one lane's
+// chain of additions. An XYZZ addition (add-2008-s) has 12 field products but only 4
+// dependent rounds of at most 4 independent products each, and a doubling
+// (dbl-2008-s-1) 9 products in 3 rounds. Here the four lanes of a quad hold the same
+// points; in each round lane k computes product k and a DPP quad_perm broadcast hands
+// every result to all four lanes. A step then costs 3-4 product latencies instead of
+// 9-14, at about 1.4x the total lane work, which pays only where lanes are idle.
+//
+// All four lanes of a quad see the same values, so every branch below is uniform
+// within the quad (quads of one wavefront may still diverge from each other).
+#pragma once
+#include "ec.hpp"
+
+namespace msmk {
+
+// Lane K of this lane's quad, for every word of v (v_mov_b32 with DPP quad_perm).
+template <int K>
+__device__ __forceinline__ fp quad_from(const fp& v) {
+  constexpr int ctrl = K | (K << 2) | (K << 4) | (K << 6);
+  fp r;
+#pragma unroll
+  for (int i = 0; i < 8; i++)
+    r.v[i] = (uint32_t)__builtin_amdgcn_mov_dpp((int)v.v[i], ctrl, 0xf, 0xf, false);
+  return r;
+}
+
+// Operand for this lane: a0 on quad lane 0, a1 on 1, ...
+__device__ __forceinline__ fp quad_pick(int q, const fp& a0, const fp& a1, const fp& a2,
+                                        const fp& a3) {
+  fp r;
+#pragma unroll
+  for (int i = 0; i < 8; i++)
+    r.v[i] = q == 0 ? a0.v[i] : q == 1 ? a1.v[i] : q == 2 ? a2.v[i] : a3.v[i];
+  return r;
+}
+
+__device__ __forceinline__ xyzz quad_dbl(const xyzz& p, int q) {
+  const fp U = fp_dbl(p.Y);
+  const fp x = quad_pick(q, U, p.X, U, p.X);
+  fp r = fp_sqr(x);                                   // V = U^2, XX = X^2
+  const fp V = quad_from<0>(r), XX = quad_from<1>(r);
+  const fp M = fp_add(fp_dbl(XX), XX);
+  r = fp_mul(quad_pick(q, U, p.X, M, V), quad_pick(q, V, V, M, p.ZZ));  // W, S, M^2, ZZ3
+  const fp W = quad_from<0>(r), S = quad_from<1>(r), MM = quad_from<2>(r);
+  xyzz o;
+  o.ZZ = quad_from<3>(r);
+  o.X = fp_sub(fp_sub(MM, S), S);
+  r = fp_mul(quad_pick(q, W, W, M, W), quad_pick(q, p.ZZZ, p.Y, fp_sub(S, o.X), p.ZZZ));
+  o.ZZZ = quad_from<0>(r);                            // ZZZ3 = W ZZZ
+  o.Y = fp_sub(quad_from<2>(r), quad_from<1>(r));     // M (S - X3) - W Y
+  return o;
+}
+
+__device__ __forceinline__ xyzz quad_add(const xyzz& p, const xyzz& s, int q) {
+  if (xyzz_is_inf(s)) return p;
+  if (xyzz_is_inf(p)) return s;
+  fp r = fp_mul(quad_pick(q, p.X, s.X, p.Y, s.Y), quad_pick(q, s.ZZ, p.ZZ, s.ZZZ, p.ZZZ));
+  const fp U1 = quad_from<0>(r), U2 = quad_from<1>(r);  // U1 = X1 ZZ2, U2 = X2 ZZ1
+  const fp S1 = quad_from<2>(r), S2 = quad_from<3>(r);  // S1 = Y1 ZZZ2, S2 = Y2 ZZZ1
+  const fp P = fp_sub(U2, U1), R = fp_sub(S2, S1);
+  if (fp_is_zero(P)) {
+    if (fp_is_zero(R)) return quad_dbl(p, q);
+    return xyzz_inf();
+  }
+  r = fp_mul(quad_pick(q, p.ZZ, p.ZZZ, P, R), quad_pick(q, s.ZZ, s.ZZZ, P, R));
+  const fp ZZ12 = quad_from<0>(r), ZZZ12 = quad_from<1>(r);
+  const fp PP = quad_from<2>(r), RR = quad_from<3>(r);
+  r = fp_mul(quad_pick(q, P, U1, ZZ12, P), PP);         // PPP, Q = U1 PP, ZZ3
+  const fp PPP = quad_from<0>(r), Qv = quad_from<1>(r);
+  xyzz o;
+  o.ZZ = quad_from<2>(r);
+  o.X = fp_sub(fp_sub(fp_sub(RR, PPP), Qv), Qv);
+  r = fp_mul(quad_pick(q, ZZZ12, S1, R, ZZZ12), quad_pick(q, PPP, PPP, fp_sub(Qv, o.X), PPP));
+  o.ZZZ = quad_from<0>(r);
+  o.Y = fp_sub(quad_from<2>(r), quad_from<1>(r));       // R (Q - X3) - S1 PPP
+  return o;
+}
+
+// k * P for a small non-negative k (MSB-first double-and-add), quad-cooperative.
+__device__ __forceinline__ xyzz quad_mul_small(const xyzz& p, uint32_t k, int q) {
+  if (k == 0) return xyzz_inf();
+  const int top = 31 - __clz(k);
+  xyzz acc = p;
+  for (int b = top - 1; b >= 0; b--) {
+    acc = quad_dbl(acc, q);
+    if ((k >> b) & 1u) acc = quad_add(acc, p, q);
+  }
+  return acc;
+}
+
+}  // namespace msmk
