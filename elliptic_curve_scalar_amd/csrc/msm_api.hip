@@ -30,8 +30,8 @@ int fail(int code, const char* fmt, const char* detail = "") {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Signed c-bit digits of scalars below 2^254 need W c >= 255.
-int num_windows(int c) { return (255 + c - 1) / c; }
+// Signed c-bit digits of the GLV half-scalars (magnitudes below 2^127) need W c >= 128.
+int num_windows(int c) { return (128 + c - 1) / c; }
 
 // Buckets per running-sum segment: enough segments to spread the reduction over the
 // chip, never fewer than 4 buckets per segment.
@@ -44,8 +44,8 @@ uint32_t segment_length(int c, int nwin) {
 }
 
 struct Layout {
-  size_t stats, counts, offsets, cursor, poff, block_sums, sorted_idx, aff_a, aff_b, xz_a, xz_b,
-      bsum, seg, win;
+  size_t stats, halfs, pts2, counts, offsets, cursor, poff, block_sums, sorted_idx, aff_a, aff_b,
+      xz_a, xz_b, bsum, seg, win;
   size_t total;
   uint32_t K, nwin, seg_len, nseg;
   size_t E_max, half;
@@ -57,7 +57,7 @@ Layout plan(size_t n, int c) {
   L.K = L.nwin << (c - 1);  // 2^(c-1) bucket slots per window (signed digits)
   L.seg_len = segment_length(c, (int)L.nwin);
   L.nseg = ((1u << (c - 1)) + L.seg_len - 1) / L.seg_len;
-  L.E_max = n * L.nwin;
+  L.E_max = 2 * n * L.nwin;  // 2n GLV points
   L.half = (L.E_max + L.K) / 2 + 1;  // elements of a level >= 1 buffer
   size_t nb = (L.K + SCAN_TILE - 1) / SCAN_TILE + 1;
   size_t off = 0;
@@ -67,6 +67,8 @@ Layout plan(size_t n, int c) {
     return at;
   };
   L.stats = take(sizeof(msm_stats));
+  L.halfs = take(2 * n * 16);
+  L.pts2 = take(2 * n * sizeof(g1a));
   L.counts = take((size_t)L.K * 4);
   L.offsets = take(((size_t)L.K + 1) * 4);
   L.cursor = take((size_t)L.K * 4);
@@ -91,6 +93,8 @@ int check_run_args(const msm_g1_affine* pts, const uint32_t* sc, size_t n, int c
   if (c < 1 || c > 16) return fail(MSM_ERR_ARG, "window c must be in 1..16%s");
   if (S != 4 && S != 8 && S != 16 && S != 32) return fail(MSM_ERR_ARG, "S must be 4, 8, 16 or 32%s");
   if (n > MSM_MAX_N) return fail(MSM_ERR_ARG, "n exceeds MSM_MAX_N%s");
+  if ((uint64_t)2 * n * (uint64_t)num_windows(c) >= ((uint64_t)1 << 32))
+    return fail(MSM_ERR_ARG, "2 n ceil(128 / c) bucket entries exceed 32-bit offsets; raise c%s");
   if (!out) return fail(MSM_ERR_ARG, "d_out is NULL%s");
   if (n && (!pts || !sc)) return fail(MSM_ERR_ARG, "points or scalars pointer is NULL%s");
   if (!aligned(pts, 16) || !aligned(sc, 16) || !aligned(out, 16))
@@ -157,13 +161,14 @@ struct PhaseMark {
 
 extern "C" {
 
-int msm_version(void) { return 100; }
+int msm_version(void) { return 200; }
 
 const char* msm_last_error(void) { return g_err; }
 
 size_t msm_workspace_bytes(size_t n, int c, int S) {
   (void)S;
   if (c < 1 || c > 16 || n > MSM_MAX_N) return 0;
+  if ((uint64_t)2 * n * (uint64_t)num_windows(c) >= ((uint64_t)1 << 32)) return 0;
   return plan(n, c).total;
 }
 
@@ -227,6 +232,8 @@ int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scala
     ws = (char*)ctx->ws;
   }
   msm_stats* stats = (msm_stats*)(ws + L.stats);
+  uint32_t* halfs = (uint32_t*)(ws + L.halfs);
+  g1a* pts2 = (g1a*)(ws + L.pts2);
   uint32_t* counts = (uint32_t*)(ws + L.counts);
   uint32_t* offsets = (uint32_t*)(ws + L.offsets);
   uint32_t* cursor = (uint32_t*)(ws + L.cursor);
@@ -238,22 +245,23 @@ int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scala
   xyzz_st* bsum = (xyzz_st*)(ws + L.bsum);
   xyzz_st* seg = (xyzz_st*)(ws + L.seg);
   xyzz_st* win = (xyzz_st*)(ws + L.win);
-  const g1a* pts = (const g1a*)d_points;
-  uint32_t n32 = (uint32_t)n, c32 = (uint32_t)c;
+  const g1a* pts = pts2;  // 2n points: P_i and phi(P_i)
+  uint32_t n32 = (uint32_t)n, m32 = 2 * (uint32_t)n, c32 = (uint32_t)c;
 
   // decompose + count, offsets, plan, scatter
   PhaseMark ph_sort(ctx, st, PH_SORT);
   HIP_TRY(launch_fill((uint32_t*)stats, sizeof(msm_stats) / 4, 0, st));
   HIP_TRY(launch_fill(counts, L.K, 0, st));
-  HIP_TRY(launch_hist(d_scalars, n32, c32, L.nwin, counts, stats, st));
+  HIP_TRY(launch_glv_prep((const g1a*)d_points, d_scalars, n32, pts2, halfs, stats, st));
+  HIP_TRY(launch_hist(halfs, m32, c32, L.nwin, counts, st));
   HIP_TRY(launch_scan(counts, L.K, -1, block_sums, offsets, cursor, st));
   HIP_TRY(launch_stats(counts, L.K, stats, st));
-  HIP_TRY(launch_scatter(d_scalars, n32, c32, L.nwin, cursor, sorted_idx, st));
+  HIP_TRY(launch_scatter(halfs, m32, c32, L.nwin, cursor, sorted_idx, st));
   HIP_TRY(hipMemcpyAsync(ctx->host_stats, stats, sizeof(msm_stats), hipMemcpyDeviceToHost, st));
   ph_sort.end();
   HIP_TRY(hipStreamSynchronize(st));
   const msm_stats hs = *ctx->host_stats;
-  if (hs.range_flag) return fail(MSM_ERR_RANGE, "a scalar is not below 2^(W*c-1)%s");
+  if (hs.range_flag) return fail(MSM_ERR_RANGE, "GLV half-scalar out of bound (internal error)%s");
 
   // accumulate: pair-tree levels until every bucket holds one point
   PhaseMark ph_acc(ctx, st, PH_ACCUM);
@@ -383,6 +391,15 @@ int msm_test_fp(int op, const uint32_t* d_a, const uint32_t* d_b, uint32_t* d_ou
   bool binary = (op <= 2);
   if (n && (!d_a || !d_out || (binary && !d_b))) return fail(MSM_ERR_ARG, "NULL pointer%s");
   HIP_TRY(launch_test_fp(op, d_a, binary ? d_b : nullptr, d_out, (uint32_t)n, (hipStream_t)stream));
+  return MSM_OK;
+}
+
+int msm_test_glv(const uint32_t* d_scalars, size_t n, uint32_t* d_halfs, void* stream) {
+  if (n > MSM_MAX_N) return fail(MSM_ERR_ARG, "n exceeds MSM_MAX_N%s");
+  if (n && (!d_scalars || !d_halfs)) return fail(MSM_ERR_ARG, "NULL pointer%s");
+  if (!aligned(d_scalars, 16) || !aligned(d_halfs, 16))
+    return fail(MSM_ERR_ARG, "pointers must be 16-byte aligned%s");
+  if (n) HIP_TRY(launch_test_glv(d_scalars, (uint32_t)n, d_halfs, (hipStream_t)stream));
   return MSM_OK;
 }
 

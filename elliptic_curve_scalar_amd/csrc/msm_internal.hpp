@@ -19,7 +19,7 @@ constexpr int SEARCH_STEPS = 22;                     // bucket searches cover K 
 
 // Plan read back to the host after the sort (one 16 + 4 * MAX_LEVELS byte copy).
 struct msm_stats {
-  uint32_t range_flag;          // some scalar has a bit >= W c
+  uint32_t range_flag;          // a GLV half-scalar came out >= 2^127 (never expected)
   uint32_t max_count;           // largest bucket
   uint32_t total;               // bucket entries E (non-zero digits)
   uint32_t pad;
@@ -32,9 +32,11 @@ struct xyzz_st {
 };
 
 hipError_t launch_fill(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
-hipError_t launch_hist(const uint32_t* scalars, uint32_t n, uint32_t c, uint32_t nwin,
-                       uint32_t* counts, msm_stats* st, hipStream_t s);
-hipError_t launch_scatter(const uint32_t* scalars, uint32_t n, uint32_t c, uint32_t nwin,
+hipError_t launch_glv_prep(const g1a* points, const uint32_t* scalars, uint32_t n, g1a* pts2,
+                           uint32_t* halfs, msm_stats* st, hipStream_t s);
+hipError_t launch_hist(const uint32_t* halfs, uint32_t m, uint32_t c, uint32_t nwin,
+                       uint32_t* counts, hipStream_t s);
+hipError_t launch_scatter(const uint32_t* halfs, uint32_t m, uint32_t c, uint32_t nwin,
                           uint32_t* cursor, uint32_t* sorted_idx, hipStream_t s);
 hipError_t launch_scan(const uint32_t* counts, uint32_t n, int level, uint32_t* block_sums,
                        uint32_t* out, uint32_t* out2, hipStream_t s);
@@ -55,6 +57,7 @@ hipError_t launch_final(const xyzz_st* win, uint32_t nwin, uint32_t c, g1a* out,
 hipError_t launch_from_scalars(const uint32_t* ks, uint32_t n, g1a* out, hipStream_t s);
 hipError_t launch_test_fp(int op, const uint32_t* a, const uint32_t* b, uint32_t* out, uint32_t n,
                           hipStream_t s);
+hipError_t launch_test_glv(const uint32_t* scalars, uint32_t n, uint32_t* halfs, hipStream_t s);
 hipError_t launch_test_pair_add(int S, const g1a* a, const g1a* b, g1a* out, uint32_t n,
                                 hipStream_t s);
 

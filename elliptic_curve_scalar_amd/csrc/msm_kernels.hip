@@ -20,6 +20,7 @@
 #include <hip/hip_runtime.h>
 
 #include "batch_add.hpp"
+#include "glv.hpp"
 #include "msm_internal.hpp"
 #include "quad.hpp"
 
@@ -90,31 +91,66 @@ __device__ __forceinline__ void for_each_signed_digit(const sc256& s, uint32_t c
   }
 }
 
-__global__ void __launch_bounds__(256) k_hist(const uint32_t* __restrict__ scalars, uint32_t n,
-                                              uint32_t c, uint32_t nwin,
-                                              uint32_t* __restrict__ counts, msm_stats* st) {
+// GLV split (glv.hpp): half-scalar i = |k1| of scalar i and half-scalar n + i = |k2|,
+// each four words with the sign in bit 127; point i is P_i and point n + i is
+// phi(P_i) = (beta x, y). Every later stage sees 2n points with 127-bit scalars.
+__global__ void __launch_bounds__(128) k_glv_prep(const g1a* __restrict__ points,
+                                                  const uint32_t* __restrict__ scalars, uint32_t n,
+                                                  g1a* __restrict__ pts2, uint32_t* __restrict__ halfs,
+                                                  msm_stats* st) {
   uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
-  sc256 s = load_scalar(scalars, i);
-  if (above_bits(s, nwin * c - 1)) atomicOr(&st->range_flag, 1u);
+  const sc256 sc = load_scalar(scalars, i);
+  uint32_t s[8], k1[4], k2[4];
+#pragma unroll
+  for (int w = 0; w < 8; w++) s[w] = sc.w[w];
+  bool bad = false;
+  glv_split(s, k1, k2, bad);
+  if (bad) atomicOr(&st->range_flag, 1u);
+  reinterpret_cast<uint4*>(halfs)[i] = make_uint4(k1[0], k1[1], k1[2], k1[3]);
+  reinterpret_cast<uint4*>(halfs)[n + i] = make_uint4(k2[0], k2[1], k2[2], k2[3]);
+  aff a = aff_load(points + i);
+  aff_store(pts2 + i, a);
+  if (!aff_is_inf(a)) a.x = fp_mul(a.x, glv_beta());
+  aff_store(pts2 + n + i, a);
+}
+
+// Half-scalar i: 127-bit magnitude in a 256-bit value, and its sign.
+__device__ __forceinline__ sc256 load_half(const uint32_t* halfs, uint32_t i, bool& neg) {
+  const uint4 h = reinterpret_cast<const uint4*>(halfs)[i];
+  neg = (h.w >> 31) != 0;
+  sc256 r;
+  r.w[0] = h.x; r.w[1] = h.y; r.w[2] = h.z; r.w[3] = h.w & 0x7fffffffu;
+  r.w[4] = r.w[5] = r.w[6] = r.w[7] = 0;
+  return r;
+}
+
+__global__ void __launch_bounds__(256) k_hist(const uint32_t* __restrict__ halfs, uint32_t m,
+                                              uint32_t c, uint32_t nwin,
+                                              uint32_t* __restrict__ counts) {
+  uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= m) return;
+  bool neg;
+  const sc256 s = load_half(halfs, i, neg);
   const uint32_t sh = c - 1;
   for_each_signed_digit(s, c, nwin, [&](uint32_t j, uint32_t slot, bool) {
     atomicAdd(&counts[(j << sh) | slot], 1u);
   });
 }
 
-// Bucket lists hold point indices with the digit's sign in bit 31.
-__global__ void __launch_bounds__(256) k_scatter(const uint32_t* __restrict__ scalars, uint32_t n,
+// Bucket lists hold point indices with the sign of (digit x half-scalar) in bit 31.
+__global__ void __launch_bounds__(256) k_scatter(const uint32_t* __restrict__ halfs, uint32_t m,
                                                  uint32_t c, uint32_t nwin,
                                                  uint32_t* __restrict__ cursor,
                                                  uint32_t* __restrict__ sorted_idx) {
   uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  sc256 s = load_scalar(scalars, i);
+  if (i >= m) return;
+  bool sneg;
+  const sc256 s = load_half(halfs, i, sneg);
   const uint32_t sh = c - 1;
   for_each_signed_digit(s, c, nwin, [&](uint32_t j, uint32_t slot, bool neg) {
     uint32_t pos = atomicAdd(&cursor[(j << sh) | slot], 1u);
-    sorted_idx[pos] = i | (neg ? 0x80000000u : 0u);
+    sorted_idx[pos] = i | ((neg != sneg) ? 0x80000000u : 0u);
   });
 }
 
@@ -691,6 +727,20 @@ struct PairSrc {
   __device__ __forceinline__ void put(int s, const aff& r) const { aff_store(out + base + s, r); }
 };
 
+__global__ void __launch_bounds__(128) k_test_glv(const uint32_t* __restrict__ scalars, uint32_t n,
+                                                  uint32_t* __restrict__ halfs) {
+  uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const sc256 sc = load_scalar(scalars, i);
+  uint32_t s[8], k1[4], k2[4];
+#pragma unroll
+  for (int w = 0; w < 8; w++) s[w] = sc.w[w];
+  bool bad = false;
+  glv_split(s, k1, k2, bad);
+  reinterpret_cast<uint4*>(halfs)[i] = make_uint4(k1[0], k1[1], k1[2], k1[3]);
+  reinterpret_cast<uint4*>(halfs)[n + i] = make_uint4(k2[0], k2[1], k2[2], k2[3]);
+}
+
 template <int S>
 __global__ void __launch_bounds__(256) k_test_pair_add(const g1a* a, const g1a* b, g1a* out,
                                                        uint32_t n) {
@@ -710,15 +760,21 @@ hipError_t launch_fill(uint32_t* p, size_t n, uint32_t v, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_hist(const uint32_t* scalars, uint32_t n, uint32_t c, uint32_t nwin,
-                       uint32_t* counts, msm_stats* st, hipStream_t s) {
-  k_hist<<<grid_for(n, 256), 256, 0, s>>>(scalars, n, c, nwin, counts, st);
+hipError_t launch_glv_prep(const g1a* points, const uint32_t* scalars, uint32_t n, g1a* pts2,
+                           uint32_t* halfs, msm_stats* st, hipStream_t s) {
+  k_glv_prep<<<grid_for(n, 128), 128, 0, s>>>(points, scalars, n, pts2, halfs, st);
   return hipGetLastError();
 }
 
-hipError_t launch_scatter(const uint32_t* scalars, uint32_t n, uint32_t c, uint32_t nwin,
+hipError_t launch_hist(const uint32_t* halfs, uint32_t m, uint32_t c, uint32_t nwin,
+                       uint32_t* counts, hipStream_t s) {
+  k_hist<<<grid_for(m, 256), 256, 0, s>>>(halfs, m, c, nwin, counts);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(const uint32_t* halfs, uint32_t m, uint32_t c, uint32_t nwin,
                           uint32_t* cursor, uint32_t* sorted_idx, hipStream_t s) {
-  k_scatter<<<grid_for(n, 256), 256, 0, s>>>(scalars, n, c, nwin, cursor, sorted_idx);
+  k_scatter<<<grid_for(m, 256), 256, 0, s>>>(halfs, m, c, nwin, cursor, sorted_idx);
   return hipGetLastError();
 }
 
@@ -810,6 +866,11 @@ hipError_t launch_test_fp(int op, const uint32_t* a, const uint32_t* b, uint32_t
                           hipStream_t s) {
   if (n == 0) return hipSuccess;
   k_test_fp<<<grid_for(n, 128), 128, 0, s>>>(op, a, b, out, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_test_glv(const uint32_t* scalars, uint32_t n, uint32_t* halfs, hipStream_t s) {
+  k_test_glv<<<grid_for(n, 128), 128, 0, s>>>(scalars, n, halfs);
   return hipGetLastError();
 }
 

@@ -36,6 +36,7 @@ SYMBOLS = {
     "msm_ctx_timing_read": (_I, [_P, _P]),
     "msm_test_fp": (_I, [_I, _P, _P, _P, _S, _P]),
     "msm_test_pair_add": (_I, [_P, _P, _P, _S, _I, _P]),
+    "msm_test_glv": (_I, [_P, _S, _P, _P]),
 }
 
 _lib = None
@@ -196,6 +197,15 @@ def test_fp(op: int, a: torch.Tensor, b: torch.Tensor | None = None) -> torch.Te
     out = torch.empty_like(a)
     _check(lib().msm_test_fp(op, _dev_ptr(a, 8, "a"), _dev_ptr(b, 8, "b"), _dev_ptr(out, 8, "out"),
                              a.shape[0], _stream_handle(a.device)))
+    return out
+
+
+def test_glv(scalars: torch.Tensor) -> torch.Tensor:
+    """GLV halves of n scalars: (2n, 4) uint32, |k1| rows then |k2| rows, sign in bit 127."""
+    n = scalars.shape[0]
+    out = torch.empty((2 * n, 4), dtype=torch.uint32, device=scalars.device)
+    _check(lib().msm_test_glv(_dev_ptr(scalars, 8, "scalars"), n, _dev_ptr(out, 4, "out"),
+                              _stream_handle(scalars.device)))
     return out
 
 

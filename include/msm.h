@@ -14,6 +14,9 @@
  * by level (the pair-tree of PR #23520, "Summary"), and the bucket sums are combined
  * per window by a running sum and across windows by doubling. The curve is the one
  * barretenberg uses; the pages do not name it, so its constants are EIP-196's.
+ * Before windowing, each scalar is split by the curve's endomorphism phi(x, y) =
+ * (beta x, y) = lambda (x, y) into s = k1 + k2 lambda (mod r) with |k1|, |k2| < 2^127
+ * (GLV; not on the pages), so the windows run over 2n points of 127-bit scalars.
  *
  * Data formats (all little-endian):
  *   - a field element is eight 32-bit words holding x * 2^256 mod p (Montgomery
@@ -47,10 +50,11 @@ enum {
   MSM_ERR_ARG = -1,   /* bad pointer, alignment, size, c or S; workspace too small */
   MSM_ERR_HIP = -2,   /* a HIP runtime call or kernel launch failed */
   MSM_ERR_OOM = -3,   /* device or pinned host allocation failed */
-  MSM_ERR_RANGE = -4  /* some scalar is >= 2^(W*c - 1), W = ceil(255 / c) windows */
+  MSM_ERR_RANGE = -4  /* internal: a GLV half-scalar came out >= 2^127 (not expected) */
 };
 
-/* Largest n accepted (bucket lists are indexed with 32-bit offsets). */
+/* Largest n accepted. Bucket lists are indexed with 32-bit offsets, so in addition
+ * 2 n ceil(128 / c) must stay below 2^32 (every c >= 5 allows MSM_MAX_N). */
 #define MSM_MAX_N ((size_t)1 << 26)
 
 /* Library version, major * 10000 + minor * 100 + patch. */
@@ -78,22 +82,24 @@ size_t msm_workspace_bytes(size_t n, int c, int S);
  * Q = sum_i s_i * P_i on `stream` (a hipStream_t; NULL is the null stream).
  *   d_points   device, n msm_g1_affine, 16-byte aligned; every point on the curve or
  *              (0, 0); the library does not check curve membership.
- *   d_scalars  device, n * 8 uint32 words, 16-byte aligned.
- *   n          0 .. MSM_MAX_N; n = 0 gives the point at infinity.
- *   c          window width in bits, 1 .. 16; W = ceil(255 / c) windows of signed
- *              digits in [-2^(c-1), 2^(c-1)] (2^(c-1) buckets per window, -P is free).
+ *   d_scalars  device, n * 8 uint32 words, 16-byte aligned; any 256-bit integers
+ *              (reduced mod r on the device).
+ *   n          0 .. MSM_MAX_N with 2 n ceil(128 / c) < 2^32; n = 0 gives the point
+ *              at infinity.
+ *   c          window width in bits, 1 .. 16; W = ceil(128 / c) windows of signed
+ *              digits in [-2^(c-1), 2^(c-1)] over the 2n half-scalars (2^(c-1)
+ *              buckets per window, -P is free).
  *   S          affine additions sharing one inversion: 4, 8, 16 or 32.
  *   d_workspace device scratch of msm_workspace_bytes(n, c, S) bytes (256-byte
  *              aligned), or NULL to use the context's own (grown on demand).
  *   d_out      device, one msm_g1_affine: Q in affine Montgomery form, (0, 0) if
  *              Q is the point at infinity.
  * The call enqueues the decompose/count/sort kernels, then blocks once on `stream`
- * to read back a small plan (largest bucket, scalar range flag), then enqueues the
+ * to read back a small plan (largest bucket, split range flag), then enqueues the
  * accumulate, reduction and combine kernels and returns; d_out is valid once the
- * stream reaches that point. Scalars s with r <= s < 2^(W*c - 1) are treated as the
- * integers they are (s * P = (s mod r) * P); every scalar below 2^254 (so every
- * canonical one, s < r) is in range for every c. MSM_ERR_RANGE if some scalar is at
- * or above 2^(W*c - 1) (nothing further is enqueued).
+ * stream reaches that point. Points must lie in the prime-order group (every
+ * BN254 G1 point does: the cofactor is 1). MSM_ERR_RANGE only if the split's bound
+ * failed, which the constants rule out (nothing further is enqueued then).
  */
 int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scalars, size_t n,
             int c, int S, void* d_workspace, size_t workspace_bytes, void* stream,
@@ -157,9 +163,15 @@ int msm_ctx_timing_read(msm_ctx* ctx, msm_timing* out);
  *
  * msm_test_pair_add: d_out[i] = d_a[i] + d_b[i] for n affine points, computed by
  * the batched-affine adder with S slots per lane (one inversion per S sums).
+ *
+ * msm_test_glv: the scalar split of msm_run for n scalars (8 words each, any
+ * 256-bit value): d_halfs[i] = |k1| and d_halfs[n + i] = |k2| of scalar i, four
+ * words each with the sign in bit 127, where s = k1 + k2 lambda (mod r).
+ * d_halfs holds 2 n * 4 words.
  */
 int msm_test_fp(int op, const uint32_t* d_a, const uint32_t* d_b, uint32_t* d_out, size_t n,
                 void* stream);
+int msm_test_glv(const uint32_t* d_scalars, size_t n, uint32_t* d_halfs, void* stream);
 int msm_test_pair_add(const msm_g1_affine* d_a, const msm_g1_affine* d_b, msm_g1_affine* d_out,
                       size_t n, int S, void* stream);
 

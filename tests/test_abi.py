@@ -44,6 +44,9 @@ def test_workspace_bytes():
     assert M.workspace_bytes(M.MSM_MAX_N + 1, 8) == 0
     assert M.workspace_bytes(1 << 20, 16) > M.workspace_bytes(1 << 16, 16)
     assert M.workspace_bytes(1 << 16, 13, 4) == M.workspace_bytes(1 << 16, 13, 32)
+    # 2 n ceil(128 / c) bucket entries must fit 32-bit offsets
+    assert M.workspace_bytes(M.MSM_MAX_N, 5) > 0
+    assert M.workspace_bytes(M.MSM_MAX_N, 4) == 0
 
 
 def _err(L):
@@ -66,12 +69,16 @@ def test_argument_errors_without_gpu():
     assert "aligned" in _err(L)
     assert L.msm(None, p, 16, 13, out) == M.MSM_ERR_ARG
     assert L.msm(p, p, M.MSM_MAX_N + 1, 13, out) == M.MSM_ERR_ARG
+    assert L.msm(p, p, M.MSM_MAX_N, 4, out) == M.MSM_ERR_ARG
+    assert "32-bit" in _err(L)
     # generator and test hooks
     assert L.msm_g1_from_scalars(None, 4, p, None) == M.MSM_ERR_ARG
     assert L.msm_g1_from_scalars(ctypes.c_void_p(4), 4, p, None) == M.MSM_ERR_ARG
     assert L.msm_test_fp(7, p, p, p, 4, None) == M.MSM_ERR_ARG
     assert L.msm_test_fp(0, p, None, p, 4, None) == M.MSM_ERR_ARG
     assert L.msm_test_pair_add(p, p, p, 4, 5, None) == M.MSM_ERR_ARG
+    assert L.msm_test_glv(None, 4, p, None) == M.MSM_ERR_ARG
+    assert L.msm_test_glv(p, 4, ctypes.c_void_p(4), None) == M.MSM_ERR_ARG
     # context creation with a NULL out pointer
     assert L.msm_ctx_create(0, None) == M.MSM_ERR_ARG
 

@@ -1,0 +1,141 @@
+"""Pins for the constants of the GLV scalar split in the HIP source (csrc/glv.hpp).
+
+The split is not on the pages; it rests on the BN254 endomorphism phi(x, y) =
+(beta x, y), which acts on G1 as multiplication by lambda (Gallant-Lambert-Vanstone,
+CRYPTO 2001). Each constant is parsed from the kernel source and checked against
+what the field, the group order and the curve fix:
+
+* beta is a primitive cube root of unity mod p, stored in Montgomery form;
+* lambda (implied by the basis) is a primitive cube root of unity mod r, and the
+  pairing is the right one: lambda * G = (beta * 1, 2) for G = (1, 2);
+* (a1, b1), (a2, b2) lie in the lattice a + b lambda = 0 (mod r) and span it
+  (determinant r), so rounding against them gives s = k1 + k2 lambda (mod r);
+* g1 = floor(2^256 b2 / r), g2 = floor(2^256 (-b1) / r) and the stored multiples
+  of r are exact;
+* the bound 3/4 (|a_i| + |b_i|) < 2^127 that makes the 127-bit windows enough;
+* a big-integer model of the split's steps with these constants meets the
+  decomposition identity and the bound on edge and random scalars.
+"""
+import os
+import random
+import re
+
+from oracle import ref
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "elliptic_curve_scalar_amd", "csrc", "glv.hpp")
+
+
+def _words(ws):
+    return sum(w << (32 * i) for i, w in enumerate(ws))
+
+
+def _constants():
+    text = open(SRC).read()
+    arrays = {}
+    for name, body in re.findall(r"const uint32_t (\w+)\[\d+\] = \{([^}]*)\}", text):
+        arrays[name] = _words([int(x, 16) for x in re.findall(r"0x([0-9a-fA-F]+)u", body)])
+    beta_words = dict((int(i), int(v, 16)) for i, v in re.findall(r"b\.v\[(\d)\] = 0x([0-9a-f]+)u", text))
+    assert sorted(beta_words) == list(range(8))
+    arrays["BETA_MONT"] = _words([beta_words[i] for i in range(8)])
+    return arrays
+
+
+C = _constants()
+P, R = ref.P, ref.R
+A1, A2, NB1, B2 = C["A1"], C["A2"], C["NB1"], C["B2"]
+B1 = -NB1
+BETA = C["BETA_MONT"] * pow(2, -256, P) % P
+
+
+def _cube_roots(m):
+    """The two primitive cube roots of unity mod a prime m = 1 (mod 3)."""
+    assert (m - 1) % 3 == 0
+    for g in range(2, 100):
+        w = pow(g, (m - 1) // 3, m)
+        if w != 1:
+            return {w, w * w % m}
+    raise AssertionError("no root found")
+
+
+def _lambda():
+    """The root lambda mod r with lambda * G = phi(G)."""
+    hits = [l for l in _cube_roots(R) if ref.scalar_mul(l, ref.G) == (BETA * ref.G[0] % P, ref.G[1])]
+    assert len(hits) == 1
+    return hits[0]
+
+
+def test_parsed_everything():
+    for k in ("R1", "R2", "R4", "G1", "G2", "A1", "A2", "NB1", "B2", "BETA_MONT"):
+        assert k in C, k
+
+
+def test_beta_is_primitive_cube_root_mod_p():
+    assert C["BETA_MONT"] < P
+    assert BETA in _cube_roots(P)
+    assert pow(BETA, 3, P) == 1 and BETA != 1
+
+
+def test_endomorphism_on_generator_and_random_points():
+    lam = _lambda()
+    assert (lam * lam + lam + 1) % R == 0
+    rng = random.Random(7)
+    for _ in range(3):
+        k = rng.randrange(1, R)
+        Q = ref.scalar_mul(k, ref.G)
+        assert ref.scalar_mul(lam, Q) == (BETA * Q[0] % P, Q[1])
+        assert ref.on_curve((BETA * Q[0] % P, Q[1]))
+
+
+def test_basis_is_in_the_lattice_and_spans_it():
+    lam = _lambda()
+    assert (A1 + B1 * lam) % R == 0
+    assert (A2 + B2 * lam) % R == 0
+    assert A1 * B2 - A2 * B1 == R
+    assert A2 == NB1  # (a2, b2) = (-b1, a1 + b1) for this curve: short vectors share a value
+    assert B2 == A1 - B1
+
+
+def test_rounding_multipliers_and_multiples_of_r():
+    assert C["G1"] == (B2 << 256) // R
+    assert C["G2"] == (NB1 << 256) // R
+    assert (C["R1"], C["R2"], C["R4"]) == (R, 2 * R, 4 * R)
+    assert 6 * R > (1 << 256) > 4 * R  # three conditional subtractions reduce any s
+
+
+def test_bound_fits_127_bits():
+    # rounding error of each coefficient < 1/2 (round) + 1/4 (truncated g, s < 2^254)
+    assert 3 * (A1 + A2) < 4 * (1 << 127)
+    assert 3 * (abs(B1) + B2) < 4 * (1 << 127)
+    assert R < (1 << 254)
+
+
+def _split_model(s):
+    """The split's steps on Python integers with the parsed constants."""
+    for m in (C["R4"], C["R2"], C["R1"]):
+        if s >= m:
+            s -= m
+    assert s < R
+    c1 = (s * C["G1"] + (1 << 255)) >> 256
+    c2 = (s * C["G2"] + (1 << 255)) >> 256
+    k1 = s - c1 * A1 - c2 * A2
+    k2 = c1 * NB1 - c2 * B2
+    return s, k1, k2
+
+
+def test_split_identity_and_bound():
+    lam = _lambda()
+    rng = random.Random(2024)
+    edge = [0, 1, 2, R - 1, R, R + 1, 2 * R, 5 * R, (1 << 256) - 1, 1 << 255, 1 << 254,
+            (1 << 254) - 1, lam, R - lam, (R - 1) // 2, (R + 1) // 2]
+    # scalars next to the rounding boundaries of c1 and c2
+    for g in (C["G1"], C["G2"]):
+        for j in range(1, 40):
+            t = ((2 * j + 1) << 255) // g
+            edge += [t - 1, t, t + 1]
+    samples = edge + [rng.getrandbits(256) for _ in range(3000)] + [rng.randrange(R) for _ in range(3000)]
+    for s in samples:
+        s_red, k1, k2 = _split_model(s)
+        assert s_red == s % R
+        assert (k1 + k2 * lam - s) % R == 0, s
+        assert abs(k1) < (1 << 127) and abs(k2) < (1 << 127), s

@@ -5,7 +5,8 @@
   and against the linearity closed form (sum_i s_i r_i mod r) * G;
 * knob invariance: the same bits for every S and several c;
 * edge cases: n = 0, 1, 2, all-zero scalars, {P, P}, {P, -P}, infinity inputs,
-  the arithmetic-progression point set, one giant bucket, and the range error.
+  the arithmetic-progression point set, one giant bucket, and scalars over the
+  whole 256-bit range.
 """
 import random
 
@@ -179,16 +180,18 @@ def test_giant_bucket():
     assert np.array_equal(_gpu_msm(pts, sc, 13, 8), want)
 
 
-def test_range_error():
-    """Signed digits with W = ceil(255 / c) windows cover scalars below 2^(W c - 1)."""
-    M = _msm()
-    pts = _pts([5])
-    sc = wl.from_ints([1 << 255])
-    for c in (15, 16):  # W c - 1 = 254 and 255
-        say("range error c", c)
-        with pytest.raises(M.MsmError) as e:
-            M.msm(to_dev(pts), to_dev(sc), c)
-        assert e.value.code == M.MSM_ERR_RANGE
-    # the same scalar is in range for c = 13 (W c - 1 = 259)
-    want = oracle.msm_pippenger(pts, sc, 13)
-    assert np.array_equal(_gpu_msm(pts, sc, 13), want)
+def test_full_range_scalars():
+    """Every 256-bit scalar is accepted: the split reduces it mod r first. Expected
+    values come from the oracle's unsigned Pippenger at c = 16 (16 windows cover all
+    256 bits, so it adds s P for the integer s) and the closed form."""
+    rng = random.Random(5)
+    dl = [rng.randrange(1, ref.R) for _ in range(40)]
+    ints = [(1 << 256) - 1, 1 << 255, ref.R, 2 * ref.R, 5 * ref.R + 3, (1 << 254) + 1,
+            ref.R - 1, 0] + [rng.getrandbits(256) for _ in range(32)]
+    pts = _pts(dl)
+    sc = wl.from_ints(ints)
+    want = oracle.msm_pippenger(pts, sc, 16)
+    assert ref.decode_point(want) == ref.msm_linear(dl, [s % ref.R for s in ints])
+    for c, S in ((1, 4), (8, 8), (13, 8), (16, 32)):
+        say("full-range scalars c", c, "S", S)
+        assert np.array_equal(_gpu_msm(pts, sc, c, S), want), (c, S)
