@@ -30,12 +30,12 @@ METRIC = "MSM latency ms and points/sec at n=2^16,c=13; achieved int-VALU % of p
 # x 16 lanes per clock (the 64-bit-result multiply issues at half the 32-lane rate of
 # plain 32-bit ALU ops) x 2.4 GHz.
 PEAK_MAD_PER_S = 256 * 4 * 16 * 2.4e9
-P_MOD = 0x30644E72E131A029B85045B68181585D97816A916871CA8D3C208C16D87CFD47
 MAD_PER_MUL = 8 * 8 * 2 + 8          # CIOS product on 8 x 32-bit limbs
 MAD_PER_ADD = 6 * MAD_PER_MUL        # batched affine add: 5 products + 1 square
-# Fermat inverse by binary square-and-multiply: 253 squarings + one product per
-# further set bit of p - 2.
-MAD_PER_INV = (253 + bin(P_MOD - 2).count("1") - 1) * MAD_PER_MUL
+# The inverse (a binary-GCD inverse, of the safegcd class the pages use) is counted as
+# 45 products: the cost that the pages' software profile implies for it (inversion
+# about 47% of the accumulate at S = 8, aztec-packages PR #23732 / #23738).
+MAD_PER_INV = 45 * MAD_PER_MUL
 
 
 def log(*a):

@@ -1,0 +1,241 @@
+// Field inversion by the optimized binary GCD of T. Pornin ("Optimized Binary GCD for
+// Modular Inversion", IACR ePrint 2020/972), the fast replacement for Fermat's x^(p-2).
+//
+// The exact binary GCD keeps a >= 0, b odd, and u, v with a = u y, b = v y (mod p),
+// starting from (a, b, u, v) = (y, p, 1, 0). One step is
+//   a odd and a < b:  swap (a, u) with (b, v)
+//   a odd:            a <- a - b,  u <- u - v
+//   always:           a <- a / 2,  u <- u / 2 (mod p)
+// and 2 len(p) - 1 = 507 steps take a to 0 and b to gcd(y, p) = 1, so y^-1 = v.
+//
+// Batches of 30 steps decide everything from 64-bit stand-ins for a and b: their
+// exact low 30 bits (enough for every parity test of the batch) under the 34 bits
+// just below the top of max(a, b) (for the comparisons). The batch's steps are
+// recorded as signed factors with
+//   a' = (f0 a + g0 b) / 2^30,  b' = (f1 a + g1 b) / 2^30,  |f| + |g| <= 2^30,
+// applied once to the full 254-bit a and b (a wrong comparison from the stand-ins
+// shows up as a negative result, which is negated together with its factors) and to
+// u, v, where the division by 2^30 is exact modular division: add the multiple of p
+// that clears the low 30 bits, shift, then bring the result from (-p, 2p) into
+// [0, p). Every lane runs the same fixed number of batches, so a wavefront never
+// diverges; a lane whose b has not reached 1 (y = 0, or a sequence the batch count
+// does not cover, which tests over many inputs do not produce) takes Fermat's
+// inverse instead, so the result is exact for every input.
+#pragma once
+#include "fp.hpp"
+
+namespace msmk {
+
+#define BG_STEPS 30        // steps per batch
+#define BG_BATCHES 18      // batches: 540 steps
+#define BG_NPINV30 0x24866389u  // -p^-1 mod 2^30
+
+__device__ __forceinline__ uint32_t bg_p(int i) {
+  switch (i) {
+    case 0: return MSM_P0;
+    case 1: return MSM_P1;
+    case 2: return MSM_P2;
+    case 3: return MSM_P3;
+    case 4: return MSM_P4;
+    case 5: return MSM_P5;
+    case 6: return MSM_P6;
+    default: return MSM_P7;
+  }
+}
+
+// 64-bit stand-ins for a and b (see above); exact when both are below 2^64.
+__device__ __forceinline__ void bg_approx(const uint32_t (&a)[8], const uint32_t (&b)[8],
+                                          uint64_t& xa, uint64_t& xb) {
+  uint32_t top = 0;
+  int tw = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const uint32_t o = a[i] | b[i];
+    tw = o ? i : tw;
+    top = o ? o : top;
+  }
+  const int n = 32 * tw + 32 - (top ? __builtin_clz(top) : 32);  // bit length of max(a, b)
+  const uint64_t a01 = ((uint64_t)a[1] << 32) | a[0];
+  const uint64_t b01 = ((uint64_t)b[1] << 32) | b[0];
+  if (n <= 64) {
+    xa = a01;
+    xb = b01;
+    return;
+  }
+  const int sh = n - 34;  // 30 .. 222: bits [sh, sh + 34) are the top 34 of max(a, b)
+  const int q = sh >> 5, r = sh & 31;
+  uint32_t a0 = 0, a1 = 0, a2 = 0, b0 = 0, b1 = 0, b2 = 0;  // words q, q + 1, q + 2
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    a0 = (i == q) ? a[i] : a0;
+    b0 = (i == q) ? b[i] : b0;
+    a1 = (i == q + 1) ? a[i] : a1;
+    b1 = (i == q + 1) ? b[i] : b1;
+    a2 = (i == q + 2) ? a[i] : a2;
+    b2 = (i == q + 2) ? b[i] : b2;
+  }
+  const uint64_t m34 = (1ull << 34) - 1;
+  uint64_t ta = (((uint64_t)a1 << 32) | a0) >> r;
+  uint64_t tb = (((uint64_t)b1 << 32) | b0) >> r;
+  if (r) {
+    ta |= (uint64_t)a2 << (64 - r);
+    tb |= (uint64_t)b2 << (64 - r);
+  }
+  xa = ((ta & m34) << 30) | (a01 & 0x3fffffffull);
+  xb = ((tb & m34) << 30) | (b01 & 0x3fffffffull);
+}
+
+// BG_STEPS binary-GCD steps on the stand-ins; returns the batch's factors.
+__device__ __forceinline__ void bg_batch(uint64_t xa, uint64_t xb, int32_t& f0, int32_t& g0,
+                                         int32_t& f1, int32_t& g1) {
+  f0 = 1;
+  g0 = 0;
+  f1 = 0;
+  g1 = 1;
+#pragma unroll 10
+  for (int j = 0; j < BG_STEPS; j++) {
+    const bool odd = (xa & 1u) != 0;
+    const bool sw = odd && xa < xb;
+    const uint64_t na = sw ? xb : xa, nb = sw ? xa : xb;
+    const int32_t nf0 = sw ? f1 : f0, ng0 = sw ? g1 : g0;
+    const int32_t nf1 = sw ? f0 : f1, ng1 = sw ? g0 : g1;
+    xa = (odd ? na - nb : na) >> 1;
+    xb = nb;
+    f0 = odd ? nf0 - nf1 : nf0;
+    g0 = odd ? ng0 - ng1 : ng0;
+    f1 = (int32_t)((uint32_t)nf1 << 1);
+    g1 = (int32_t)((uint32_t)ng1 << 1);
+  }
+}
+
+// x * f as a two's-complement 64-bit value, for a word x and |f| <= 2^30.
+__device__ __forceinline__ uint64_t bg_smul(uint32_t x, int32_t f) {
+  uint64_t r = (uint64_t)x * (uint32_t)f;
+  return f < 0 ? r - ((uint64_t)x << 32) : r;
+}
+
+// out = |a f + b g| / 2^30 (the sum is a multiple of 2^30); returns true when the sum
+// was negative. |f| + |g| <= 2^30 keeps every column inside a signed 64-bit value.
+__device__ __forceinline__ bool bg_lin(const uint32_t (&a)[8], const uint32_t (&b)[8], int32_t f,
+                                       int32_t g, uint32_t (&out)[8]) {
+  uint32_t t[9];
+  int64_t carry = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int64_t s = (int64_t)bg_smul(a[i], f) + (int64_t)bg_smul(b[i], g) + carry;
+    t[i] = (uint32_t)s;
+    carry = s >> 32;
+  }
+  t[8] = (uint32_t)carry;
+  const bool neg = carry < 0;
+  const uint32_t m = neg ? 0xffffffffu : 0u;
+  uint32_t c = neg ? 1u : 0u;
+#pragma unroll
+  for (int i = 0; i < 9; i++) {
+    const uint64_t s = (uint64_t)(t[i] ^ m) + c;
+    t[i] = (uint32_t)s;
+    c = (uint32_t)(s >> 32);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; i++) out[i] = (t[i] >> 30) | (t[i + 1] << 2);
+  return neg;
+}
+
+// out = (u f + v g) / 2^30 mod p in [0, p), for u, v in [0, p) and |f| + |g| <= 2^30.
+__device__ __forceinline__ void bg_lin_mod(const uint32_t (&u)[8], const uint32_t (&v)[8],
+                                           int32_t f, int32_t g, uint32_t (&out)[8]) {
+  // k p clears the low 30 bits: k = -(u f + v g) p^-1 mod 2^30
+  const uint32_t lo = u[0] * (uint32_t)f + v[0] * (uint32_t)g;
+  const uint32_t k = (lo * BG_NPINV30) & 0x3fffffffu;
+  uint32_t t[9];
+  int64_t carry = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const int64_t s = (int64_t)bg_smul(u[i], f) + (int64_t)bg_smul(v[i], g) +
+                      (int64_t)((uint64_t)k * bg_p(i)) + carry;
+    t[i] = (uint32_t)s;
+    carry = s >> 32;
+  }
+  t[8] = (uint32_t)carry;
+  // r = t / 2^30 lies in (-p, 2p): nine words, the top one signed
+  uint32_t r[9];
+#pragma unroll
+  for (int i = 0; i < 8; i++) r[i] = (t[i] >> 30) | (t[i + 1] << 2);
+  r[8] = (uint32_t)((int32_t)t[8] >> 30);
+  // r + p (used when r < 0) and r - p (used when r >= p)
+  uint32_t rp[8], rm[8];
+  uint32_t cp = 0, bm = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const uint64_t s = (uint64_t)r[i] + bg_p(i) + cp;
+    rp[i] = (uint32_t)s;
+    cp = (uint32_t)(s >> 32);
+    const uint64_t d = (uint64_t)r[i] - bg_p(i) - bm;
+    rm[i] = (uint32_t)d;
+    bm = (uint32_t)(d >> 63);
+  }
+  const bool neg = (int32_t)r[8] < 0;
+  const bool ge = !neg && (r[8] != 0 || bm == 0);
+#pragma unroll
+  for (int i = 0; i < 8; i++) out[i] = neg ? rp[i] : ge ? rm[i] : r[i];
+}
+
+// R^3 mod p: mont(v, R^3) = v R^2 turns the integer inverse of x R into (x^-1) R.
+__device__ __forceinline__ fp bg_r3() {
+  fp c;
+  c.v[0] = 0xda1530dfu; c.v[1] = 0xb1cd6dafu; c.v[2] = 0xa7283db6u; c.v[3] = 0x62f210e6u;
+  c.v[4] = 0x0ada0afbu; c.v[5] = 0xef7f0b0cu; c.v[6] = 0x2d592544u; c.v[7] = 0x20fd6e90u;
+  return c;
+}
+
+// x^-1 for x in Montgomery form (the Montgomery form of the inverse); 0 maps to 0.
+__device__ __forceinline__ fp fp_inv_bingcd(const fp& x) {
+  uint32_t a[8], b[8], u[8], v[8];
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    a[i] = x.v[i];
+    b[i] = bg_p(i);
+    u[i] = i == 0 ? 1u : 0u;
+    v[i] = 0u;
+  }
+  for (int it = 0; it < BG_BATCHES; it++) {
+    uint64_t xa, xb;
+    bg_approx(a, b, xa, xb);
+    int32_t f0, g0, f1, g1;
+    bg_batch(xa, xb, f0, g0, f1, g1);
+    uint32_t na[8], nb[8];
+    if (bg_lin(a, b, f0, g0, na)) {
+      f0 = -f0;
+      g0 = -g0;
+    }
+    if (bg_lin(a, b, f1, g1, nb)) {
+      f1 = -f1;
+      g1 = -g1;
+    }
+    uint32_t nu[8], nv[8];
+    bg_lin_mod(u, v, f0, g0, nu);
+    bg_lin_mod(u, v, f1, g1, nv);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      a[i] = na[i];
+      b[i] = nb[i];
+      u[i] = nu[i];
+      v[i] = nv[i];
+    }
+  }
+  uint32_t one = b[0] ^ 1u;
+#pragma unroll
+  for (int i = 1; i < 8; i++) one |= b[i];
+  fp r;
+  if (one == 0) {
+    fp w;
+#pragma unroll
+    for (int i = 0; i < 8; i++) w.v[i] = v[i];
+    r = fp_mul(w, bg_r3());
+  } else {
+    r = fp_inv_fermat(x);  // x = 0, or b did not reach 1
+  }
+  return r;
+}
+
+}  // namespace msmk

@@ -13,8 +13,8 @@
 //     ALU ops); p < 2^254 keeps every partial sum inside 288 bits and the result
 //     before the final subtraction below 2p. A carry-free form on nine 29-bit limbs
 //     is kept behind MSMK_MONT29 (off);
-//   * inversion is Fermat's x^(p-2) (fp_inv_fermat); a divstep inverse lives in
-//     inv.hpp behind MSMK_DIVSTEPS (off).
+//   * Fermat's x^(p-2) (fp_inv_fermat) is here; the inverse the kernels use is the
+//     binary GCD of bingcd.hpp (Fermat remains its fallback), selected in inv.hpp.
 //
 // Everything is branch-free except where noted, so a wavefront never diverges on
 // field values.

@@ -20,6 +20,7 @@
 // 30 bits. At the end x^-1 = f d (f = +-1). |d| and |e| grow by less than p per
 // batch, so they stay below 26 p and fit the nine signed 30-bit limbs.
 #pragma once
+#include "bingcd.hpp"
 #include "fp.hpp"
 
 namespace msmk {
@@ -205,10 +206,17 @@ __device__ __forceinline__ fp fp_inv_divsteps(const fp& x) {
   return fp_mul(inv, r3);
 }
 
+// fp_inv: the binary-GCD inverse (bingcd.hpp) unless MSMK_FERMAT_INV selects
+// Fermat's x^(p-2) or MSMK_DIVSTEPS the divstep inverse above (off, see there).
+#ifndef MSMK_FERMAT_INV
+#define MSMK_FERMAT_INV 0
+#endif
 #if MSMK_DIVSTEPS
 __device__ __forceinline__ fp fp_inv(const fp& x) { return fp_inv_divsteps(x); }
-#else
+#elif MSMK_FERMAT_INV
 __device__ __forceinline__ fp fp_inv(const fp& x) { return fp_inv_fermat(x); }
+#else
+__device__ __forceinline__ fp fp_inv(const fp& x) { return fp_inv_bingcd(x); }
 #endif
 
 }  // namespace msmk

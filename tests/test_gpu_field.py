@@ -29,9 +29,13 @@ EDGE = [e % P for e in EDGE]
 def test_fp_ops_match_python(op):
     from elliptic_curve_scalar_amd import msm as M
     rng = random.Random(100 + op)
-    n = 4099 if op != 4 else 515   # several blocks and a ragged tail
-    xs = EDGE + [rng.randrange(P) for _ in range(n - len(EDGE))]
-    ys = list(reversed(EDGE)) + [rng.randrange(P) for _ in range(n - len(EDGE))]
+    n = 4099  # several blocks and a ragged tail
+    edge = EDGE
+    if op == 4:  # the binary-GCD inverse: powers of two and their neighbours, tiny values
+        edge = EDGE + [1 << k for k in range(254)] + [P - (1 << k) for k in range(254)] + \
+            [(1 << k) - 1 for k in range(2, 254)] + list(range(4, 64))
+    xs = edge + [rng.randrange(P) for _ in range(n - len(edge))]
+    ys = list(reversed(edge)) + [rng.randrange(P) for _ in range(n - len(edge))]
     say("fp op", op, "n", n)
     got = wl.to_ints(to_host(M.test_fp(op, to_dev(_words(xs)), to_dev(_words(ys)))))
     rinv = pow(1 << 256, -1, P)
