@@ -53,6 +53,9 @@ def main() -> int:
                     help="pair-tree levels done with batched affine adds (-1: all)")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0,
                     help="CPU seconds for the oracle baseline (0 disables it)")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="after timing, copy a buffer of this many MiB on the device once: "
+                         "a kernel of known traffic for scaling hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -102,6 +105,11 @@ def main() -> int:
     ctx.set_timing(False)
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     gpu_out = out.cpu().numpy().astype(np.uint32)
+    if args.copy_mb > 0:
+        src = torch.ones(args.copy_mb << 18, dtype=torch.int32, device=dev)
+        dst = src.clone()
+        torch.cuda.synchronize()
+        del src, dst
     log(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step")
 
     runs = max(1, tm["runs"])

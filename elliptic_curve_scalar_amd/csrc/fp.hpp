@@ -146,29 +146,51 @@ __device__ __forceinline__ fp fp_dbl(const fp& a) { return fp_add(a, a); }
 
 // Montgomery product a * b * 2^-256 mod p, coarsely integrated operand scanning on
 // 32-bit limbs (the default product; see MSMK_MONT29 below).
+// 64-bit value kept whole through code generation: the empty asm stops the compiler
+// from re-associating a * b + (t + c) into (a * b + t) + c, which costs two 64-bit
+// adds and the register moves that widen t and c, where the form below costs one
+// 32-bit add and the select of its carry.
+__device__ __forceinline__ uint64_t fp_opaque(uint64_t x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm("" : "+v"(x));
+#endif
+  return x;
+}
+
+// t + c (both 32-bit) as a 64-bit multiply-add addend.
+__device__ __forceinline__ uint64_t fp_add33(uint32_t t, uint32_t c) {
+  const uint32_t lo = t + c;
+  const uint32_t hi = lo < c ? 1u : 0u;
+  return fp_opaque(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ fp fp_mul_cios(const fp& a, const fp& b) {
   uint32_t t[9];
 #pragma unroll
   for (int j = 0; j < 9; j++) t[j] = 0;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
-    uint64_t c = 0;
+    // t += a * b_i: each step is (hi, lo) = a_j b_i + (t_j + carry), which fits 64 bits
+    uint32_t c = 0;
 #pragma unroll
     for (int j = 0; j < 8; j++) {
-      c = (uint64_t)a.v[j] * b.v[i] + t[j] + (c >> 32);
-      t[j] = (uint32_t)c;
+      const uint64_t s = (uint64_t)a.v[j] * b.v[i] + (i == 0 ? fp_opaque(c) : fp_add33(t[j], c));
+      t[j] = (uint32_t)s;
+      c = (uint32_t)(s >> 32);
     }
-    uint64_t top = (uint64_t)t[8] + (c >> 32);
+    uint64_t top = (uint64_t)t[8] + c;
     t[8] = (uint32_t)top;
     // with p < 2^254 the running value stays below 2p * 2^32, so no word above t[8]
-    uint32_t m = t[0] * MSM_PINV;
-    c = (uint64_t)m * p_limb(0) + t[0];
+    const uint32_t m = t[0] * MSM_PINV;
+    const uint64_t s0 = (uint64_t)m * p_limb(0) + fp_opaque(t[0]);
+    c = (uint32_t)(s0 >> 32);
 #pragma unroll
     for (int j = 1; j < 8; j++) {
-      c = (uint64_t)m * p_limb(j) + t[j] + (c >> 32);
-      t[j - 1] = (uint32_t)c;
+      const uint64_t s = (uint64_t)m * p_limb(j) + fp_add33(t[j], c);
+      t[j - 1] = (uint32_t)s;
+      c = (uint32_t)(s >> 32);
     }
-    top = (uint64_t)t[8] + (c >> 32);
+    top = (uint64_t)t[8] + c;
     t[7] = (uint32_t)top;
     t[8] = (uint32_t)(top >> 32);
   }
@@ -310,8 +332,8 @@ __device__ __forceinline__ fp fp_from_u32(uint32_t c) {
 
 // x^(p-2) mod p, the inverse of a non-zero x (0 maps to 0): left-to-right binary
 // square-and-multiply. The exponent is the same for every lane, so the multiply
-// branch is uniform across the wavefront. (The library inverts with divsteps,
-// inv.hpp; this form is kept as a cross-check.)
+// branch is uniform across the wavefront. (The library inverts with the binary GCD
+// of bingcd.hpp, which falls back to this form for x = 0.)
 __device__ __forceinline__ fp fp_inv_fermat(const fp& x) {
   const uint32_t e[8] = {MSM_P0 - 2u, MSM_P1, MSM_P2, MSM_P3, MSM_P4, MSM_P5, MSM_P6, MSM_P7};
   fp acc = x;  // the exponent's top bit (bit 253) is set

@@ -44,7 +44,7 @@ uint32_t segment_length(int c, int nwin) {
 }
 
 struct Layout {
-  size_t stats, halfs, pts2, counts, offsets, cursor, poff, block_sums, sorted_idx, aff_a, aff_b,
+  size_t stats, halfs, pts2, counts, offsets, rank, poff, block_sums, sorted_idx, aff_a, aff_b,
       xz_a, xz_b, bsum, seg, win;
   size_t total;
   uint32_t K, nwin, seg_len, nseg;
@@ -71,7 +71,7 @@ Layout plan(size_t n, int c) {
   L.pts2 = take(2 * n * sizeof(g1a));
   L.counts = take((size_t)L.K * 4);
   L.offsets = take(((size_t)L.K + 1) * 4);
-  L.cursor = take((size_t)L.K * 4);
+  L.rank = take((size_t)L.nwin * 2 * n * 4);  // rank of each (window, half-scalar) entry
   L.poff = take(((size_t)L.K + 1) * 4);
   L.block_sums = take((nb + 1) * 4);
   L.sorted_idx = take(L.E_max * 4);
@@ -236,7 +236,7 @@ int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scala
   g1a* pts2 = (g1a*)(ws + L.pts2);
   uint32_t* counts = (uint32_t*)(ws + L.counts);
   uint32_t* offsets = (uint32_t*)(ws + L.offsets);
-  uint32_t* cursor = (uint32_t*)(ws + L.cursor);
+  uint32_t* rank = (uint32_t*)(ws + L.rank);
   uint32_t* poff = (uint32_t*)(ws + L.poff);
   uint32_t* block_sums = (uint32_t*)(ws + L.block_sums);
   uint32_t* sorted_idx = (uint32_t*)(ws + L.sorted_idx);
@@ -253,10 +253,10 @@ int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scala
   HIP_TRY(launch_fill((uint32_t*)stats, sizeof(msm_stats) / 4, 0, st));
   HIP_TRY(launch_fill(counts, L.K, 0, st));
   HIP_TRY(launch_glv_prep((const g1a*)d_points, d_scalars, n32, pts2, halfs, stats, st));
-  HIP_TRY(launch_hist(halfs, m32, c32, L.nwin, counts, st));
-  HIP_TRY(launch_scan(counts, L.K, -1, block_sums, offsets, cursor, st));
+  HIP_TRY(launch_hist(halfs, m32, c32, L.nwin, counts, rank, st));
+  HIP_TRY(launch_scan(counts, L.K, -1, block_sums, offsets, nullptr, st));
   HIP_TRY(launch_stats(counts, L.K, stats, st));
-  HIP_TRY(launch_scatter(halfs, m32, c32, L.nwin, cursor, sorted_idx, st));
+  HIP_TRY(launch_scatter(halfs, m32, c32, L.nwin, offsets, rank, sorted_idx, st));
   HIP_TRY(hipMemcpyAsync(ctx->host_stats, stats, sizeof(msm_stats), hipMemcpyDeviceToHost, st));
   ph_sort.end();
   HIP_TRY(hipStreamSynchronize(st));

@@ -35,9 +35,10 @@ hipError_t launch_fill(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
 hipError_t launch_glv_prep(const g1a* points, const uint32_t* scalars, uint32_t n, g1a* pts2,
                            uint32_t* halfs, msm_stats* st, hipStream_t s);
 hipError_t launch_hist(const uint32_t* halfs, uint32_t m, uint32_t c, uint32_t nwin,
-                       uint32_t* counts, hipStream_t s);
+                       uint32_t* counts, uint32_t* rank, hipStream_t s);
 hipError_t launch_scatter(const uint32_t* halfs, uint32_t m, uint32_t c, uint32_t nwin,
-                          uint32_t* cursor, uint32_t* sorted_idx, hipStream_t s);
+                          const uint32_t* offsets, const uint32_t* rank, uint32_t* sorted_idx,
+                          hipStream_t s);
 hipError_t launch_scan(const uint32_t* counts, uint32_t n, int level, uint32_t* block_sums,
                        uint32_t* out, uint32_t* out2, hipStream_t s);
 hipError_t launch_stats(const uint32_t* counts, uint32_t K, msm_stats* st, hipStream_t s);

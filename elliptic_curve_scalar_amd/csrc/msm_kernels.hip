@@ -3,7 +3,7 @@
 // Pipeline (one stream; W = ceil(254 / c) windows, 2^c buckets per window, digit 0
 // dropped since it adds nothing):
 //   k_hist        scalar -> W window digits, per-(window, digit) counts (global atomics)
-//   k_scan_*      exclusive scan of the counts -> bucket offsets (and scatter cursors)
+//   k_scan_*      exclusive scan of the counts -> bucket offsets
 //   k_stats       largest bucket, number of pair adds at every pair-tree level
 //   k_scatter     point indices into per-bucket lists (sorted_idx)
 //   -- host reads the stats back (one sync) --
@@ -125,23 +125,29 @@ __device__ __forceinline__ sc256 load_half(const uint32_t* halfs, uint32_t i, bo
   return r;
 }
 
+// Counting pass of the counting sort. The atomic on a bucket's count also returns the
+// entry's rank among the bucket's entries; it is kept (rank[j m + i] for window j of
+// half-scalar i) so that the scatter needs no second round of atomics.
 __global__ void __launch_bounds__(256) k_hist(const uint32_t* __restrict__ halfs, uint32_t m,
                                               uint32_t c, uint32_t nwin,
-                                              uint32_t* __restrict__ counts) {
+                                              uint32_t* __restrict__ counts,
+                                              uint32_t* __restrict__ rank) {
   uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= m) return;
   bool neg;
   const sc256 s = load_half(halfs, i, neg);
   const uint32_t sh = c - 1;
   for_each_signed_digit(s, c, nwin, [&](uint32_t j, uint32_t slot, bool) {
-    atomicAdd(&counts[(j << sh) | slot], 1u);
+    rank[(size_t)j * m + i] = atomicAdd(&counts[(j << sh) | slot], 1u);
   });
 }
 
-// Bucket lists hold point indices with the sign of (digit x half-scalar) in bit 31.
+// Bucket lists hold point indices with the sign of (digit x half-scalar) in bit 31,
+// written at the bucket's offset plus the rank the counting pass handed out.
 __global__ void __launch_bounds__(256) k_scatter(const uint32_t* __restrict__ halfs, uint32_t m,
                                                  uint32_t c, uint32_t nwin,
-                                                 uint32_t* __restrict__ cursor,
+                                                 const uint32_t* __restrict__ offsets,
+                                                 const uint32_t* __restrict__ rank,
                                                  uint32_t* __restrict__ sorted_idx) {
   uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= m) return;
@@ -149,7 +155,7 @@ __global__ void __launch_bounds__(256) k_scatter(const uint32_t* __restrict__ ha
   const sc256 s = load_half(halfs, i, sneg);
   const uint32_t sh = c - 1;
   for_each_signed_digit(s, c, nwin, [&](uint32_t j, uint32_t slot, bool neg) {
-    uint32_t pos = atomicAdd(&cursor[(j << sh) | slot], 1u);
+    const uint32_t pos = offsets[(j << sh) | slot] + rank[(size_t)j * m + i];
     sorted_idx[pos] = i | ((neg != sneg) ? 0x80000000u : 0u);
   });
 }
@@ -767,14 +773,15 @@ hipError_t launch_glv_prep(const g1a* points, const uint32_t* scalars, uint32_t 
 }
 
 hipError_t launch_hist(const uint32_t* halfs, uint32_t m, uint32_t c, uint32_t nwin,
-                       uint32_t* counts, hipStream_t s) {
-  k_hist<<<grid_for(m, 256), 256, 0, s>>>(halfs, m, c, nwin, counts);
+                       uint32_t* counts, uint32_t* rank, hipStream_t s) {
+  k_hist<<<grid_for(m, 256), 256, 0, s>>>(halfs, m, c, nwin, counts, rank);
   return hipGetLastError();
 }
 
 hipError_t launch_scatter(const uint32_t* halfs, uint32_t m, uint32_t c, uint32_t nwin,
-                          uint32_t* cursor, uint32_t* sorted_idx, hipStream_t s) {
-  k_scatter<<<grid_for(m, 256), 256, 0, s>>>(halfs, m, c, nwin, cursor, sorted_idx);
+                          const uint32_t* offsets, const uint32_t* rank, uint32_t* sorted_idx,
+                          hipStream_t s) {
+  k_scatter<<<grid_for(m, 256), 256, 0, s>>>(halfs, m, c, nwin, offsets, rank, sorted_idx);
   return hipGetLastError();
 }
 
