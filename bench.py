@@ -42,6 +42,37 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources: hardware counters taken on another build do not apply."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "elliptic_curve_scalar_amd", "csrc", "*"))):
+        if f.endswith((".hip", ".hpp")):
+            h.update(os.path.basename(f).encode())
+            with open(f, "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, S: int, affine_levels: int, src: str):
+    """HBM bytes per launch of the batched-affine kernel from the committed counter
+    summary (rocprofv3 FETCH_SIZE and WRITE_SIZE, scaled by a copy of known size), or
+    None when no entry matches this workload, S, schedule and kernel source."""
+    path = os.path.join(ROOT, "profiles", "k_level_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        for line in fh:
+            if not line.startswith("traffic: "):
+                continue
+            rec = json.loads(line[len("traffic: "):])
+            if (rec["workload"], rec["S"], rec["affine_levels"], rec["src"]) == (
+                    workload, S, affine_levels, src):
+                return rec
+    return None
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +148,8 @@ def main() -> int:
     mads = tm["level_pairs"] * MAD_PER_ADD + tm["level_lanes"] * MAD_PER_INV
     level_s = tm["level_kernel_ms"] * 1e-3
     achieved = mads / level_s if level_s > 0 else 0.0
+    al = args.affine_levels if args.affine_levels is not None else 1
+    tr = measured_traffic(args.workload, S, al, kernel_source_hash())
     roofline = {
         "bound": "alu",
         "kernel": f"k_level<{S}> (pair-tree batched-affine accumulate)",
@@ -125,7 +158,8 @@ def main() -> int:
         "unit": "TOP/s",
         "op": "32x32->64-bit multiply-add (algorithmic count)",
         "frac": achieved / PEAK_MAD_PER_S,
-        "traffic": None,
+        "traffic": tr["bytes_per_launch"] if tr else None,
+        "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
         "launches_per_step": tm["level_launches"] / runs,
         "avg_launch_ms": tm["level_kernel_ms"] / launches,
         "algorithmic_ops_per_launch": mads / launches,

@@ -45,7 +45,7 @@ uint32_t segment_length(int c, int nwin) {
 
 struct Layout {
   size_t stats, halfs, pts2, counts, offsets, rank, poff, block_sums, sorted_idx, aff_a, aff_b,
-      xz_a, xz_b, bsum, seg, win;
+      xz_a, xz_b, bsum, seg, part, win;
   size_t total;
   uint32_t K, nwin, seg_len, nseg;
   size_t E_max, half;
@@ -81,6 +81,7 @@ Layout plan(size_t n, int c) {
   L.xz_b = take(L.half * sizeof(xyzz_st));
   L.bsum = take((size_t)L.K * sizeof(xyzz_st));
   L.seg = take((size_t)L.nwin * L.nseg * sizeof(xyzz_st));
+  L.part = take((size_t)L.nwin * reduce_blocks(L.nseg) * sizeof(xyzz_st));
   L.win = take((size_t)L.nwin * sizeof(xyzz_st));
   L.total = off;
   return L;
@@ -244,6 +245,7 @@ int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scala
   xyzz_st* xz[2] = {(xyzz_st*)(ws + L.xz_a), (xyzz_st*)(ws + L.xz_b)};
   xyzz_st* bsum = (xyzz_st*)(ws + L.bsum);
   xyzz_st* seg = (xyzz_st*)(ws + L.seg);
+  xyzz_st* part = (xyzz_st*)(ws + L.part);
   xyzz_st* win = (xyzz_st*)(ws + L.win);
   const g1a* pts = pts2;  // 2n points: P_i and phi(P_i)
   uint32_t n32 = (uint32_t)n, m32 = 2 * (uint32_t)n, c32 = (uint32_t)c;
@@ -300,7 +302,7 @@ int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scala
 
   // running sum per window, window combine
   PhaseMark ph_red(ctx, st, PH_REDUCE);
-  HIP_TRY(launch_reduce(bsum, c32, L.nwin, L.seg_len, L.nseg, seg, win, st));
+  HIP_TRY(launch_reduce(bsum, c32, L.nwin, L.seg_len, L.nseg, seg, part, win, st));
   ph_red.end();
   PhaseMark ph_fin(ctx, st, PH_FINAL);
   HIP_TRY(launch_final(win, L.nwin, c32, (g1a*)d_out, st));

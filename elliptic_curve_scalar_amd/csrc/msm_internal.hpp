@@ -52,8 +52,14 @@ hipError_t launch_level_xyzz(bool in_aff, const void* in, const uint32_t* idx, x
                              xyzz_st* bsum, const uint32_t* counts, const uint32_t* offsets,
                              const uint32_t* poff, uint32_t K, uint32_t npairs, int level,
                              hipStream_t s);
+// Blocks per window in the first pass of the segment-sum tree: 64 segments per block,
+// at most 64 blocks.
+inline uint32_t reduce_blocks(uint32_t nseg) {
+  uint32_t b = (nseg + 63) / 64;
+  return b < 1 ? 1 : (b > 64 ? 64 : b);
+}
 hipError_t launch_reduce(const xyzz_st* bsum, uint32_t c, uint32_t nwin, uint32_t seg_len,
-                         uint32_t nseg, xyzz_st* seg, xyzz_st* win, hipStream_t s);
+                         uint32_t nseg, xyzz_st* seg, xyzz_st* part, xyzz_st* win, hipStream_t s);
 hipError_t launch_final(const xyzz_st* win, uint32_t nwin, uint32_t c, g1a* out, hipStream_t s);
 hipError_t launch_from_scalars(const uint32_t* ks, uint32_t n, g1a* out, hipStream_t s);
 hipError_t launch_test_fp(int op, const uint32_t* a, const uint32_t* b, uint32_t* out, uint32_t n,

@@ -11,7 +11,7 @@
 //   k_level<S>    pair-tree level l: pair (2m, 2m+1) of every bucket -> element m,
 //                 S pairs per lane with one inversion (batch_add.hpp)
 //   k_rsum_seg    per window, segments of buckets: sum_b b * B_b by a running sum
-//   k_rsum_win    per window: tree over its segments -> W_j
+//   k_tree_sum    per window: two-pass tree over its segments -> W_j
 //   k_final       Q = sum_j 2^(c j) W_j by doubling (Horner), then affine
 //
 // The method is aztec-packages PR #23738 / #23736 / #23520 ("bb/msm"); its WebGPU
@@ -545,15 +545,20 @@ __global__ void __launch_bounds__(128) k_rsum_seg(const xyzz_st* __restrict__ bs
   if (q == 0) xyzz_store(seg_out + t, res);
 }
 
-// One block per window: 64 quads sum strided segments, then a tree through LDS.
-__global__ void __launch_bounds__(256) k_rsum_win(const xyzz_st* __restrict__ seg, uint32_t nseg,
-                                                  xyzz_st* __restrict__ win) {
+// Sums of groups of n consecutive XYZZ points, split over nblk blocks per group:
+// block b of group g adds items [b chunk, (b + 1) chunk) of the group (chunk =
+// ceil(n / nblk)), its 64 quads striding over them, then a tree through LDS, and
+// writes out[g nblk + b]. Two passes (nblk blocks, then one) turn a group of up to
+// 4096 segment sums into its window sum with about 14 dependent additions.
+__global__ void __launch_bounds__(256) k_tree_sum(const xyzz_st* __restrict__ in, uint32_t n,
+                                                  uint32_t nblk, xyzz_st* __restrict__ out) {
   __shared__ xyzz_st lds[64];
-  const uint32_t j = blockIdx.x, quad = threadIdx.x >> 2;
+  const uint32_t g = blockIdx.x / nblk, b = blockIdx.x % nblk, quad = threadIdx.x >> 2;
   const int q = (int)(threadIdx.x & 3u);
+  const uint32_t chunk = (n + nblk - 1) / nblk;
+  const uint32_t lo = b * chunk, hi = min(n, lo + chunk);
   xyzz acc = xyzz_inf();
-  for (uint32_t s = quad; s < nseg; s += 64)
-    acc = quad_add(acc, xyzz_load(seg + (size_t)j * nseg + s), q);
+  for (uint32_t i = lo + quad; i < hi; i += 64) acc = quad_add(acc, xyzz_load(in + (size_t)g * n + i), q);
   if (q == 0) xyzz_store(&lds[quad], acc);
   __syncthreads();
   for (uint32_t stride = 32; stride > 0; stride >>= 1) {
@@ -563,7 +568,7 @@ __global__ void __launch_bounds__(256) k_rsum_win(const xyzz_st* __restrict__ se
     }
     __syncthreads();
   }
-  if (threadIdx.x == 0) xyzz_store(win + j, acc);
+  if (threadIdx.x == 0) xyzz_store(out + (size_t)g * nblk + b, acc);
 }
 
 // ---- window combine: one wave, independent products spread over its lanes ----
@@ -852,9 +857,11 @@ hipError_t launch_level_xyzz(bool in_aff, const void* in, const uint32_t* idx, x
 }
 
 hipError_t launch_reduce(const xyzz_st* bsum, uint32_t c, uint32_t nwin, uint32_t seg_len,
-                         uint32_t nseg, xyzz_st* seg, xyzz_st* win, hipStream_t s) {
+                         uint32_t nseg, xyzz_st* seg, xyzz_st* part, xyzz_st* win, hipStream_t s) {
   k_rsum_seg<<<grid_for((size_t)nwin * nseg * 4, 128), 128, 0, s>>>(bsum, c, nwin, seg_len, nseg, seg);
-  k_rsum_win<<<nwin, 256, 0, s>>>(seg, nseg, win);
+  const uint32_t nblk = reduce_blocks(nseg);
+  k_tree_sum<<<nwin * nblk, 256, 0, s>>>(seg, nseg, nblk, part);
+  k_tree_sum<<<nwin, 256, 0, s>>>(part, nblk, 1, win);
   return hipGetLastError();
 }
 
