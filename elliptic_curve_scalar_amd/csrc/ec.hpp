@@ -145,6 +145,28 @@ __device__ __forceinline__ xyzz xyzz_add_aff(const xyzz& p, const aff& q) {
   return r;
 }
 
+// P + Q for two affine points, XYZZ result (mmadd-2008-s: 4M + 2S); every special
+// case handled.
+__device__ __forceinline__ xyzz xyzz_add_aa(const aff& p, const aff& q) {
+  if (aff_is_inf(q)) return xyzz_from_aff(p);
+  if (aff_is_inf(p)) return xyzz_from_aff(q);
+  const fp P = fp_sub(q.x, p.x);
+  const fp R = fp_sub(q.y, p.y);
+  if (fp_is_zero(P)) {
+    if (fp_is_zero(R)) return xyzz_dbl_aff(p);
+    return xyzz_inf();
+  }
+  const fp PP = fp_sqr(P);
+  const fp PPP = fp_mul(P, PP);
+  const fp Q = fp_mul(p.x, PP);
+  xyzz r;
+  r.X = fp_sub(fp_sub(fp_sub(fp_sqr(R), PPP), Q), Q);
+  r.Y = fp_sub(fp_mul(R, fp_sub(Q, r.X)), fp_mul(p.y, PPP));
+  r.ZZ = PP;
+  r.ZZZ = PPP;
+  return r;
+}
+
 // P + Q, both XYZZ (add-2008-s), every special case handled.
 __device__ __forceinline__ xyzz xyzz_add(const xyzz& p, const xyzz& q) {
   if (xyzz_is_inf(q)) return p;

@@ -468,7 +468,7 @@ __global__ void __launch_bounds__(128) k_level_xyzz(const void* __restrict__ in_
   xyzz r;
   if (IN_AFF) {
     uint32_t ia = base + 2 * m;
-    r = xyzz_add_aff(xyzz_from_aff(load_aff(ia)), load_aff(ia + 1));
+    r = xyzz_add_aa(load_aff(ia), load_aff(ia + 1));
   } else {
     r = xyzz_add(load(base + 2 * m), load(base + 2 * m + 1));
   }
@@ -501,14 +501,16 @@ __global__ void __launch_bounds__(128) k_level_xyzz_q(const void* __restrict__ i
   uint32_t off = offsets[k];
   uint32_t base = idx ? off : half_base(off, k);
   uint32_t cl = level_count(counts[k], level);
+  auto load_aff = [&](uint32_t pos) -> aff {
+    const g1a* in = reinterpret_cast<const g1a*>(in_);
+    return idx ? load_entry(in, idx[pos]) : aff_load(in + pos);
+  };
   auto load = [&](uint32_t pos) -> xyzz {
-    if (IN_AFF) {
-      const g1a* in = reinterpret_cast<const g1a*>(in_);
-      return xyzz_from_aff(idx ? load_entry(in, idx[pos]) : aff_load(in + pos));
-    }
+    if (IN_AFF) return xyzz_from_aff(load_aff(pos));
     return xyzz_load(reinterpret_cast<const xyzz_st*>(in_) + pos);
   };
-  const xyzz r = quad_add(load(base + 2 * m), load(base + 2 * m + 1), q);
+  const xyzz r = IN_AFF ? quad_add_aa(load_aff(base + 2 * m), load_aff(base + 2 * m + 1), q)
+                        : quad_add(load(base + 2 * m), load(base + 2 * m + 1), q);
   if (q != 0) return;
   if (cl == 2) {
     xyzz_store(bsum + k, r);

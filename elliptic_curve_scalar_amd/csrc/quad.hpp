@@ -79,6 +79,28 @@ __device__ __forceinline__ xyzz quad_add(const xyzz& p, const xyzz& s, int q) {
   return o;
 }
 
+// P + Q for two affine points (mmadd-2008-s), quad-cooperative: 3 rounds.
+__device__ __forceinline__ xyzz quad_add_aa(const aff& p, const aff& s, int q) {
+  if (aff_is_inf(s)) return xyzz_from_aff(p);
+  if (aff_is_inf(p)) return xyzz_from_aff(s);
+  const fp P = fp_sub(s.x, p.x), R = fp_sub(s.y, p.y);
+  if (fp_is_zero(P)) {
+    if (fp_is_zero(R)) return quad_dbl(xyzz_from_aff(p), q);
+    return xyzz_inf();
+  }
+  fp r = fp_mul(quad_pick(q, P, R, P, R), quad_pick(q, P, R, P, R));  // PP, RR
+  const fp PP = quad_from<0>(r), RR = quad_from<1>(r);
+  r = fp_mul(quad_pick(q, P, p.x, P, p.x), PP);                        // PPP, Q
+  const fp PPP = quad_from<0>(r), Qv = quad_from<1>(r);
+  xyzz o;
+  o.X = fp_sub(fp_sub(fp_sub(RR, PPP), Qv), Qv);
+  r = fp_mul(quad_pick(q, R, p.y, R, p.y), quad_pick(q, fp_sub(Qv, o.X), PPP, fp_sub(Qv, o.X), PPP));
+  o.Y = fp_sub(quad_from<0>(r), quad_from<1>(r));                      // R (Q - X3) - Y1 PPP
+  o.ZZ = PP;
+  o.ZZZ = PPP;
+  return o;
+}
+
 // k * P for a small non-negative k (MSB-first double-and-add), quad-cooperative.
 __device__ __forceinline__ xyzz quad_mul_small(const xyzz& p, uint32_t k, int q) {
   if (k == 0) return xyzz_inf();
