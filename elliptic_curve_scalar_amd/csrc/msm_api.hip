@@ -59,7 +59,6 @@ Layout plan(size_t n, int c) {
   L.nseg = ((1u << (c - 1)) + L.seg_len - 1) / L.seg_len;
   L.E_max = 2 * n * L.nwin;  // 2n GLV points
   L.half = (L.E_max + L.K) / 2 + 1;  // elements of a level >= 1 buffer
-  size_t nb = (L.K + SCAN_TILE - 1) / SCAN_TILE + 1;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t at = off;
@@ -72,8 +71,8 @@ Layout plan(size_t n, int c) {
   L.counts = take((size_t)L.K * 4);
   L.offsets = take(((size_t)L.K + 1) * 4);
   L.rank = take((size_t)L.nwin * 2 * n * 4);  // rank of each (window, half-scalar) entry
-  L.poff = take(((size_t)L.K + 1) * 4);
-  L.block_sums = take((nb + 1) * 4);
+  L.poff = take((size_t)MAX_LEVELS * ((size_t)L.K + 1) * 4);  // pair offsets of every level
+  L.block_sums = take((size_t)MAX_LEVELS * (scan_blocks(L.K) + 1) * 4);
   L.sorted_idx = take(L.E_max * 4);
   L.aff_a = take(L.half * sizeof(g1a));
   L.aff_b = take(L.half * sizeof(g1a));
@@ -256,7 +255,7 @@ int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scala
   HIP_TRY(launch_fill(counts, L.K, 0, st));
   HIP_TRY(launch_glv_prep((const g1a*)d_points, d_scalars, n32, pts2, halfs, stats, st));
   HIP_TRY(launch_hist(halfs, m32, c32, L.nwin, counts, rank, st));
-  HIP_TRY(launch_scan(counts, L.K, -1, block_sums, offsets, nullptr, st));
+  HIP_TRY(launch_scan(counts, L.K, -1, 1, block_sums, offsets, L.K + 1, st));
   HIP_TRY(launch_stats(counts, L.K, stats, st));
   HIP_TRY(launch_scatter(halfs, m32, c32, L.nwin, offsets, rank, sorted_idx, st));
   HIP_TRY(hipMemcpyAsync(ctx->host_stats, stats, sizeof(msm_stats), hipMemcpyDeviceToHost, st));
@@ -270,17 +269,20 @@ int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scala
   HIP_TRY(launch_bucket_init(counts, offsets, L.K, sorted_idx, pts, bsum, st));
   int levels = 0;
   while (levels < MAX_LEVELS && ((uint64_t)1 << levels) < hs.max_count) levels++;
+  // pair offsets of every level at once: level l at poff_all + l (K + 1)
+  uint32_t* const poff_all = poff;
+  HIP_TRY(launch_scan(counts, L.K, 0, levels, block_sums, poff_all, (size_t)L.K + 1, st));
   for (int l = 0; l < levels; l++) {
     uint32_t np = hs.pairs[l];
     if (np == 0) continue;
-    HIP_TRY(launch_scan(counts, L.K, l, block_sums, poff, nullptr, st));
+    const uint32_t* lvl_poff = poff_all + (size_t)l * (L.K + 1);
     const uint32_t* idx = (l == 0) ? sorted_idx : nullptr;
     const int La = ctx->affine_levels < 0 ? MAX_LEVELS : ctx->affine_levels;
     if (l < La) {
       // batched affine adds, S per lane sharing one inversion
       const g1a* in = (l == 0) ? pts : aff[(l - 1) & 1];
       PhaseMark ph_lvl(ctx, st, PH_LEVEL);
-      HIP_TRY(launch_level(S, in, idx, aff[l & 1], bsum, counts, offsets, poff, L.K, np, l, st));
+      HIP_TRY(launch_level(S, in, idx, aff[l & 1], bsum, counts, offsets, lvl_poff, L.K, np, l, st));
       ph_lvl.end();
       if (ctx->timing) {
         ctx->level_launches++;
@@ -293,8 +295,8 @@ int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scala
       const void* in = (l == 0) ? (const void*)pts
                        : in_aff ? (const void*)aff[(l - 1) & 1] : (const void*)xz[(l - 1) & 1];
       PhaseMark ph_lvl(ctx, st, PH_XYZZ);
-      HIP_TRY(launch_level_xyzz(in_aff, in, idx, xz[l & 1], bsum, counts, offsets, poff, L.K, np,
-                                l, st));
+      HIP_TRY(launch_level_xyzz(in_aff, in, idx, xz[l & 1], bsum, counts, offsets, lvl_poff, L.K,
+                                np, l, st));
       ph_lvl.end();
     }
   }

@@ -39,8 +39,17 @@ hipError_t launch_hist(const uint32_t* halfs, uint32_t m, uint32_t c, uint32_t n
 hipError_t launch_scatter(const uint32_t* halfs, uint32_t m, uint32_t c, uint32_t nwin,
                           const uint32_t* offsets, const uint32_t* rank, uint32_t* sorted_idx,
                           hipStream_t s);
-hipError_t launch_scan(const uint32_t* counts, uint32_t n, int level, uint32_t* block_sums,
-                       uint32_t* out, uint32_t* out2, hipStream_t s);
+// Blocks of the tile scan over n values.
+inline uint32_t scan_blocks(uint32_t n) {
+  uint32_t nb = (n + SCAN_TILE - 1) / SCAN_TILE;
+  return nb ? nb : 1;
+}
+// Exclusive scans of the per-bucket values of levels level0 .. level0 + nlev - 1 (level
+// -1: the counts themselves; level l >= 0: the pair adds at pair-tree level l). Level
+// level0 + y writes n + 1 values (the total last) at out + y out_stride; block_sums
+// needs nlev (scan_blocks(n) + 1) words.
+hipError_t launch_scan(const uint32_t* counts, uint32_t n, int level0, int nlev,
+                       uint32_t* block_sums, uint32_t* out, size_t out_stride, hipStream_t s);
 hipError_t launch_stats(const uint32_t* counts, uint32_t K, msm_stats* st, hipStream_t s);
 hipError_t launch_bucket_init(const uint32_t* counts, const uint32_t* offsets, uint32_t K,
                               const uint32_t* sorted_idx, const g1a* points, xyzz_st* bsum,

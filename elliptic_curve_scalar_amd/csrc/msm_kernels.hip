@@ -192,22 +192,27 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* l
   return incl - v;
 }
 
+// The scans run over several levels at once: blockIdx.y selects level level0 + y,
+// whose block sums sit at block_sums + y (nb + 1) and whose output at out + y stride.
 __global__ void __launch_bounds__(256) k_scan_reduce(const uint32_t* __restrict__ counts, uint32_t n,
-                                                     int level, uint32_t* __restrict__ block_sums) {
+                                                     int level0, uint32_t* __restrict__ block_sums,
+                                                     uint32_t nb) {
   __shared__ uint32_t lds[256];
+  const int level = level0 + (int)blockIdx.y;
   uint32_t base = blockIdx.x * SCAN_TILE + threadIdx.x * SCAN_ITEMS;
   uint32_t sum = 0;
 #pragma unroll
   for (int e = 0; e < SCAN_ITEMS; e++) sum += scan_value(counts, base + e, n, level);
   uint32_t total;
   block_exclusive_scan(sum, lds, &total);
-  if (threadIdx.x == 0) block_sums[blockIdx.x] = total;
+  if (threadIdx.x == 0) block_sums[(size_t)blockIdx.y * (nb + 1) + blockIdx.x] = total;
 }
 
-// One block of 256 threads scans up to 256 * SCAN_TOP_ITEMS block sums in place
-// (exclusive) and stores the grand total at block_sums[nb].
-__global__ void __launch_bounds__(256) k_scan_top(uint32_t* block_sums, uint32_t nb) {
+// One block of 256 threads per level scans up to 256 * SCAN_TOP_ITEMS block sums in
+// place (exclusive) and stores the grand total at block_sums[nb].
+__global__ void __launch_bounds__(256) k_scan_top(uint32_t* block_sums_all, uint32_t nb) {
   __shared__ uint32_t lds[256];
+  uint32_t* block_sums = block_sums_all + (size_t)blockIdx.x * (nb + 1);
   uint32_t base = threadIdx.x * SCAN_TOP_ITEMS;
   uint32_t v[SCAN_TOP_ITEMS];
   uint32_t sum = 0;
@@ -227,10 +232,13 @@ __global__ void __launch_bounds__(256) k_scan_top(uint32_t* block_sums, uint32_t
 }
 
 __global__ void __launch_bounds__(256) k_scan_down(const uint32_t* __restrict__ counts, uint32_t n,
-                                                   int level, const uint32_t* __restrict__ block_sums,
-                                                   uint32_t nb, uint32_t* __restrict__ out,
-                                                   uint32_t* __restrict__ out2) {
+                                                   int level0, const uint32_t* __restrict__ block_sums_all,
+                                                   uint32_t nb, uint32_t* __restrict__ out_all,
+                                                   size_t out_stride) {
   __shared__ uint32_t lds[256];
+  const int level = level0 + (int)blockIdx.y;
+  const uint32_t* block_sums = block_sums_all + (size_t)blockIdx.y * (nb + 1);
+  uint32_t* out = out_all + (size_t)blockIdx.y * out_stride;
   uint32_t base = blockIdx.x * SCAN_TILE + threadIdx.x * SCAN_ITEMS;
   uint32_t v[SCAN_ITEMS];
   uint32_t sum = 0;
@@ -243,10 +251,7 @@ __global__ void __launch_bounds__(256) k_scan_down(const uint32_t* __restrict__ 
   uint32_t run = block_exclusive_scan(sum, lds, &total) + block_sums[blockIdx.x];
 #pragma unroll
   for (int e = 0; e < SCAN_ITEMS; e++) {
-    if (base + e < n) {
-      out[base + e] = run;
-      if (out2) out2[base + e] = run;
-    }
+    if (base + e < n) out[base + e] = run;
     run += v[e];
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) out[n] = block_sums[nb];
@@ -792,13 +797,13 @@ hipError_t launch_scatter(const uint32_t* halfs, uint32_t m, uint32_t c, uint32_
   return hipGetLastError();
 }
 
-hipError_t launch_scan(const uint32_t* counts, uint32_t n, int level, uint32_t* block_sums,
-                       uint32_t* out, uint32_t* out2, hipStream_t s) {
-  uint32_t nb = (n + SCAN_TILE - 1) / SCAN_TILE;
-  if (nb == 0) nb = 1;
-  k_scan_reduce<<<nb, 256, 0, s>>>(counts, n, level, block_sums);
-  k_scan_top<<<1, 256, 0, s>>>(block_sums, nb);
-  k_scan_down<<<nb, 256, 0, s>>>(counts, n, level, block_sums, nb, out, out2);
+hipError_t launch_scan(const uint32_t* counts, uint32_t n, int level0, int nlev,
+                       uint32_t* block_sums, uint32_t* out, size_t out_stride, hipStream_t s) {
+  uint32_t nb = scan_blocks(n);
+  if (nlev < 1) return hipSuccess;
+  k_scan_reduce<<<dim3(nb, nlev), 256, 0, s>>>(counts, n, level0, block_sums, nb);
+  k_scan_top<<<nlev, 256, 0, s>>>(block_sums, nb);
+  k_scan_down<<<dim3(nb, nlev), 256, 0, s>>>(counts, n, level0, block_sums, nb, out, out_stride);
   return hipGetLastError();
 }
 
