@@ -12,8 +12,8 @@
 //   backward: for s = S-1 .. 0:  1/d_s = inv * pref_{s-1} (inv itself for s = 0),
 //             then inv = inv * d_s; lambda = numerator_s / d_s; finish the add.
 //
-// Slot state lives in VGPRs: pref_s (8 words per slot) and the operands' element
-// indices; operands are re-read in the backward pass instead of being held.
+// Slot state is pref_s (8 words per slot) and the operands' element indices;
+// operands are re-read in the backward pass instead of being held.
 //
 // Special cases (the pages only report that x-collisions break an affine add,
 // PR #23736 "Correctness-harness fix"; the handling below is this library's):
@@ -60,8 +60,11 @@ __device__ __forceinline__ aff add_finish(const aff& A, const aff& B, int cs, co
   return r;
 }
 
-// Src supplies: aff a(int s), aff b(int s), void put(int s, const aff&).
-// Slots s >= cnt are idle (d = 1, nothing stored).
+// Src supplies: fp ax(int s), fp bx(int s) (x-coordinates only), aff a(int s),
+// aff b(int s) (whole points), void put(int s, const aff&). Slots s >= cnt are idle
+// (d = 1, nothing stored). The forward pass reads only the x-coordinates unless an x
+// is 0 or the two x agree (infinity, tangent, cancel), which then loads the whole
+// points.
 template <int S, class Src>
 __device__ __forceinline__ void batch_affine_add(Src& src, int cnt) {
   fp pref[S];
@@ -69,8 +72,14 @@ __device__ __forceinline__ void batch_affine_add(Src& src, int cnt) {
 #pragma unroll
   for (int s = 0; s < S; s++) {
     if (s < cnt) {
-      aff A = src.a(s), B = src.b(s);
-      fp d = add_denominator(A, B, add_case(A, B));
+      const fp xa = src.ax(s), xb = src.bx(s);
+      fp d;
+      if (!fp_eq(xa, xb) && !fp_is_zero(xa) && !fp_is_zero(xb)) {
+        d = fp_sub(xb, xa);  // chord, the common case
+      } else {
+        const aff A = src.a(s), B = src.b(s);
+        d = add_denominator(A, B, add_case(A, B));
+      }
       acc = (s == 0) ? d : fp_mul(acc, d);
     }
     pref[s] = acc;
@@ -79,9 +88,9 @@ __device__ __forceinline__ void batch_affine_add(Src& src, int cnt) {
 #pragma unroll
   for (int s = S - 1; s >= 0; s--) {
     if (s < cnt) {
-      fp inv_d = (s > 0) ? fp_mul(inv, pref[s - 1]) : inv;
-      aff A = src.a(s), B = src.b(s);
-      int cs = add_case(A, B);
+      const fp inv_d = (s > 0) ? fp_mul(inv, pref[s - 1]) : inv;
+      const aff A = src.a(s), B = src.b(s);
+      const int cs = add_case(A, B);
       inv = fp_mul(inv, add_denominator(A, B, cs));
       src.put(s, add_finish(A, B, cs, inv_d));
     }

@@ -397,8 +397,12 @@ struct LevelSrc {
   }
   __device__ __forceinline__ uint32_t elem(uint32_t pos) const { return idx ? idx[pos] : pos; }
   __device__ __forceinline__ aff get(uint32_t e) const { return idx ? load_entry(in, e) : aff_load(in + e); }
+  // the x-coordinate does not depend on the entry's sign bit
+  __device__ __forceinline__ fp getx(uint32_t e) const { return fp_load_x(in + (idx ? (e & 0x7fffffffu) : e)); }
   __device__ __forceinline__ aff a(int s) const { return get(ea[s]); }
   __device__ __forceinline__ aff b(int s) const { return get(eb[s]); }
+  __device__ __forceinline__ fp ax(int s) const { return getx(ea[s]); }
+  __device__ __forceinline__ fp bx(int s) const { return getx(eb[s]); }
   __device__ __forceinline__ void put(int s, const aff& r) const {
     uint32_t k = kb[s], m = mm[s];
     uint32_t cl = level_count(counts[k], level);
@@ -578,109 +582,23 @@ __global__ void __launch_bounds__(256) k_tree_sum(const xyzz_st* __restrict__ in
   if (threadIdx.x == 0) xyzz_store(out + (size_t)g * nblk + b, acc);
 }
 
-// ---- window combine: one wave, independent products spread over its lanes ----
+// ---- window combine ----------------------------------------------------------------
 // The combine is one long chain (c (W - 1) doublings), so its time is latency, not
 // throughput. Each XYZZ doubling has 9 products but only 3 dependent rounds, and an
-// addition 12 products in 4 rounds; lane i computes product i of a round and every
-// lane reads all results back with v_readlane, so a step costs 3 (or 4) product
-// latencies instead of 9 (or 12). All lanes hold the same point, so every branch is
-// uniform.
-
-__device__ __forceinline__ fp fp_from_lane(const fp& v, int src) {
-  fp r;
-#pragma unroll
-  for (int i = 0; i < 8; i++) r.v[i] = __builtin_amdgcn_readlane(v.v[i], src);
-  return r;
-}
-
-// Operand k for this lane (lanes beyond the list take the last entry).
-template <int N>
-__device__ __forceinline__ fp fp_pick(int lane, const fp (&opt)[N]) {
-  fp r = opt[N - 1];
-#pragma unroll
-  for (int k = N - 2; k >= 0; k--) {
-    const bool hit = (lane == k);
-#pragma unroll
-    for (int i = 0; i < 8; i++) r.v[i] = hit ? opt[k].v[i] : r.v[i];
-  }
-  return r;
-}
-
-__device__ __forceinline__ xyzz wave_dbl(const xyzz& p, int lane) {
-  const fp U = fp_dbl(p.Y);
-  fp r;
-  {  // V = U^2, XX = X^2
-    const fp a[2] = {U, p.X};
-    const fp x = fp_pick(lane, a);
-    r = fp_mul(x, x);
-  }
-  const fp V = fp_from_lane(r, 0), XX = fp_from_lane(r, 1);
-  const fp M = fp_add(fp_dbl(XX), XX);
-  {  // W = U V, S = X V, MM = M^2, ZZ3 = V ZZ
-    const fp a[4] = {U, p.X, M, V}, b[4] = {V, V, M, p.ZZ};
-    r = fp_mul(fp_pick(lane, a), fp_pick(lane, b));
-  }
-  const fp W = fp_from_lane(r, 0), S = fp_from_lane(r, 1), MM = fp_from_lane(r, 2);
-  xyzz q;
-  q.ZZ = fp_from_lane(r, 3);
-  q.X = fp_sub(fp_sub(MM, S), S);
-  {  // ZZZ3 = W ZZZ, WY = W Y, T = M (S - X3)
-    const fp a[3] = {W, W, M}, b[3] = {p.ZZZ, p.Y, fp_sub(S, q.X)};
-    r = fp_mul(fp_pick(lane, a), fp_pick(lane, b));
-  }
-  q.ZZZ = fp_from_lane(r, 0);
-  q.Y = fp_sub(fp_from_lane(r, 2), fp_from_lane(r, 1));
-  return q;
-}
-
-__device__ __forceinline__ xyzz wave_add(const xyzz& p, const xyzz& q, int lane) {
-  if (xyzz_is_inf(q)) return p;
-  if (xyzz_is_inf(p)) return q;
-  fp r;
-  {  // U1, U2, S1, S2, ZZ1 ZZ2, ZZZ1 ZZZ2
-    const fp a[6] = {p.X, q.X, p.Y, q.Y, p.ZZ, p.ZZZ}, b[6] = {q.ZZ, p.ZZ, q.ZZZ, p.ZZZ, q.ZZ, q.ZZZ};
-    r = fp_mul(fp_pick(lane, a), fp_pick(lane, b));
-  }
-  const fp U1 = fp_from_lane(r, 0), U2 = fp_from_lane(r, 1), S1 = fp_from_lane(r, 2);
-  const fp S2 = fp_from_lane(r, 3), ZZ12 = fp_from_lane(r, 4), ZZZ12 = fp_from_lane(r, 5);
-  const fp P = fp_sub(U2, U1), R = fp_sub(S2, S1);
-  if (fp_is_zero(P)) {
-    if (fp_is_zero(R)) return wave_dbl(p, lane);
-    return xyzz_inf();
-  }
-  {  // PP = P^2, RR = R^2
-    const fp a[2] = {P, R};
-    const fp x = fp_pick(lane, a);
-    r = fp_mul(x, x);
-  }
-  const fp PP = fp_from_lane(r, 0), RR = fp_from_lane(r, 1);
-  {  // PPP = P PP, Q = U1 PP, ZZ3 = ZZ12 PP
-    const fp a[3] = {P, U1, ZZ12};
-    r = fp_mul(fp_pick(lane, a), PP);
-  }
-  const fp PPP = fp_from_lane(r, 0), Q = fp_from_lane(r, 1);
-  xyzz o;
-  o.ZZ = fp_from_lane(r, 2);
-  o.X = fp_sub(fp_sub(fp_sub(RR, PPP), Q), Q);
-  {  // ZZZ3 = ZZZ12 PPP, S1 PPP, R (Q - X3)
-    const fp a[3] = {ZZZ12, S1, R}, b[3] = {PPP, PPP, fp_sub(Q, o.X)};
-    r = fp_mul(fp_pick(lane, a), fp_pick(lane, b));
-  }
-  o.ZZZ = fp_from_lane(r, 0);
-  o.Y = fp_sub(fp_from_lane(r, 2), fp_from_lane(r, 1));
-  return o;
-}
+// addition 14 products in 4 rounds; the four lanes of a quad split each round
+// (quad.hpp), so a step costs 3 (or 4) product latencies instead of 9 (or 14). Every
+// quad of the wave computes the same chain, so every branch is uniform.
 
 // Q = sum_j 2^(c j) W_j by Horner from the top window, then to affine. One wave.
 __global__ void __launch_bounds__(64) k_final(const xyzz_st* __restrict__ win, uint32_t nwin,
                                               uint32_t c, g1a* out) {
-  const int lane = threadIdx.x;
-  xyzz q = xyzz_load(win + nwin - 1);
+  const int lane = threadIdx.x, q = lane & 3;
+  xyzz acc = xyzz_load(win + nwin - 1);
   for (int j = (int)nwin - 2; j >= 0; j--) {
-    for (uint32_t b = 0; b < c; b++) q = wave_dbl(q, lane);
-    q = wave_add(q, xyzz_load(win + j), lane);
+    for (uint32_t b = 0; b < c; b++) acc = quad_dbl(acc, q);
+    acc = quad_add(acc, xyzz_load(win + j), q);
   }
-  const aff a = xyzz_to_aff(q);
+  const aff a = xyzz_to_aff(acc);
   if (lane == 0) aff_store(out, a);
 }
 
@@ -742,6 +660,8 @@ struct PairSrc {
   uint32_t base;
   __device__ __forceinline__ aff a(int s) const { return aff_load(a_ + base + s); }
   __device__ __forceinline__ aff b(int s) const { return aff_load(b_ + base + s); }
+  __device__ __forceinline__ fp ax(int s) const { return fp_load_x(a_ + base + s); }
+  __device__ __forceinline__ fp bx(int s) const { return fp_load_x(b_ + base + s); }
   __device__ __forceinline__ void put(int s, const aff& r) const { aff_store(out + base + s, r); }
 };
 

@@ -27,13 +27,19 @@ __device__ __forceinline__ fp quad_from(const fp& v) {
   return r;
 }
 
-// Operand for this lane: a0 on quad lane 0, a1 on 1, ...
+// Operand for this lane: a0 on quad lane 0, a1 on 1, ... Written as bit selects on the
+// two bits of q: a chain of q == k tests is turned by the compiler into a lookup table
+// in private memory (a scratch store and a lane-indexed load per word).
 __device__ __forceinline__ fp quad_pick(int q, const fp& a0, const fp& a1, const fp& a2,
                                         const fp& a3) {
+  const uint32_t m0 = 0u - ((uint32_t)q & 1u), m1 = 0u - (((uint32_t)q >> 1) & 1u);
   fp r;
 #pragma unroll
-  for (int i = 0; i < 8; i++)
-    r.v[i] = q == 0 ? a0.v[i] : q == 1 ? a1.v[i] : q == 2 ? a2.v[i] : a3.v[i];
+  for (int i = 0; i < 8; i++) {
+    const uint32_t lo = (a1.v[i] & m0) | (a0.v[i] & ~m0);
+    const uint32_t hi = (a3.v[i] & m0) | (a2.v[i] & ~m0);
+    r.v[i] = (hi & m1) | (lo & ~m1);
+  }
   return r;
 }
 
