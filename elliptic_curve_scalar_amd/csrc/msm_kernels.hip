@@ -53,19 +53,6 @@ __device__ __forceinline__ uint32_t window_digit(const sc256& s, uint32_t bit, u
   return (uint32_t)(v >> sh) & ((1u << c) - 1u);
 }
 
-// Any bit at or above `top` set?
-__device__ __forceinline__ bool above_bits(const sc256& s, uint32_t top) {
-  if (top >= 256) return false;
-  uint32_t acc = 0;
-#pragma unroll
-  for (uint32_t k = 0; k < 8; k++) {
-    uint32_t lo_bit = 32 * k;
-    uint32_t m = (top <= lo_bit) ? 0xffffffffu : (top >= lo_bit + 32 ? 0u : (0xffffffffu << (top - lo_bit)));
-    acc |= s.w[k] & m;
-  }
-  return acc != 0;
-}
-
 __global__ void k_fill_u32(uint32_t* p, size_t n, uint32_t v) {
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -125,25 +112,92 @@ __device__ __forceinline__ sc256 load_half(const uint32_t* halfs, uint32_t i, bo
   return r;
 }
 
+// Signed digits of one half-scalar for a fixed maximum window count: slot[j] = |d_j| - 1
+// and act[j] = (d_j != 0), the same recoding as for_each_signed_digit. Unrolled, so the
+// per-window memory operations that follow can all be in flight together.
+template <int MAXW>
+__device__ __forceinline__ void signed_digits(const sc256& s, uint32_t c, uint32_t nwin,
+                                              uint32_t (&slot)[MAXW], bool (&act)[MAXW],
+                                              bool (&neg)[MAXW]) {
+  const uint32_t half = 1u << (c - 1);
+  uint32_t carry = 0;
+#pragma unroll
+  for (int j = 0; j < MAXW; j++) {
+    const bool in = (uint32_t)j < nwin;
+    const uint32_t raw = (in ? window_digit(s, j * c, c) : 0u) + carry;
+    const bool ng = ((uint32_t)j + 1 < nwin) && raw > half;
+    carry = ng ? 1u : 0u;
+    const uint32_t mag = ng ? (1u << c) - raw : raw;
+    act[j] = in && mag != 0;
+    slot[j] = mag - 1;
+    neg[j] = ng;
+  }
+}
+
 // Counting pass of the counting sort. The atomic on a bucket's count also returns the
 // entry's rank among the bucket's entries; it is kept (rank[j m + i] for window j of
-// half-scalar i) so that the scatter needs no second round of atomics.
+// half-scalar i) so that the scatter needs no second round of atomics. MAXW > 0
+// unrolls over at most MAXW windows so that all atomics of a half-scalar are issued
+// before their results are waited for; MAXW = 0 loops over any window count.
+template <int MAXW>
 __global__ void __launch_bounds__(256) k_hist(const uint32_t* __restrict__ halfs, uint32_t m,
                                               uint32_t c, uint32_t nwin,
                                               uint32_t* __restrict__ counts,
                                               uint32_t* __restrict__ rank) {
   uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= m) return;
-  bool neg;
-  const sc256 s = load_half(halfs, i, neg);
+  bool sneg;
+  const sc256 s = load_half(halfs, i, sneg);
   const uint32_t sh = c - 1;
-  for_each_signed_digit(s, c, nwin, [&](uint32_t j, uint32_t slot, bool) {
-    rank[(size_t)j * m + i] = atomicAdd(&counts[(j << sh) | slot], 1u);
-  });
+  if constexpr (MAXW > 0) {
+    uint32_t slot[MAXW], r[MAXW], below[MAXW];
+    bool act[MAXW], neg[MAXW];
+    uint8_t grp[MAXW];
+    uint64_t m0[MAXW], m1[MAXW];
+    signed_digits<MAXW>(s, c, nwin, slot, act, neg);
+    // Skewed inputs can send a large share of all entries to one bucket, whose count
+    // would then take one serialized atomic per entry. Within the wavefront, two groups
+    // share one atomic each: the lanes on the window's |d| = 1 bucket (where the carry
+    // out of a small scalar's top window lands) and the lanes on the first remaining
+    // lane's bucket; every other lane takes its own. All atomics are issued before any
+    // result is used.
+#pragma unroll
+    for (int j = 0; j < MAXW; j++) {
+      const uint32_t addr = ((uint32_t)j << sh) | slot[j];
+      const bool g0 = act[j] && slot[j] == 0;
+      const bool rest = act[j] && !g0;
+      m0[j] = __ballot(g0);
+      const uint64_t mr = __ballot(rest);
+      uint32_t lead = 0xffffffffu;
+      if (mr) lead = __builtin_amdgcn_readlane(addr, (int)__builtin_ctzll(mr));
+      const bool g1 = rest && addr == lead;
+      m1[j] = __ballot(g1);
+      const uint64_t gm = g0 ? m0[j] : m1[j];
+      below[j] = __builtin_amdgcn_mbcnt_hi((uint32_t)(gm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)gm, 0u));
+      grp[j] = g0 ? 0 : (g1 ? 1 : 2);
+      r[j] = 0;
+      if (act[j] && (grp[j] == 2 || below[j] == 0))
+        r[j] = atomicAdd(&counts[addr], grp[j] == 2 ? 1u : (uint32_t)__popcll(gm));
+    }
+#pragma unroll
+    for (int j = 0; j < MAXW; j++) {
+      uint32_t b0 = 0, b1 = 0;
+      if (m0[j]) b0 = __builtin_amdgcn_readlane(r[j], (int)__builtin_ctzll(m0[j]));
+      if (m1[j]) b1 = __builtin_amdgcn_readlane(r[j], (int)__builtin_ctzll(m1[j]));
+      if (grp[j] == 0) r[j] = b0 + below[j];
+      if (grp[j] == 1) r[j] = b1 + below[j];
+      if (act[j]) rank[(size_t)j * m + i] = r[j];
+    }
+  } else {
+    for_each_signed_digit(s, c, nwin, [&](uint32_t j, uint32_t sl, bool) {
+      rank[(size_t)j * m + i] = atomicAdd(&counts[(j << sh) | sl], 1u);
+    });
+  }
 }
 
 // Bucket lists hold point indices with the sign of (digit x half-scalar) in bit 31,
 // written at the bucket's offset plus the rank the counting pass handed out.
+template <int MAXW>
 __global__ void __launch_bounds__(256) k_scatter(const uint32_t* __restrict__ halfs, uint32_t m,
                                                  uint32_t c, uint32_t nwin,
                                                  const uint32_t* __restrict__ offsets,
@@ -154,10 +208,22 @@ __global__ void __launch_bounds__(256) k_scatter(const uint32_t* __restrict__ ha
   bool sneg;
   const sc256 s = load_half(halfs, i, sneg);
   const uint32_t sh = c - 1;
-  for_each_signed_digit(s, c, nwin, [&](uint32_t j, uint32_t slot, bool neg) {
-    const uint32_t pos = offsets[(j << sh) | slot] + rank[(size_t)j * m + i];
-    sorted_idx[pos] = i | ((neg != sneg) ? 0x80000000u : 0u);
-  });
+  if constexpr (MAXW > 0) {
+    uint32_t slot[MAXW], pos[MAXW];
+    bool act[MAXW], neg[MAXW];
+    signed_digits<MAXW>(s, c, nwin, slot, act, neg);
+#pragma unroll
+    for (int j = 0; j < MAXW; j++)
+      if (act[j]) pos[j] = offsets[((uint32_t)j << sh) | slot[j]] + rank[(size_t)j * m + i];
+#pragma unroll
+    for (int j = 0; j < MAXW; j++)
+      if (act[j]) sorted_idx[pos[j]] = i | ((neg[j] != sneg) ? 0x80000000u : 0u);
+  } else {
+    for_each_signed_digit(s, c, nwin, [&](uint32_t j, uint32_t sl, bool ng) {
+      const uint32_t pos = offsets[(j << sh) | sl] + rank[(size_t)j * m + i];
+      sorted_idx[pos] = i | ((ng != sneg) ? 0x80000000u : 0u);
+    });
+  }
 }
 
 // ------------------------------------------------------------------ scan
@@ -452,7 +518,7 @@ __global__ void __launch_bounds__(256) k_level(const g1a* __restrict__ in,
 // inversion's. Inputs are affine (IN_AFF, the output of a batched-affine level, or
 // the points themselves through sorted_idx at level 0) or XYZZ; outputs are XYZZ.
 template <bool IN_AFF>
-__global__ void __launch_bounds__(128) k_level_xyzz(const void* __restrict__ in_,
+__global__ void __launch_bounds__(128, 3) k_level_xyzz(const void* __restrict__ in_,
                                                     const uint32_t* __restrict__ idx,
                                                     xyzz_st* __restrict__ out, xyzz_st* bsum,
                                                     const uint32_t* __restrict__ counts,
@@ -706,14 +772,20 @@ hipError_t launch_glv_prep(const g1a* points, const uint32_t* scalars, uint32_t 
 
 hipError_t launch_hist(const uint32_t* halfs, uint32_t m, uint32_t c, uint32_t nwin,
                        uint32_t* counts, uint32_t* rank, hipStream_t s) {
-  k_hist<<<grid_for(m, 256), 256, 0, s>>>(halfs, m, c, nwin, counts, rank);
+  if (nwin <= 16)
+    k_hist<16><<<grid_for(m, 256), 256, 0, s>>>(halfs, m, c, nwin, counts, rank);
+  else
+    k_hist<0><<<grid_for(m, 256), 256, 0, s>>>(halfs, m, c, nwin, counts, rank);
   return hipGetLastError();
 }
 
 hipError_t launch_scatter(const uint32_t* halfs, uint32_t m, uint32_t c, uint32_t nwin,
                           const uint32_t* offsets, const uint32_t* rank, uint32_t* sorted_idx,
                           hipStream_t s) {
-  k_scatter<<<grid_for(m, 256), 256, 0, s>>>(halfs, m, c, nwin, offsets, rank, sorted_idx);
+  if (nwin <= 16)
+    k_scatter<16><<<grid_for(m, 256), 256, 0, s>>>(halfs, m, c, nwin, offsets, rank, sorted_idx);
+  else
+    k_scatter<0><<<grid_for(m, 256), 256, 0, s>>>(halfs, m, c, nwin, offsets, rank, sorted_idx);
   return hipGetLastError();
 }
 
