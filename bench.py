@@ -55,18 +55,20 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, S: int, affine_levels: int, src: str):
-    """HBM bytes per launch of the batched-affine kernel from the committed counter
-    summary (rocprofv3 FETCH_SIZE and WRITE_SIZE, scaled by a copy of known size), or
-    None when no entry matches this workload, S, schedule and kernel source."""
-    path = os.path.join(ROOT, "profiles", "k_level_hbm_traffic.md")
+def counter_record(kind: str, workload: str, S: int, affine_levels: int, src: str):
+    """A hardware-counter figure for the batched-affine kernel from the committed
+    summaries under profiles/: kind "traffic" (HBM bytes per launch from rocprofv3
+    FETCH_SIZE and WRITE_SIZE, scaled by a copy of known size) or "valu" (int-VALU
+    issue %). None when no entry matches this workload, S, schedule and kernel source."""
+    name = {"traffic": "k_level_hbm_traffic.md", "valu": "k_level_valu_counters.md"}[kind]
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         for line in fh:
-            if not line.startswith("traffic: "):
+            if not line.startswith(kind + ": "):
                 continue
-            rec = json.loads(line[len("traffic: "):])
+            rec = json.loads(line[len(kind) + 2:])
             if (rec["workload"], rec["S"], rec["affine_levels"], rec["src"]) == (
                     workload, S, affine_levels, src):
                 return rec
@@ -149,7 +151,9 @@ def main() -> int:
     level_s = tm["level_kernel_ms"] * 1e-3
     achieved = mads / level_s if level_s > 0 else 0.0
     al = args.affine_levels if args.affine_levels is not None else 1
-    tr = measured_traffic(args.workload, S, al, kernel_source_hash())
+    src = kernel_source_hash()
+    tr = counter_record("traffic", args.workload, S, al, src)
+    vu = counter_record("valu", args.workload, S, al, src)
     roofline = {
         "bound": "alu",
         "kernel": f"k_level<{S}> (pair-tree batched-affine accumulate)",
@@ -160,6 +164,7 @@ def main() -> int:
         "frac": achieved / PEAK_MAD_PER_S,
         "traffic": tr["bytes_per_launch"] if tr else None,
         "traffic_unit": "bytes per launch (HBM, rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
+        "int_valu_pct": vu["int_valu_pct"] if vu else None,
         "launches_per_step": tm["level_launches"] / runs,
         "avg_launch_ms": tm["level_kernel_ms"] / launches,
         "algorithmic_ops_per_launch": mads / launches,
