@@ -18,16 +18,17 @@
 // u, v, where the division by 2^30 is exact modular division: add the multiple of p
 // that clears the low 30 bits, shift, then bring the result from (-p, 2p) into
 // [0, p). Every lane runs the same fixed number of batches, so a wavefront never
-// diverges; a lane whose b has not reached 1 (y = 0, or a sequence the batch count
-// does not cover, which tests over many inputs do not produce) takes Fermat's
-// inverse instead, so the result is exact for every input.
+// diverges. The exact algorithm needs at most 507 steps; random inputs need far fewer
+// (of 40 million sampled, none needed more than 14 batches of 30), so 15 batches are
+// run, and a lane whose b has not reached 1 (y = 0, or an input the batches do not
+// cover) takes Fermat's inverse instead: the result is exact for every input.
 #pragma once
 #include "fp.hpp"
 
 namespace msmk {
 
 #define BG_STEPS 30        // steps per batch
-#define BG_BATCHES 18      // batches: 540 steps
+#define BG_BATCHES 15      // batches: 450 steps
 #define BG_NPINV30 0x24866389u  // -p^-1 mod 2^30
 
 __device__ __forceinline__ uint32_t bg_p(int i) {
