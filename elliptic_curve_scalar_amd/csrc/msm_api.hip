@@ -117,8 +117,8 @@ struct msm_ctx {
   void* ws = nullptr;
   size_t ws_bytes = 0;
   msm_stats* host_stats = nullptr;  // pinned
-  // phase timing
-  bool timing = false;
+  // phase timing: 0 off, 1 the batched-affine level kernels only, 2 every phase
+  int timing = 0;
   std::vector<hipEvent_t> events;
   size_t ev_used = 0;
   std::vector<Span> spans;
@@ -145,11 +145,13 @@ struct PhaseMark {
   hipStream_t st;
   int phase;
   size_t e0 = SIZE_MAX;
+  // level 1 brackets only the batched-affine level kernels, level 2 every phase
+  bool on() const { return ctx->timing >= 2 || (ctx->timing == 1 && phase == PH_LEVEL); }
   PhaseMark(msm_ctx* c, hipStream_t s, int ph) : ctx(c), st(s), phase(ph) {
-    if (ctx->timing) e0 = mark(ctx, st);
+    if (on()) e0 = mark(ctx, st);
   }
   void end() {
-    if (ctx->timing && e0 != SIZE_MAX) {
+    if (on() && e0 != SIZE_MAX) {
       size_t e1 = mark(ctx, st);
       if (e1 != SIZE_MAX) ctx->spans.push_back({phase, e0, e1});
     }
@@ -322,7 +324,8 @@ int msm_ctx_set_affine_levels(msm_ctx* ctx, int levels) {
 
 int msm_ctx_set_timing(msm_ctx* ctx, int enable) {
   if (!ctx) return fail(MSM_ERR_ARG, "ctx is NULL%s");
-  ctx->timing = enable != 0;
+  if (enable < 0 || enable > 2) return fail(MSM_ERR_ARG, "timing level must be 0, 1 or 2%s");
+  ctx->timing = enable;
   return MSM_OK;
 }
 

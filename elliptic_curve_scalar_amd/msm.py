@@ -127,8 +127,10 @@ class Context:
         """Leading pair-tree levels done with batched affine adds (-1: all)."""
         _check(lib().msm_ctx_set_affine_levels(self._h, int(levels)))
 
-    def set_timing(self, enable: bool = True):
-        _check(lib().msm_ctx_set_timing(self._h, int(bool(enable))))
+    def set_timing(self, level: int = 2):
+        """0 off, 1 the batched-affine level kernels only, 2 every phase (True = 2)."""
+        level = 2 if level is True else 0 if level is False else int(level)
+        _check(lib().msm_ctx_set_timing(self._h, level))
 
     def timing_read(self) -> dict:
         """Per-phase HIP-event times summed since the last read (waits for them)."""

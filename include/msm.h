@@ -131,12 +131,15 @@ int msm_g1_from_scalars(const uint32_t* d_k, size_t n, msm_g1_affine* d_out, voi
 int msm_ctx_set_affine_levels(msm_ctx* ctx, int levels);
 
 /*
- * Phase timing. When enabled on a context, msm_run records HIP events on its stream
- * around each phase: sort (count, scan, scatter), accumulate (pair-tree levels, with
- * every level kernel launch bracketed on its own), reduce (running sums) and final
- * (window combine). msm_ctx_timing_read waits for the events recorded since the last
- * read, sums them into *out and resets. Events are reused; enabling costs a few
- * microseconds per call. Returns MSM_ERR_ARG for NULL arguments.
+ * Phase timing. msm_ctx_set_timing(ctx, level) makes msm_run record HIP events on its
+ * stream: level 1 brackets only the batched-affine level-kernel launches (what a
+ * roofline of that kernel needs, at the least cost to the rest of the pipeline); level
+ * 2 also brackets each phase: sort (count, scan, scatter), accumulate (bucket init and
+ * all pair-tree levels, each XYZZ level kernel on its own), reduce (running sums) and
+ * final (window combine); level 0 turns timing off. Each event pair costs the stream
+ * a few microseconds. msm_ctx_timing_read waits for the events recorded since the
+ * last read, sums them into *out and resets. Returns MSM_ERR_ARG for NULL arguments
+ * or a level outside 0 .. 2.
  */
 typedef struct msm_timing {
   double sort_ms;          /* decompose, histogram, scans, scatter (incl. the read-back) */

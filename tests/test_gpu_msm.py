@@ -195,3 +195,28 @@ def test_full_range_scalars():
     for c, S in ((1, 4), (8, 8), (13, 8), (16, 32)):
         say("full-range scalars c", c, "S", S)
         assert np.array_equal(_gpu_msm(pts, sc, c, S), want), (c, S)
+
+
+def test_timing_levels():
+    """Level 1 times only the batched-affine kernels, level 2 every phase, 0 nothing;
+    the result does not depend on the level."""
+    M = _msm()
+    w = wl.generate("n65536_c13", n=4000)
+    pts = oracle.g1_from_scalars(w["dlogs"])
+    want = oracle.msm_pippenger(pts, w["scalars"], 13)
+    ctx = M.Context(0)
+    try:
+        for level in (0, 1, 2):
+            say("timing level", level)
+            ctx.set_timing(level)
+            got = to_host(ctx.run(to_dev(pts), to_dev(w["scalars"]), 13, 8))
+            assert np.array_equal(got, want)
+            tm = ctx.timing_read()
+            assert tm["runs"] == (1 if level else 0)
+            assert (tm["level_kernel_ms"] > 0) == (level >= 1)
+            assert (tm["sort_ms"] > 0) == (level == 2)
+            assert (tm["final_ms"] > 0) == (level == 2)
+        with pytest.raises(M.MsmError):
+            ctx.set_timing(3)
+    finally:
+        ctx.close()
