@@ -117,6 +117,7 @@ struct msm_ctx {
   void* ws = nullptr;
   size_t ws_bytes = 0;
   msm_stats* host_stats = nullptr;  // pinned
+  hipEvent_t plan_ready = nullptr;   // the plan's copy to host_stats has completed
   // phase timing: 0 off, 1 the batched-affine level kernels only, 2 every phase
   int timing = 0;
   std::vector<hipEvent_t> events;
@@ -188,6 +189,11 @@ int msm_ctx_create(int device, msm_ctx** out) {
     delete ctx;
     return fail(MSM_ERR_OOM, "pinned host allocation failed%s");
   }
+  if (hipEventCreateWithFlags(&ctx->plan_ready, hipEventDisableTiming) != hipSuccess) {
+    (void)hipHostFree(ctx->host_stats);
+    delete ctx;
+    return fail(MSM_ERR_HIP, "event creation failed%s");
+  }
   *out = ctx;
   return MSM_OK;
 }
@@ -196,6 +202,7 @@ void msm_ctx_destroy(msm_ctx* ctx) {
   if (!ctx) return;
   (void)hipSetDevice(ctx->device);
   for (hipEvent_t e : ctx->events) (void)hipEventDestroy(e);
+  if (ctx->plan_ready) (void)hipEventDestroy(ctx->plan_ready);
   if (ctx->ws) (void)hipFree(ctx->ws);
   if (ctx->host_stats) (void)hipHostFree(ctx->host_stats);
   delete ctx;
@@ -251,29 +258,38 @@ int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scala
   const g1a* pts = pts2;  // 2n points: P_i and phi(P_i)
   uint32_t n32 = (uint32_t)n, m32 = 2 * (uint32_t)n, c32 = (uint32_t)c;
 
-  // decompose + count, offsets, plan, scatter
+  // Levels the plan can require: a bucket holds at most one entry per half-scalar.
+  int level_bound = 0;
+  while (level_bound < MAX_LEVELS && ((uint64_t)1 << level_bound) < (uint64_t)m32) level_bound++;
+
+  // decompose + count, offsets, plan; the plan is copied to the host as soon as the
+  // counts are known, and the scatter, bucket init and the pair offsets of every level
+  // the plan can require are queued behind it, so the GPU keeps working while the host
+  // waits for the plan
   PhaseMark ph_sort(ctx, st, PH_SORT);
   HIP_TRY(launch_fill((uint32_t*)stats, sizeof(msm_stats) / 4, 0, st));
   HIP_TRY(launch_fill(counts, L.K, 0, st));
   HIP_TRY(launch_glv_prep((const g1a*)d_points, d_scalars, n32, pts2, halfs, stats, st));
   HIP_TRY(launch_hist(halfs, m32, c32, L.nwin, counts, rank, st));
-  HIP_TRY(launch_scan(counts, L.K, -1, 1, block_sums, offsets, L.K + 1, st));
+  HIP_TRY(launch_scan(counts, L.K, -1, 1, block_sums, offsets, L.K + 1, nullptr, st));
   HIP_TRY(launch_stats(counts, L.K, stats, st));
-  HIP_TRY(launch_scatter(halfs, m32, c32, L.nwin, offsets, rank, sorted_idx, st));
   HIP_TRY(hipMemcpyAsync(ctx->host_stats, stats, sizeof(msm_stats), hipMemcpyDeviceToHost, st));
+  HIP_TRY(hipEventRecord(ctx->plan_ready, st));
+  HIP_TRY(launch_scatter(halfs, m32, c32, L.nwin, offsets, rank, sorted_idx, st));
   ph_sort.end();
-  HIP_TRY(hipStreamSynchronize(st));
+  PhaseMark ph_acc(ctx, st, PH_ACCUM);
+  HIP_TRY(launch_bucket_init(counts, offsets, L.K, sorted_idx, pts, bsum, st));
+  // pair offsets of every level at once: level l at poff_all + l (K + 1)
+  uint32_t* const poff_all = poff;
+  HIP_TRY(launch_scan(counts, L.K, 0, level_bound, block_sums, poff_all, (size_t)L.K + 1,
+                      &stats->max_count, st));
+  HIP_TRY(hipEventSynchronize(ctx->plan_ready));
   const msm_stats hs = *ctx->host_stats;
   if (hs.range_flag) return fail(MSM_ERR_RANGE, "GLV half-scalar out of bound (internal error)%s");
 
   // accumulate: pair-tree levels until every bucket holds one point
-  PhaseMark ph_acc(ctx, st, PH_ACCUM);
-  HIP_TRY(launch_bucket_init(counts, offsets, L.K, sorted_idx, pts, bsum, st));
   int levels = 0;
-  while (levels < MAX_LEVELS && ((uint64_t)1 << levels) < hs.max_count) levels++;
-  // pair offsets of every level at once: level l at poff_all + l (K + 1)
-  uint32_t* const poff_all = poff;
-  HIP_TRY(launch_scan(counts, L.K, 0, levels, block_sums, poff_all, (size_t)L.K + 1, st));
+  while (levels < level_bound && ((uint64_t)1 << levels) < hs.max_count) levels++;
   for (int l = 0; l < levels; l++) {
     uint32_t np = hs.pairs[l];
     if (np == 0) continue;

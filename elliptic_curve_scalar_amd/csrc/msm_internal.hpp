@@ -47,9 +47,11 @@ inline uint32_t scan_blocks(uint32_t n) {
 // Exclusive scans of the per-bucket values of levels level0 .. level0 + nlev - 1 (level
 // -1: the counts themselves; level l >= 0: the pair adds at pair-tree level l). Level
 // level0 + y writes n + 1 values (the total last) at out + y out_stride; block_sums
-// needs nlev (scan_blocks(n) + 1) words.
+// needs nlev (scan_blocks(n) + 1) words. With max_count (device, may be NULL), levels
+// l >= 0 that a largest bucket of *max_count entries does not need are skipped.
 hipError_t launch_scan(const uint32_t* counts, uint32_t n, int level0, int nlev,
-                       uint32_t* block_sums, uint32_t* out, size_t out_stride, hipStream_t s);
+                       uint32_t* block_sums, uint32_t* out, size_t out_stride,
+                       const uint32_t* max_count, hipStream_t s);
 hipError_t launch_stats(const uint32_t* counts, uint32_t K, msm_stats* st, hipStream_t s);
 hipError_t launch_bucket_init(const uint32_t* counts, const uint32_t* offsets, uint32_t K,
                               const uint32_t* sorted_idx, const g1a* points, xyzz_st* bsum,

@@ -258,13 +258,19 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* l
   return incl - v;
 }
 
+// Pair-tree levels needed for a largest bucket of max_count entries.
+__device__ __forceinline__ bool level_needed(int level, const uint32_t* max_count) {
+  return level < 0 || !max_count || ((uint64_t)1 << level) < *max_count;
+}
+
 // The scans run over several levels at once: blockIdx.y selects level level0 + y,
 // whose block sums sit at block_sums + y (nb + 1) and whose output at out + y stride.
 __global__ void __launch_bounds__(256) k_scan_reduce(const uint32_t* __restrict__ counts, uint32_t n,
                                                      int level0, uint32_t* __restrict__ block_sums,
-                                                     uint32_t nb) {
+                                                     uint32_t nb, const uint32_t* max_count) {
   __shared__ uint32_t lds[256];
   const int level = level0 + (int)blockIdx.y;
+  if (!level_needed(level, max_count)) return;
   uint32_t base = blockIdx.x * SCAN_TILE + threadIdx.x * SCAN_ITEMS;
   uint32_t sum = 0;
 #pragma unroll
@@ -276,8 +282,10 @@ __global__ void __launch_bounds__(256) k_scan_reduce(const uint32_t* __restrict_
 
 // One block of 256 threads per level scans up to 256 * SCAN_TOP_ITEMS block sums in
 // place (exclusive) and stores the grand total at block_sums[nb].
-__global__ void __launch_bounds__(256) k_scan_top(uint32_t* block_sums_all, uint32_t nb) {
+__global__ void __launch_bounds__(256) k_scan_top(uint32_t* block_sums_all, uint32_t nb, int level0,
+                                                  const uint32_t* max_count) {
   __shared__ uint32_t lds[256];
+  if (!level_needed(level0 + (int)blockIdx.x, max_count)) return;
   uint32_t* block_sums = block_sums_all + (size_t)blockIdx.x * (nb + 1);
   uint32_t base = threadIdx.x * SCAN_TOP_ITEMS;
   uint32_t v[SCAN_TOP_ITEMS];
@@ -300,9 +308,10 @@ __global__ void __launch_bounds__(256) k_scan_top(uint32_t* block_sums_all, uint
 __global__ void __launch_bounds__(256) k_scan_down(const uint32_t* __restrict__ counts, uint32_t n,
                                                    int level0, const uint32_t* __restrict__ block_sums_all,
                                                    uint32_t nb, uint32_t* __restrict__ out_all,
-                                                   size_t out_stride) {
+                                                   size_t out_stride, const uint32_t* max_count) {
   __shared__ uint32_t lds[256];
   const int level = level0 + (int)blockIdx.y;
+  if (!level_needed(level, max_count)) return;
   const uint32_t* block_sums = block_sums_all + (size_t)blockIdx.y * (nb + 1);
   uint32_t* out = out_all + (size_t)blockIdx.y * out_stride;
   uint32_t base = blockIdx.x * SCAN_TILE + threadIdx.x * SCAN_ITEMS;
@@ -790,12 +799,14 @@ hipError_t launch_scatter(const uint32_t* halfs, uint32_t m, uint32_t c, uint32_
 }
 
 hipError_t launch_scan(const uint32_t* counts, uint32_t n, int level0, int nlev,
-                       uint32_t* block_sums, uint32_t* out, size_t out_stride, hipStream_t s) {
+                       uint32_t* block_sums, uint32_t* out, size_t out_stride,
+                       const uint32_t* max_count, hipStream_t s) {
   uint32_t nb = scan_blocks(n);
   if (nlev < 1) return hipSuccess;
-  k_scan_reduce<<<dim3(nb, nlev), 256, 0, s>>>(counts, n, level0, block_sums, nb);
-  k_scan_top<<<nlev, 256, 0, s>>>(block_sums, nb);
-  k_scan_down<<<dim3(nb, nlev), 256, 0, s>>>(counts, n, level0, block_sums, nb, out, out_stride);
+  k_scan_reduce<<<dim3(nb, nlev), 256, 0, s>>>(counts, n, level0, block_sums, nb, max_count);
+  k_scan_top<<<nlev, 256, 0, s>>>(block_sums, nb, level0, max_count);
+  k_scan_down<<<dim3(nb, nlev), 256, 0, s>>>(counts, n, level0, block_sums, nb, out, out_stride,
+                                              max_count);
   return hipGetLastError();
 }
 
