@@ -664,17 +664,33 @@ __global__ void __launch_bounds__(256) k_tree_sum(const xyzz_st* __restrict__ in
 // (quad.hpp), so a step costs 3 (or 4) product latencies instead of 9 (or 14). Every
 // quad of the wave computes the same chain, so every branch is uniform.
 
-// Q = sum_j 2^(c j) W_j by Horner from the top window, then to affine. One wave.
-__global__ void __launch_bounds__(64) k_final(const xyzz_st* __restrict__ win, uint32_t nwin,
-                                              uint32_t c, g1a* out) {
-  const int lane = threadIdx.x, q = lane & 3;
-  xyzz acc = xyzz_load(win + nwin - 1);
-  for (int j = (int)nwin - 2; j >= 0; j--) {
-    for (uint32_t b = 0; b < c; b++) acc = quad_dbl(acc, q);
-    acc = quad_add(acc, xyzz_load(win + j), q);
+// Q = sum_j 2^(c j) W_j, then to affine. Two wavefronts split the chain: wave 0 doubles
+// the top window's sum c (W - 1) times, with no addition on its chain, while wave 1
+// runs Horner over the lower windows (c (W - 2) doublings and W - 2 additions, a
+// shorter chain); one addition joins them. W >= 8 for every c <= 16.
+__global__ void __launch_bounds__(128) k_final(const xyzz_st* __restrict__ win, uint32_t nwin,
+                                               uint32_t c, g1a* out) {
+  __shared__ xyzz_st low;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane & 3;
+  xyzz acc;
+  if (wave == 0) {
+    acc = xyzz_load(win + nwin - 1);
+    const uint32_t nd = c * (nwin - 1);
+    for (uint32_t b = 0; b < nd; b++) acc = quad_dbl(acc, q);
+  } else {
+    acc = xyzz_load(win + nwin - 2);
+    for (int j = (int)nwin - 3; j >= 0; j--) {
+      for (uint32_t b = 0; b < c; b++) acc = quad_dbl(acc, q);
+      acc = quad_add(acc, xyzz_load(win + j), q);
+    }
+    if (lane == 0) xyzz_store(&low, acc);
   }
-  const aff a = xyzz_to_aff(acc);
-  if (lane == 0) aff_store(out, a);
+  __syncthreads();
+  if (wave == 0) {
+    acc = quad_add(acc, xyzz_load(&low), q);
+    const aff a = xyzz_to_aff(acc);
+    if (lane == 0) aff_store(out, a);
+  }
 }
 
 // ------------------------------------------------------------------ generator
@@ -876,7 +892,7 @@ hipError_t launch_reduce(const xyzz_st* bsum, uint32_t c, uint32_t nwin, uint32_
 }
 
 hipError_t launch_final(const xyzz_st* win, uint32_t nwin, uint32_t c, g1a* out, hipStream_t s) {
-  k_final<<<1, 64, 0, s>>>(win, nwin, c, out);
+  k_final<<<1, 128, 0, s>>>(win, nwin, c, out);
   return hipGetLastError();
 }
 
