@@ -92,14 +92,12 @@ __device__ __forceinline__ bool fp_eq(const fp& a, const fp& b) {
 
 // r = t - p if t >= p else t, for t < 2^256 given as 8 limbs.
 __device__ __forceinline__ fp fp_reduce_once(const fp& t) {
+  // 32-bit borrow chain (clang's subtract-with-borrow builtin, v_sub_co / v_subb_co):
+  // uint64_t arithmetic here compiles to 64-bit adds of widened operands
   fp d;
   uint32_t borrow = 0;
 #pragma unroll
-  for (int i = 0; i < 8; i++) {
-    uint64_t s = (uint64_t)t.v[i] - p_limb(i) - borrow;
-    d.v[i] = (uint32_t)s;
-    borrow = (uint32_t)(s >> 63);
-  }
+  for (int i = 0; i < 8; i++) d.v[i] = __builtin_subc(t.v[i], p_limb(i), borrow, &borrow);
   fp r;
 #pragma unroll
   for (int i = 0; i < 8; i++) r.v[i] = borrow ? t.v[i] : d.v[i];
@@ -110,11 +108,7 @@ __device__ __forceinline__ fp fp_add(const fp& a, const fp& b) {
   fp s;
   uint32_t carry = 0;
 #pragma unroll
-  for (int i = 0; i < 8; i++) {
-    uint64_t t = (uint64_t)a.v[i] + b.v[i] + carry;
-    s.v[i] = (uint32_t)t;
-    carry = (uint32_t)(t >> 32);
-  }
+  for (int i = 0; i < 8; i++) s.v[i] = __builtin_addc(a.v[i], b.v[i], carry, &carry);
   // a, b < p < 2^254: the sum is below 2^255, so no carry leaves limb 7.
   return fp_reduce_once(s);
 }
@@ -123,20 +117,12 @@ __device__ __forceinline__ fp fp_sub(const fp& a, const fp& b) {
   fp d;
   uint32_t borrow = 0;
 #pragma unroll
-  for (int i = 0; i < 8; i++) {
-    uint64_t t = (uint64_t)a.v[i] - b.v[i] - borrow;
-    d.v[i] = (uint32_t)t;
-    borrow = (uint32_t)(t >> 63);
-  }
+  for (int i = 0; i < 8; i++) d.v[i] = __builtin_subc(a.v[i], b.v[i], borrow, &borrow);
   // a < b: add p back (masked, branch-free)
-  uint32_t mask = 0u - borrow;
+  const uint32_t mask = 0u - borrow;
   uint32_t carry = 0;
 #pragma unroll
-  for (int i = 0; i < 8; i++) {
-    uint64_t t = (uint64_t)d.v[i] + (p_limb(i) & mask) + carry;
-    d.v[i] = (uint32_t)t;
-    carry = (uint32_t)(t >> 32);
-  }
+  for (int i = 0; i < 8; i++) d.v[i] = __builtin_addc(d.v[i], p_limb(i) & mask, carry, &carry);
   return d;
 }
 
