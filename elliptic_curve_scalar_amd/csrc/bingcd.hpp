@@ -132,11 +132,7 @@ __device__ __forceinline__ bool bg_lin(const uint32_t (&a)[8], const uint32_t (&
   const uint32_t m = neg ? 0xffffffffu : 0u;
   uint32_t c = neg ? 1u : 0u;
 #pragma unroll
-  for (int i = 0; i < 9; i++) {
-    const uint64_t s = (uint64_t)(t[i] ^ m) + c;
-    t[i] = (uint32_t)s;
-    c = (uint32_t)(s >> 32);
-  }
+  for (int i = 0; i < 9; i++) t[i] = __builtin_addc(t[i] ^ m, 0u, c, &c);
 #pragma unroll
   for (int i = 0; i < 8; i++) out[i] = (t[i] >> 30) | (t[i + 1] << 2);
   return neg;
@@ -168,12 +164,8 @@ __device__ __forceinline__ void bg_lin_mod(const uint32_t (&u)[8], const uint32_
   uint32_t cp = 0, bm = 0;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
-    const uint64_t s = (uint64_t)r[i] + bg_p(i) + cp;
-    rp[i] = (uint32_t)s;
-    cp = (uint32_t)(s >> 32);
-    const uint64_t d = (uint64_t)r[i] - bg_p(i) - bm;
-    rm[i] = (uint32_t)d;
-    bm = (uint32_t)(d >> 63);
+    rp[i] = __builtin_addc(r[i], bg_p(i), cp, &cp);
+    rm[i] = __builtin_subc(r[i], bg_p(i), bm, &bm);
   }
   const bool neg = (int32_t)r[8] < 0;
   const bool ge = !neg && (r[8] != 0 || bm == 0);
