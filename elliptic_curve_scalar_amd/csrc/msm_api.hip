@@ -44,10 +44,10 @@ uint32_t segment_length(int c, int nwin) {
 }
 
 struct Layout {
-  size_t stats, halfs, pts2, counts, offsets, rank, poff, block_sums, sorted_idx, aff_a, aff_b,
+  size_t stats, halfs, pts2, counts, offsets, rank, hist_blk, poff, block_sums, sorted_idx, aff_a, aff_b,
       xz_a, xz_b, bsum, seg, part, win;
   size_t total;
-  uint32_t K, nwin, seg_len, nseg;
+  uint32_t K, nwin, seg_len, nseg, chunk, nchunk;
   size_t E_max, half;
 };
 
@@ -71,6 +71,16 @@ Layout plan(size_t n, int c) {
   L.counts = take((size_t)L.K * 4);
   L.offsets = take(((size_t)L.K + 1) * 4);
   L.rank = take((size_t)L.nwin * 2 * n * 4);  // rank of each (window, half-scalar) entry
+  // counting-sort chunks: about 512 (chunk, window) blocks, chunks a multiple of 1024
+  {
+    const size_t m = 2 * n;
+    size_t ch = (m * L.nwin + 511) / 512;
+    ch = ch < 1024 ? 1024 : (ch + 1023) / 1024 * 1024;  // never 0 (n = 0 still plans)
+    L.chunk = (uint32_t)ch;
+    L.nchunk = (uint32_t)((m + ch - 1) / ch);
+    if (L.nchunk == 0) L.nchunk = 1;
+  }
+  L.hist_blk = take((size_t)L.nwin * L.nchunk * ((size_t)1 << (c - 1)) * 4);
   L.poff = take((size_t)MAX_LEVELS * ((size_t)L.K + 1) * 4);  // pair offsets of every level
   L.block_sums = take((size_t)MAX_LEVELS * (scan_blocks(L.K) + 1) * 4);
   L.sorted_idx = take(L.E_max * 4);
@@ -246,6 +256,7 @@ int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scala
   uint32_t* counts = (uint32_t*)(ws + L.counts);
   uint32_t* offsets = (uint32_t*)(ws + L.offsets);
   uint32_t* rank = (uint32_t*)(ws + L.rank);
+  uint32_t* hist_blk = (uint32_t*)(ws + L.hist_blk);
   uint32_t* poff = (uint32_t*)(ws + L.poff);
   uint32_t* block_sums = (uint32_t*)(ws + L.block_sums);
   uint32_t* sorted_idx = (uint32_t*)(ws + L.sorted_idx);
@@ -268,14 +279,14 @@ int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scala
   // waits for the plan
   PhaseMark ph_sort(ctx, st, PH_SORT);
   HIP_TRY(launch_fill((uint32_t*)stats, sizeof(msm_stats) / 4, 0, st));
-  HIP_TRY(launch_fill(counts, L.K, 0, st));
   HIP_TRY(launch_glv_prep((const g1a*)d_points, d_scalars, n32, pts2, halfs, stats, st));
-  HIP_TRY(launch_hist(halfs, m32, c32, L.nwin, counts, rank, st));
+  HIP_TRY(launch_hist(halfs, m32, c32, L.nwin, L.chunk, L.nchunk, hist_blk, counts, rank, st));
   HIP_TRY(launch_scan(counts, L.K, -1, 1, block_sums, offsets, L.K + 1, nullptr, st));
   HIP_TRY(launch_stats(counts, L.K, stats, st));
   HIP_TRY(hipMemcpyAsync(ctx->host_stats, stats, sizeof(msm_stats), hipMemcpyDeviceToHost, st));
   HIP_TRY(hipEventRecord(ctx->plan_ready, st));
-  HIP_TRY(launch_scatter(halfs, m32, c32, L.nwin, offsets, rank, sorted_idx, st));
+  HIP_TRY(launch_scatter(halfs, m32, c32, L.nwin, L.chunk, L.nchunk, offsets, hist_blk, rank,
+                         sorted_idx, st));
   ph_sort.end();
   PhaseMark ph_acc(ctx, st, PH_ACCUM);
   HIP_TRY(launch_bucket_init(counts, offsets, L.K, sorted_idx, pts, bsum, st));

@@ -34,10 +34,14 @@ struct xyzz_st {
 hipError_t launch_fill(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
 hipError_t launch_glv_prep(const g1a* points, const uint32_t* scalars, uint32_t n, g1a* pts2,
                            uint32_t* halfs, msm_stats* st, hipStream_t s);
+// Counting pass: per (chunk of half-scalars, window) LDS histograms into hist_blk
+// (nwin nchunk 2^(c-1) words), turned into per-chunk prefixes, and the bucket counts.
 hipError_t launch_hist(const uint32_t* halfs, uint32_t m, uint32_t c, uint32_t nwin,
-                       uint32_t* counts, uint32_t* rank, hipStream_t s);
+                       uint32_t chunk, uint32_t nchunk, uint32_t* hist_blk, uint32_t* counts,
+                       uint32_t* rank, hipStream_t s);
 hipError_t launch_scatter(const uint32_t* halfs, uint32_t m, uint32_t c, uint32_t nwin,
-                          const uint32_t* offsets, const uint32_t* rank, uint32_t* sorted_idx,
+                          uint32_t chunk, uint32_t nchunk, const uint32_t* offsets,
+                          const uint32_t* hist_blk, const uint32_t* rank, uint32_t* sorted_idx,
                           hipStream_t s);
 // Blocks of the tile scan over n values.
 inline uint32_t scan_blocks(uint32_t n) {

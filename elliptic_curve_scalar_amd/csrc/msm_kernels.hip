@@ -1,18 +1,23 @@
 // Device kernels of the BN254 G1 bucket MSM for gfx950, and their launchers.
 //
-// Pipeline (one stream; W = ceil(254 / c) windows, 2^c buckets per window, digit 0
-// dropped since it adds nothing):
-//   k_hist        scalar -> W window digits, per-(window, digit) counts (global atomics)
+// Pipeline (one stream; W = ceil(128 / c) windows of signed digits over the 2n GLV
+// half-scalars, 2^(c-1) buckets per window, digit 0 dropped since it adds nothing):
+//   k_glv_prep    scalar -> two half-scalars below 2^127; points [P, phi(P)]
+//   k_hist_tile   per (chunk of half-scalars, window): LDS histogram, rank per entry
+//   k_chunk_scan  per bucket: prefix over the chunks, bucket count
 //   k_scan_*      exclusive scan of the counts -> bucket offsets
 //   k_stats       largest bucket, number of pair adds at every pair-tree level
+//   -- the plan is copied to the host --
 //   k_scatter     point indices into per-bucket lists (sorted_idx)
-//   -- host reads the stats back (one sync) --
 //   k_bucket_init buckets of size 0 / 1 are final at once
-//   k_level<S>    pair-tree level l: pair (2m, 2m+1) of every bucket -> element m,
+//   k_scan_*      pair offsets of every pair-tree level
+//   -- the host reads the plan --
+//   k_level<S>    pair-tree level 0: pair (2m, 2m+1) of every bucket -> element m,
 //                 S pairs per lane with one inversion (batch_add.hpp)
+//   k_level_xyzz  deeper levels in XYZZ coordinates (quad-cooperative when small)
 //   k_rsum_seg    per window, segments of buckets: sum_b b * B_b by a running sum
 //   k_tree_sum    per window: two-pass tree over its segments -> W_j
-//   k_final       Q = sum_j 2^(c j) W_j by doubling (Horner), then affine
+//   k_final       Q = sum_j 2^(c j) W_j by doubling, then affine
 //
 // The method is aztec-packages PR #23738 / #23736 / #23520 ("bb/msm"); its WebGPU
 // kernels are prior art only: the level kernel takes S pairs per lane the way the
@@ -134,94 +139,100 @@ __device__ __forceinline__ void signed_digits(const sc256& s, uint32_t c, uint32
   }
 }
 
-// Counting pass of the counting sort. The atomic on a bucket's count also returns the
-// entry's rank among the bucket's entries; it is kept (rank[j m + i] for window j of
-// half-scalar i) so that the scatter needs no second round of atomics. MAXW > 0
-// unrolls over at most MAXW windows so that all atomics of a half-scalar are issued
-// before their results are waited for; MAXW = 0 loops over any window count.
-template <int MAXW>
-__global__ void __launch_bounds__(256) k_hist(const uint32_t* __restrict__ halfs, uint32_t m,
-                                              uint32_t c, uint32_t nwin,
-                                              uint32_t* __restrict__ counts,
-                                              uint32_t* __restrict__ rank) {
-  uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= m) return;
-  bool sneg;
-  const sc256 s = load_half(halfs, i, sneg);
-  const uint32_t sh = c - 1;
-  if constexpr (MAXW > 0) {
-    uint32_t slot[MAXW], r[MAXW], below[MAXW];
-    bool act[MAXW], neg[MAXW];
-    uint8_t grp[MAXW];
-    uint64_t m0[MAXW], m1[MAXW];
-    signed_digits<MAXW>(s, c, nwin, slot, act, neg);
-    // Skewed inputs can send a large share of all entries to one bucket, whose count
-    // would then take one serialized atomic per entry. Within the wavefront, two groups
-    // share one atomic each: the lanes on the window's |d| = 1 bucket (where the carry
-    // out of a small scalar's top window lands) and the lanes on the first remaining
-    // lane's bucket; every other lane takes its own. All atomics are issued before any
-    // result is used.
-#pragma unroll
-    for (int j = 0; j < MAXW; j++) {
-      const uint32_t addr = ((uint32_t)j << sh) | slot[j];
-      const bool g0 = act[j] && slot[j] == 0;
-      const bool rest = act[j] && !g0;
-      m0[j] = __ballot(g0);
-      const uint64_t mr = __ballot(rest);
-      uint32_t lead = 0xffffffffu;
-      if (mr) lead = __builtin_amdgcn_readlane(addr, (int)__builtin_ctzll(mr));
-      const bool g1 = rest && addr == lead;
-      m1[j] = __ballot(g1);
-      const uint64_t gm = g0 ? m0[j] : m1[j];
-      below[j] = __builtin_amdgcn_mbcnt_hi((uint32_t)(gm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)gm, 0u));
-      grp[j] = g0 ? 0 : (g1 ? 1 : 2);
-      r[j] = 0;
-      if (act[j] && (grp[j] == 2 || below[j] == 0))
-        r[j] = atomicAdd(&counts[addr], grp[j] == 2 ? 1u : (uint32_t)__popcll(gm));
-    }
-#pragma unroll
-    for (int j = 0; j < MAXW; j++) {
-      uint32_t b0 = 0, b1 = 0;
-      if (m0[j]) b0 = __builtin_amdgcn_readlane(r[j], (int)__builtin_ctzll(m0[j]));
-      if (m1[j]) b1 = __builtin_amdgcn_readlane(r[j], (int)__builtin_ctzll(m1[j]));
-      if (grp[j] == 0) r[j] = b0 + below[j];
-      if (grp[j] == 1) r[j] = b1 + below[j];
-      if (act[j]) rank[(size_t)j * m + i] = r[j];
-    }
-  } else {
-    for_each_signed_digit(s, c, nwin, [&](uint32_t j, uint32_t sl, bool) {
-      rank[(size_t)j * m + i] = atomicAdd(&counts[(j << sh) | sl], 1u);
-    });
+// Signed digit of window jw of a half-scalar, the recoding of for_each_signed_digit:
+// the carry is run up from window 0. mag = |d|, neg = d < 0.
+__device__ __forceinline__ void signed_digit_at(const sc256& s, uint32_t c, uint32_t nwin,
+                                                uint32_t jw, uint32_t& mag, bool& neg) {
+  const uint32_t half = 1u << (c - 1);
+  uint32_t carry = 0;
+  for (uint32_t j = 0; j < jw; j++) carry = (window_digit(s, j * c, c) + carry > half) ? 1u : 0u;
+  const uint32_t raw = window_digit(s, jw * c, c) + carry;
+  neg = (jw + 1 < nwin) && raw > half;
+  mag = neg ? (1u << c) - raw : raw;
+}
+
+// Counting pass of the counting sort, one block per (chunk of half-scalars, window):
+// the block counts its entries into an LDS histogram of the window's 2^(c-1) buckets,
+// the LDS atomic returning each entry's rank among the chunk's entries of its bucket
+// (kept in rank[j m + i]), and writes the histogram to hist_blk[(j nchunk + chunk) H
+// + slot]. No atomic leaves the block, so a bucket that collects a large share of the
+// entries costs no more than any other.
+__global__ void __launch_bounds__(1024) k_hist_tile(const uint32_t* __restrict__ halfs, uint32_t m,
+                                                    uint32_t c, uint32_t nwin, uint32_t chunk,
+                                                    uint32_t nchunk, uint32_t* __restrict__ hist_blk,
+                                                    uint32_t* __restrict__ rank) {
+  extern __shared__ uint32_t lds_hist[];
+  const uint32_t H = 1u << (c - 1);
+  const uint32_t ch = blockIdx.x, j = blockIdx.y;
+  for (uint32_t k = threadIdx.x; k < H; k += blockDim.x) lds_hist[k] = 0;
+  __syncthreads();
+  const uint32_t i0 = ch * chunk, i1 = min(m, i0 + chunk);
+  for (uint32_t i = i0 + threadIdx.x; i < i1; i += blockDim.x) {
+    bool sneg;
+    const sc256 s = load_half(halfs, i, sneg);
+    uint32_t mag;
+    bool neg;
+    signed_digit_at(s, c, nwin, j, mag, neg);
+    if (mag) rank[(size_t)j * m + i] = atomicAdd(&lds_hist[mag - 1], 1u);
   }
+  __syncthreads();
+  uint32_t* out = hist_blk + ((size_t)j * nchunk + ch) * H;
+  for (uint32_t k = threadIdx.x; k < H; k += blockDim.x) out[k] = lds_hist[k];
+}
+
+// Per bucket (thread t = j 2^(c-1) + slot): the per-chunk counts become each chunk's
+// exclusive prefix within the bucket, and counts[t] the bucket's total.
+__global__ void __launch_bounds__(256) k_chunk_scan(uint32_t* __restrict__ hist_blk, uint32_t c,
+                                                    uint32_t nwin, uint32_t nchunk,
+                                                    uint32_t* __restrict__ counts) {
+  const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint32_t H = 1u << (c - 1);
+  if (t >= nwin * H) return;
+  const uint32_t j = t >> (c - 1), slot = t & (H - 1);
+  uint32_t run = 0;
+  for (uint32_t ch = 0; ch < nchunk; ch++) {
+    uint32_t* p = hist_blk + ((size_t)j * nchunk + ch) * H + slot;
+    const uint32_t v = *p;
+    *p = run;
+    run += v;
+  }
+  counts[t] = run;
 }
 
 // Bucket lists hold point indices with the sign of (digit x half-scalar) in bit 31,
-// written at the bucket's offset plus the rank the counting pass handed out.
+// written at the bucket's offset plus the chunk's prefix within the bucket plus the
+// rank the counting pass handed out. MAXW > 0 unrolls over at most MAXW windows so
+// that the loads of one half-scalar are all in flight together.
 template <int MAXW>
 __global__ void __launch_bounds__(256) k_scatter(const uint32_t* __restrict__ halfs, uint32_t m,
-                                                 uint32_t c, uint32_t nwin,
+                                                 uint32_t c, uint32_t nwin, uint32_t chunk,
+                                                 uint32_t nchunk,
                                                  const uint32_t* __restrict__ offsets,
+                                                 const uint32_t* __restrict__ hist_blk,
                                                  const uint32_t* __restrict__ rank,
                                                  uint32_t* __restrict__ sorted_idx) {
   uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= m) return;
   bool sneg;
   const sc256 s = load_half(halfs, i, sneg);
-  const uint32_t sh = c - 1;
+  const uint32_t sh = c - 1, ch = i / chunk;
+  auto pos_of = [&](uint32_t j, uint32_t slot) -> uint32_t {
+    return offsets[(j << sh) | slot] + hist_blk[(((size_t)j * nchunk + ch) << sh) + slot] +
+           rank[(size_t)j * m + i];
+  };
   if constexpr (MAXW > 0) {
     uint32_t slot[MAXW], pos[MAXW];
     bool act[MAXW], neg[MAXW];
     signed_digits<MAXW>(s, c, nwin, slot, act, neg);
 #pragma unroll
     for (int j = 0; j < MAXW; j++)
-      if (act[j]) pos[j] = offsets[((uint32_t)j << sh) | slot[j]] + rank[(size_t)j * m + i];
+      if (act[j]) pos[j] = pos_of((uint32_t)j, slot[j]);
 #pragma unroll
     for (int j = 0; j < MAXW; j++)
       if (act[j]) sorted_idx[pos[j]] = i | ((neg[j] != sneg) ? 0x80000000u : 0u);
   } else {
     for_each_signed_digit(s, c, nwin, [&](uint32_t j, uint32_t sl, bool ng) {
-      const uint32_t pos = offsets[(j << sh) | sl] + rank[(size_t)j * m + i];
-      sorted_idx[pos] = i | ((ng != sneg) ? 0x80000000u : 0u);
+      sorted_idx[pos_of(j, sl)] = i | ((ng != sneg) ? 0x80000000u : 0u);
     });
   }
 }
@@ -796,21 +807,30 @@ hipError_t launch_glv_prep(const g1a* points, const uint32_t* scalars, uint32_t 
 }
 
 hipError_t launch_hist(const uint32_t* halfs, uint32_t m, uint32_t c, uint32_t nwin,
-                       uint32_t* counts, uint32_t* rank, hipStream_t s) {
-  if (nwin <= 16)
-    k_hist<16><<<grid_for(m, 256), 256, 0, s>>>(halfs, m, c, nwin, counts, rank);
-  else
-    k_hist<0><<<grid_for(m, 256), 256, 0, s>>>(halfs, m, c, nwin, counts, rank);
+                       uint32_t chunk, uint32_t nchunk, uint32_t* hist_blk, uint32_t* counts,
+                       uint32_t* rank, hipStream_t s) {
+  const size_t lds = ((size_t)1 << (c - 1)) * 4;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)k_hist_tile,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  k_hist_tile<<<dim3(nchunk, nwin), 1024, lds, s>>>(halfs, m, c, nwin, chunk, nchunk, hist_blk, rank);
+  const uint32_t K = nwin << (c - 1);
+  k_chunk_scan<<<grid_for(K, 256), 256, 0, s>>>(hist_blk, c, nwin, nchunk, counts);
   return hipGetLastError();
 }
 
 hipError_t launch_scatter(const uint32_t* halfs, uint32_t m, uint32_t c, uint32_t nwin,
-                          const uint32_t* offsets, const uint32_t* rank, uint32_t* sorted_idx,
+                          uint32_t chunk, uint32_t nchunk, const uint32_t* offsets,
+                          const uint32_t* hist_blk, const uint32_t* rank, uint32_t* sorted_idx,
                           hipStream_t s) {
   if (nwin <= 16)
-    k_scatter<16><<<grid_for(m, 256), 256, 0, s>>>(halfs, m, c, nwin, offsets, rank, sorted_idx);
+    k_scatter<16><<<grid_for(m, 256), 256, 0, s>>>(halfs, m, c, nwin, chunk, nchunk, offsets,
+                                                    hist_blk, rank, sorted_idx);
   else
-    k_scatter<0><<<grid_for(m, 256), 256, 0, s>>>(halfs, m, c, nwin, offsets, rank, sorted_idx);
+    k_scatter<0><<<grid_for(m, 256), 256, 0, s>>>(halfs, m, c, nwin, chunk, nchunk, offsets,
+                                                   hist_blk, rank, sorted_idx);
   return hipGetLastError();
 }
 

@@ -39,6 +39,8 @@ def test_library_exports_every_declared_symbol():
 def test_workspace_bytes():
     assert M.workspace_bytes(1 << 16, 13) > 0
     assert M.workspace_bytes(1 << 16, 13) % 256 == 0
+    for c in (1, 8, 13, 16):  # n = 0 and tiny n still plan a workspace
+        assert M.workspace_bytes(0, c) > 0 and M.workspace_bytes(1, c) > 0
     assert M.workspace_bytes(1 << 16, 0) == 0
     assert M.workspace_bytes(1 << 16, 17) == 0
     assert M.workspace_bytes(M.MSM_MAX_N + 1, 8) == 0
