@@ -130,6 +130,21 @@ __device__ __forceinline__ fp fp_neg(const fp& a) { return fp_sub(fp_zero(), a);
 
 __device__ __forceinline__ fp fp_dbl(const fp& a) { return fp_add(a, a); }
 
+// a / 2 mod p: (a + p) / 2 for odd a, a / 2 for even a (a + p < 2p < 2^255, so the
+// sum fits the eight limbs).
+__device__ __forceinline__ fp fp_half(const fp& a) {
+  const uint32_t mask = 0u - (a.v[0] & 1u);
+  fp s;
+  uint32_t carry = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) s.v[i] = __builtin_addc(a.v[i], p_limb(i) & mask, carry, &carry);
+  fp r;
+#pragma unroll
+  for (int i = 0; i < 7; i++) r.v[i] = (s.v[i] >> 1) | (s.v[i + 1] << 31);
+  r.v[7] = s.v[7] >> 1;
+  return r;
+}
+
 // Montgomery product a * b * 2^-256 mod p, coarsely integrated operand scanning on
 // 32-bit limbs (the default product; see MSMK_MONT29 below).
 // 64-bit value kept whole through code generation: the empty asm stops the compiler

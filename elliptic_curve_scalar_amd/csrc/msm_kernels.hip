@@ -670,29 +670,47 @@ __global__ void __launch_bounds__(256) k_tree_sum(const xyzz_st* __restrict__ in
 
 // ---- window combine ----------------------------------------------------------------
 // The combine is one long chain (c (W - 1) doublings), so its time is latency, not
-// throughput. Each XYZZ doubling has 9 products but only 3 dependent rounds, and an
-// addition 14 products in 4 rounds; the four lanes of a quad split each round
-// (quad.hpp), so a step costs 3 (or 4) product latencies instead of 9 (or 14). Every
-// quad of the wave computes the same chain, so every branch is uniform.
+// throughput. The four lanes of a quad split each round of products (quad.hpp): a run
+// of doublings with one round of lookahead costs 2.5 product latencies per doubling,
+// an addition 4. Every quad computes its own chain, so every branch is uniform within
+// a quad.
 
-// Q = sum_j 2^(c j) W_j, then to affine. Two wavefronts split the chain: wave 0 doubles
-// the top window's sum c (W - 1) times, with no addition on its chain, while wave 1
-// runs Horner over the lower windows (c (W - 2) doublings and W - 2 additions, a
-// shorter chain); one addition joins them. W >= 8 for every c <= 16.
+// XYZZ point of lane (this lane xor `mask`), for a mask that is a multiple of 4 (a whole
+// other quad); ds_bpermute, no LDS storage.
+__device__ __forceinline__ xyzz xyzz_shfl_xor(const xyzz& a, int mask) {
+  xyzz r;
+  const int src = (((int)(threadIdx.x & 63)) ^ mask) << 2;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    r.X.v[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)a.X.v[i]);
+    r.Y.v[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)a.Y.v[i]);
+    r.ZZ.v[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)a.ZZ.v[i]);
+    r.ZZZ.v[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)a.ZZZ.v[i]);
+  }
+  return r;
+}
+
+// Q = sum_j 2^(c j) W_j, then to affine. Two wavefronts: wave 0 doubles the top window's
+// sum c (W - 1) times. In wave 1, quad g doubles W_g c g times (at most c (W - 2)), and a
+// tree over the quads adds the results (four additions deep), so no addition sits on the
+// longest chain; with more than 17 windows (c <= 7) wave 1 runs Horner over the lower
+// windows instead. One addition joins the two waves. W >= 8 for every c <= 16.
 __global__ void __launch_bounds__(128) k_final(const xyzz_st* __restrict__ win, uint32_t nwin,
                                                uint32_t c, g1a* out) {
   __shared__ xyzz_st low;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane & 3;
+  const uint32_t g = (uint32_t)lane >> 2;
   xyzz acc;
   if (wave == 0) {
-    acc = xyzz_load(win + nwin - 1);
-    const uint32_t nd = c * (nwin - 1);
-    for (uint32_t b = 0; b < nd; b++) acc = quad_dbl(acc, q);
+    acc = quad_dbl_n(xyzz_load(win + nwin - 1), c * (nwin - 1), q);
   } else {
-    acc = xyzz_load(win + nwin - 2);
-    for (int j = (int)nwin - 3; j >= 0; j--) {
-      for (uint32_t b = 0; b < c; b++) acc = quad_dbl(acc, q);
-      acc = quad_add(acc, xyzz_load(win + j), q);
+    if (nwin - 1 <= 16) {
+      acc = (g < nwin - 1) ? quad_dbl_n(xyzz_load(win + g), c * g, q) : xyzz_inf();
+#pragma unroll
+      for (int m = 4; m < 64; m <<= 1) acc = quad_add(acc, xyzz_shfl_xor(acc, m), q);
+    } else {
+      acc = xyzz_load(win + nwin - 2);
+      for (int j = (int)nwin - 3; j >= 0; j--) acc = quad_add(quad_dbl_n(acc, c, q), xyzz_load(win + j), q);
     }
     if (lane == 0) xyzz_store(&low, acc);
   }

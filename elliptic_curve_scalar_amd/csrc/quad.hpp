@@ -60,6 +60,91 @@ __device__ __forceinline__ xyzz quad_dbl(const xyzz& p, int q) {
   return o;
 }
 
+// ---- runs of doublings with one round of lookahead --------------------------------
+// A run keeps (X, U = 2Y, M = 3X^2) and a factor z; the XYZZ point it stands for is
+// (X, U / 2, ZZ0 z^2, ZZZ0 z^3), with ZZ0, ZZZ0 those of the run's input. With a = 0, the
+// doubling dbl-2008-s-1 written in U reads
+//   V = U^2,  S = X V,  X' = M^2 - 2 S,
+//   U' = 2 M (S - X') - V^2 = 6 (M X) V - 2 M M^2 - V^2,  z' = z U,
+// its ZZ' = V ZZ and ZZZ' = U V ZZZ being folded into z. M X and M^2 need only X, which
+// the previous step knows a round before its U', so those products start early: two
+// doublings take five rounds of at most four products, against six for two quad_dbl.
+// ZZ and ZZZ never enter the recurrence, so a run on the point at infinity (ZZ0 = 0)
+// stays at infinity.
+struct dchain {
+  fp X, U, M, z;
+};
+
+__device__ __forceinline__ fp fp_triple(const fp& a) { return fp_add(fp_dbl(a), a); }
+
+// Start a run on p. The one product (X^2) is the same on every lane: no broadcast.
+__device__ __forceinline__ dchain quad_chain_begin(const xyzz& p) {
+  dchain c;
+  c.X = p.X;
+  c.U = fp_dbl(p.Y);
+  c.M = fp_triple(fp_sqr(p.X));
+  c.z = fp_one();
+  return c;
+}
+
+// Two doublings in five rounds.
+__device__ __forceinline__ void quad_chain_dbl2(dchain& c, int q) {
+  // round A: V = U^2, M X, M^2, z U
+  fp r = fp_mul(quad_pick(q, c.U, c.M, c.M, c.z), quad_pick(q, c.U, c.X, c.M, c.U));
+  const fp V = quad_from<0>(r), MX = quad_from<1>(r), MM = quad_from<2>(r), z1 = quad_from<3>(r);
+  // round B: X V, (M X) V, M M^2, V^2
+  r = fp_mul(quad_pick(q, c.X, MX, c.M, V), quad_pick(q, V, V, MM, V));
+  const fp XV = quad_from<0>(r), MXV = quad_from<1>(r), M3 = quad_from<2>(r), VV = quad_from<3>(r);
+  const fp X1 = fp_sub(MM, fp_dbl(XV));
+  const fp U1 = fp_sub(fp_dbl(fp_sub(fp_triple(MXV), M3)), VV);
+  // round C: X1^2, V1 = U1^2, z1 U1 (lane 3 repeats lane 0)
+  r = fp_mul(quad_pick(q, X1, U1, z1, X1), quad_pick(q, X1, U1, U1, X1));
+  const fp M1 = fp_triple(quad_from<0>(r)), V1 = quad_from<1>(r);
+  c.z = quad_from<2>(r);
+  // round D: M1 X1, M1^2, X1 V1, V1^2
+  r = fp_mul(quad_pick(q, M1, M1, X1, V1), quad_pick(q, X1, M1, V1, V1));
+  const fp M1X1 = quad_from<0>(r), MM1 = quad_from<1>(r), X1V1 = quad_from<2>(r), VV1 = quad_from<3>(r);
+  c.X = fp_sub(MM1, fp_dbl(X1V1));
+  // round E: (M1 X1) V1, M1 M1^2, X2^2 (lane 3 repeats lane 2)
+  r = fp_mul(quad_pick(q, M1X1, M1, c.X, c.X), quad_pick(q, V1, MM1, c.X, c.X));
+  c.U = fp_sub(fp_dbl(fp_sub(fp_triple(quad_from<0>(r)), quad_from<1>(r))), VV1);
+  c.M = fp_triple(quad_from<2>(r));
+}
+
+// One doubling in three rounds (the last one, X'^2, the same on every lane).
+__device__ __forceinline__ void quad_chain_dbl1(dchain& c, int q) {
+  fp r = fp_mul(quad_pick(q, c.U, c.M, c.M, c.z), quad_pick(q, c.U, c.X, c.M, c.U));
+  const fp V = quad_from<0>(r), MX = quad_from<1>(r), MM = quad_from<2>(r);
+  c.z = quad_from<3>(r);
+  r = fp_mul(quad_pick(q, c.X, MX, c.M, V), quad_pick(q, V, V, MM, V));
+  const fp XV = quad_from<0>(r), MXV = quad_from<1>(r), M3 = quad_from<2>(r), VV = quad_from<3>(r);
+  c.X = fp_sub(MM, fp_dbl(XV));
+  c.U = fp_sub(fp_dbl(fp_sub(fp_triple(MXV), M3)), VV);
+  c.M = fp_triple(fp_sqr(c.X));
+}
+
+// The XYZZ point a run stands for, given its input's ZZ0 and ZZZ0: two rounds.
+__device__ __forceinline__ xyzz quad_chain_end(const dchain& c, const fp& ZZ0, const fp& ZZZ0, int q) {
+  fp r = fp_mul(c.z, quad_pick(q, c.z, ZZZ0, c.z, ZZZ0));  // z^2, z ZZZ0
+  const fp zz = quad_from<0>(r), zZZZ = quad_from<1>(r);
+  r = fp_mul(quad_pick(q, ZZ0, zZZZ, ZZ0, zZZZ), zz);  // ZZ0 z^2, ZZZ0 z^3
+  xyzz o;
+  o.X = c.X;
+  o.Y = fp_half(c.U);
+  o.ZZ = quad_from<0>(r);
+  o.ZZZ = quad_from<1>(r);
+  return o;
+}
+
+// 2^n p by runs of two doublings.
+__device__ __forceinline__ xyzz quad_dbl_n(const xyzz& p, uint32_t n, int q) {
+  if (n == 0) return p;
+  dchain c = quad_chain_begin(p);
+  for (uint32_t i = 0; i < n / 2; i++) quad_chain_dbl2(c, q);
+  if (n & 1u) quad_chain_dbl1(c, q);
+  return quad_chain_end(c, p.ZZ, p.ZZZ, q);
+}
+
 __device__ __forceinline__ xyzz quad_add(const xyzz& p, const xyzz& s, int q) {
   if (xyzz_is_inf(s)) return p;
   if (xyzz_is_inf(p)) return s;
