@@ -117,6 +117,23 @@ __device__ __forceinline__ sc256 load_half(const uint32_t* halfs, uint32_t i, bo
   return r;
 }
 
+// Slots per digit value in window j. The half-scalars have 127-bit magnitudes, so the
+// top window's digits never exceed 2^(127 - c (W - 1)) while it has 2^(c-1) slots like
+// every window: each of its digits is spread over 2^(c W - 128) slots, chosen by the
+// half-scalar's index, which evens out the bucket sizes (at c = 13 the top window's
+// buckets would otherwise be eight times fuller and the pair tree three levels deeper).
+// The running sum weights slot b of window j by floor(b / spread) + 1.
+__device__ __forceinline__ uint32_t window_spread(uint32_t c, uint32_t nwin, uint32_t j) {
+  return (j + 1 == nwin) ? (1u << (c * nwin - 128)) : 1u;
+}
+
+// Slot of a digit of magnitude mag >= 1 in window j, for half-scalar i.
+__device__ __forceinline__ uint32_t digit_slot(uint32_t c, uint32_t nwin, uint32_t j, uint32_t mag,
+                                               uint32_t i) {
+  const uint32_t f = window_spread(c, nwin, j);
+  return (mag - 1) * f + (i & (f - 1));
+}
+
 // Signed digits of one half-scalar for a fixed maximum window count: slot[j] = |d_j| - 1
 // and act[j] = (d_j != 0), the same recoding as for_each_signed_digit. Unrolled, so the
 // per-window memory operations that follow can all be in flight together.
@@ -173,7 +190,7 @@ __global__ void __launch_bounds__(1024) k_hist_tile(const uint32_t* __restrict__
     uint32_t mag;
     bool neg;
     signed_digit_at(s, c, nwin, j, mag, neg);
-    if (mag) rank[(size_t)j * m + i] = atomicAdd(&lds_hist[mag - 1], 1u);
+    if (mag) rank[(size_t)j * m + i] = atomicAdd(&lds_hist[digit_slot(c, nwin, j, mag, i)], 1u);
   }
   __syncthreads();
   uint32_t* out = hist_blk + ((size_t)j * nchunk + ch) * H;
@@ -226,13 +243,13 @@ __global__ void __launch_bounds__(256) k_scatter(const uint32_t* __restrict__ ha
     signed_digits<MAXW>(s, c, nwin, slot, act, neg);
 #pragma unroll
     for (int j = 0; j < MAXW; j++)
-      if (act[j]) pos[j] = pos_of((uint32_t)j, slot[j]);
+      if (act[j]) pos[j] = pos_of((uint32_t)j, digit_slot(c, nwin, (uint32_t)j, slot[j] + 1, i));
 #pragma unroll
     for (int j = 0; j < MAXW; j++)
       if (act[j]) sorted_idx[pos[j]] = i | ((neg[j] != sneg) ? 0x80000000u : 0u);
   } else {
     for_each_signed_digit(s, c, nwin, [&](uint32_t j, uint32_t sl, bool ng) {
-      sorted_idx[pos_of(j, sl)] = i | ((ng != sneg) ? 0x80000000u : 0u);
+      sorted_idx[pos_of(j, digit_slot(c, nwin, j, sl + 1, i))] = i | ((ng != sneg) ? 0x80000000u : 0u);
     });
   }
 }
@@ -618,10 +635,11 @@ __global__ void __launch_bounds__(128) k_level_xyzz_q(const void* __restrict__ i
 }
 
 // ------------------------------------------------------------------ reduction
-// Window j has 2^(c-1) bucket slots; slot b holds the points whose digit has
-// magnitude b + 1, so W_j = sum_b (b + 1) B_b. Segment s covers slots [lo, hi): with
-// T = sum of its slots and R = sum_b (b - lo + 1) B_b (a running sum from the top slot
-// down), its share of W_j is R + lo T.
+// Window j has 2^(c-1) bucket slots; slot b holds points whose digit has magnitude
+// floor(b / f) + 1 (f = window_spread), so W_j = sum_b (floor(b / f) + 1) B_b. Segment s
+// covers slots [lo, hi). Running from the top slot down, T sums the slots so far and R
+// adds T at every slot that is a multiple of f; then R = sum_b (floor(b / f) -
+// ceil(lo / f) + 1) B_b, and the segment's share of W_j is R + ceil(lo / f) T.
 __global__ void __launch_bounds__(128) k_rsum_seg(const xyzz_st* __restrict__ bsum, uint32_t c,
                                                   uint32_t nwin, uint32_t seg_len, uint32_t nseg,
                                                   xyzz_st* __restrict__ seg_out) {
@@ -633,12 +651,13 @@ __global__ void __launch_bounds__(128) k_rsum_seg(const xyzz_st* __restrict__ bs
   const uint32_t nb = 1u << (c - 1);
   uint32_t j = t / nseg, s = t % nseg;
   uint32_t lo = s * seg_len, hi = min(nb, (s + 1) * seg_len);
+  const uint32_t f = window_spread(c, nwin, j);
   xyzz T = xyzz_inf(), R = xyzz_inf();
   for (uint32_t b = hi; b-- > lo;) {
     T = quad_add(T, xyzz_load(bsum + (size_t)j * nb + b), q);
-    R = quad_add(R, T, q);
+    if ((b & (f - 1)) == 0) R = quad_add(R, T, q);
   }
-  const xyzz res = quad_add(R, quad_mul_small(T, lo, q), q);
+  const xyzz res = quad_add(R, quad_mul_small(T, (lo + f - 1) / f, q), q);
   if (q == 0) xyzz_store(seg_out + t, res);
 }
 
