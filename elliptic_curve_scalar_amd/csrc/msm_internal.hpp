@@ -15,7 +15,6 @@ constexpr uint32_t SCAN_MAX_BLOCKS = 256 * SCAN_TOP_ITEMS;
 constexpr int MAX_LEVELS = 32;                       // pair-tree levels tracked
 constexpr unsigned LEVEL_BLOCK = 128;                // lanes per block in k_level
 constexpr uint32_t XYZZ_QUAD_MAX_PAIRS = 65536;      // XYZZ levels this small use 4 lanes per add
-constexpr int SEARCH_STEPS = 22;                     // bucket searches cover K < 2^22
 
 // Plan read back to the host after the sort (one 16 + 4 * MAX_LEVELS byte copy).
 struct msm_stats {

@@ -465,17 +465,41 @@ __global__ void __launch_bounds__(256) k_bucket_init(const uint32_t* __restrict_
 // that much room before the next bucket.
 __device__ __forceinline__ uint32_t half_base(uint32_t off, uint32_t k) { return (off + k) >> 1; }
 
-// Largest k in [0, n) with a[k] <= x, for a non-decreasing a with a[0] <= x: a
-// branch-free binary search with a fixed trip count (n <= 2^SEARCH_STEPS), so it can
-// sit inside fully unrolled slot loops.
-__device__ __forceinline__ uint32_t last_le(const uint32_t* a, uint32_t n, uint32_t x) {
-  uint32_t k = 0;
-#pragma unroll
-  for (int b = SEARCH_STEPS - 1; b >= 0; b--) {
-    uint32_t t = k + (1u << b);
-    k = (t < n && a[t] <= x) ? t : k;
+// Bucket of a pair: the largest k in [0, n) with a[k] <= x, for the non-decreasing pair
+// offsets a of a level (n + 1 entries, a[0] = 0 <= x < a[n]). Each read is a dependent
+// load, so rather than bisecting all n buckets the search first tests, with two loads
+// issued together, whether the answer lies within GUESS_SPAN buckets of a guess, and
+// then bisects that bracket (about log2(2 GUESS_SPAN) reads) or, when it does not (skewed
+// bucket sizes), the whole array. Every lane runs the same code path, so a wavefront
+// waits for its slowest lane's reads and for nothing else.
+constexpr uint32_t GUESS_SPAN = 128;
+
+// Largest k in [lo, hi) with a[k] <= x, given a[lo] <= x < a[hi].
+__device__ __forceinline__ uint32_t bisect_le(const uint32_t* a, uint32_t lo, uint32_t hi, uint32_t x) {
+  while (hi - lo > 1) {
+    const uint32_t mid = lo + ((hi - lo) >> 1);
+    if (a[mid] <= x) lo = mid;
+    else hi = mid;
   }
-  return k;
+  return lo;
+}
+
+// The bucket of x, searched from the guess g.
+__device__ __forceinline__ uint32_t bucket_of(const uint32_t* a, uint32_t n, uint32_t x, uint32_t g) {
+  if (g >= n) g = n - 1;
+  uint32_t lo = g > GUESS_SPAN ? g - GUESS_SPAN : 0u;
+  uint32_t hi = min(g + GUESS_SPAN, n);
+  const bool in = (a[lo] <= x) & (a[hi] > x);
+  if (!in) {
+    lo = 0;
+    hi = n;
+  }
+  return bisect_le(a, lo, hi, x);
+}
+
+// Guess for the bucket of pair p: pairs spread evenly over the K buckets.
+__device__ __forceinline__ uint32_t bucket_guess(uint32_t p, uint32_t K, uint32_t npairs) {
+  return (uint32_t)(((uint64_t)p * K) / npairs);
 }
 
 // Operands of pair-tree level `level`: pair m of bucket k adds elements 2m and 2m+1
@@ -532,12 +556,18 @@ __global__ void __launch_bounds__(256) k_level(const g1a* __restrict__ in,
   int cnt = (int)min((uint64_t)S, (uint64_t)npairs - p0);
   LevelSrc<S> src{in, idx, out, bsum, counts, offsets, level, {}, {}, {}, {}};
   // bucket of the first pair; later pairs stay in it or move to a later bucket
-  uint32_t k = last_le(poff, K, (uint32_t)p0);
+  uint32_t k = bucket_of(poff, K, (uint32_t)p0, bucket_guess((uint32_t)p0, K, npairs));
 #pragma unroll
   for (int s = 0; s < S; s++) {
     if (s < cnt) {
       uint32_t p = (uint32_t)p0 + s;
-      if (p >= poff[k + 1]) k = last_le(poff, K, p);
+      if (p >= poff[k + 1]) {  // a later bucket: most often the next one
+        k++;
+        if (k + 1 < K && p >= poff[k + 1]) {
+          const uint32_t hi = min(k + 9, K);
+          k = bisect_le(poff, k + 1, poff[hi] > p ? hi : K, p);
+        }
+      }
       uint32_t m = p - poff[k];
       src.kb[s] = k;
       src.mm[s] = m;
@@ -564,7 +594,7 @@ __global__ void __launch_bounds__(128, 3) k_level_xyzz(const void* __restrict__ 
                                                     uint32_t npairs, int level) {
   uint32_t p = blockIdx.x * blockDim.x + threadIdx.x;
   if (p >= npairs) return;
-  uint32_t k = last_le(poff, K, p);
+  uint32_t k = bucket_of(poff, K, p, bucket_guess(p, K, npairs));
   uint32_t m = p - poff[k];
   uint32_t off = offsets[k];
   uint32_t base = idx ? off : half_base(off, k);
@@ -608,7 +638,7 @@ __global__ void __launch_bounds__(128) k_level_xyzz_q(const void* __restrict__ i
   const uint32_t p = gid >> 2;
   const int q = (int)(gid & 3u);
   if (p >= npairs) return;
-  uint32_t k = last_le(poff, K, p);
+  uint32_t k = bucket_of(poff, K, p, bucket_guess(p, K, npairs));
   uint32_t m = p - poff[k];
   uint32_t off = offsets[k];
   uint32_t base = idx ? off : half_base(off, k);
