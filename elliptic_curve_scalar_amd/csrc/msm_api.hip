@@ -45,7 +45,7 @@ uint32_t segment_length(int c, int nwin) {
 
 struct Layout {
   size_t stats, halfs, pts2, counts, offsets, rank, hist_blk, poff, block_sums, sorted_idx, aff_a, aff_b,
-      xz_a, xz_b, bsum, seg, part, win;
+      xz_a, xz_b, bsum, part, win;
   size_t total;
   uint32_t K, nwin, seg_len, nseg, chunk, nchunk;
   size_t E_max, half;
@@ -89,7 +89,6 @@ Layout plan(size_t n, int c) {
   L.xz_a = take(L.half * sizeof(xyzz_st));
   L.xz_b = take(L.half * sizeof(xyzz_st));
   L.bsum = take((size_t)L.K * sizeof(xyzz_st));
-  L.seg = take((size_t)L.nwin * L.nseg * sizeof(xyzz_st));
   L.part = take((size_t)L.nwin * reduce_blocks(L.nseg) * sizeof(xyzz_st));
   L.win = take((size_t)L.nwin * sizeof(xyzz_st));
   L.total = off;
@@ -263,7 +262,6 @@ int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scala
   g1a* aff[2] = {(g1a*)(ws + L.aff_a), (g1a*)(ws + L.aff_b)};
   xyzz_st* xz[2] = {(xyzz_st*)(ws + L.xz_a), (xyzz_st*)(ws + L.xz_b)};
   xyzz_st* bsum = (xyzz_st*)(ws + L.bsum);
-  xyzz_st* seg = (xyzz_st*)(ws + L.seg);
   xyzz_st* part = (xyzz_st*)(ws + L.part);
   xyzz_st* win = (xyzz_st*)(ws + L.win);
   const g1a* pts = pts2;  // 2n points: P_i and phi(P_i)
@@ -333,7 +331,7 @@ int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scala
 
   // running sum per window, window combine
   PhaseMark ph_red(ctx, st, PH_REDUCE);
-  HIP_TRY(launch_reduce(bsum, c32, L.nwin, L.seg_len, L.nseg, seg, part, win, st));
+  HIP_TRY(launch_reduce(bsum, c32, L.nwin, L.seg_len, L.nseg, part, win, st));
   ph_red.end();
   PhaseMark ph_fin(ctx, st, PH_FINAL);
   HIP_TRY(launch_final(win, L.nwin, c32, (g1a*)d_out, st));

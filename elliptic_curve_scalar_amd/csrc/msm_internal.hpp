@@ -73,7 +73,7 @@ inline uint32_t reduce_blocks(uint32_t nseg) {
   return b < 1 ? 1 : (b > 64 ? 64 : b);
 }
 hipError_t launch_reduce(const xyzz_st* bsum, uint32_t c, uint32_t nwin, uint32_t seg_len,
-                         uint32_t nseg, xyzz_st* seg, xyzz_st* part, xyzz_st* win, hipStream_t s);
+                         uint32_t nseg, xyzz_st* part, xyzz_st* win, hipStream_t s);
 hipError_t launch_final(const xyzz_st* win, uint32_t nwin, uint32_t c, g1a* out, hipStream_t s);
 hipError_t launch_from_scalars(const uint32_t* ks, uint32_t n, g1a* out, hipStream_t s);
 hipError_t launch_test_fp(int op, const uint32_t* a, const uint32_t* b, uint32_t* out, uint32_t n,

@@ -15,8 +15,9 @@
 //   k_level<S>    pair-tree level 0: pair (2m, 2m+1) of every bucket -> element m,
 //                 S pairs per lane with one inversion (batch_add.hpp)
 //   k_level_xyzz  deeper levels in XYZZ coordinates (quad-cooperative when small)
-//   k_rsum_seg    per window, segments of buckets: sum_b b * B_b by a running sum
-//   k_tree_sum    per window: two-pass tree over its segments -> W_j
+//   k_rsum_tree   per window, segments of buckets: sum_b b * B_b by running sums,
+//                 summed per block through an LDS tree
+//   k_tree_sum    per window: the blocks' partial sums -> W_j
 //   k_final       Q = sum_j 2^(c j) W_j by doubling, then affine
 //
 // The method is aztec-packages PR #23738 / #23736 / #23520 ("bb/msm"); its WebGPU
@@ -670,41 +671,24 @@ __global__ void __launch_bounds__(128) k_level_xyzz_q(const void* __restrict__ i
 // covers slots [lo, hi). Running from the top slot down, T sums the slots so far and R
 // adds T at every slot that is a multiple of f; then R = sum_b (floor(b / f) -
 // ceil(lo / f) + 1) B_b, and the segment's share of W_j is R + ceil(lo / f) T.
-__global__ void __launch_bounds__(128) k_rsum_seg(const xyzz_st* __restrict__ bsum, uint32_t c,
-                                                  uint32_t nwin, uint32_t seg_len, uint32_t nseg,
-                                                  xyzz_st* __restrict__ seg_out) {
-  // one segment per quad (quad.hpp)
-  const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
-  const uint32_t t = gid >> 2;
-  const int q = (int)(gid & 3u);
-  if (t >= nwin * nseg) return;
+__device__ __forceinline__ xyzz rsum_segment(const xyzz_st* __restrict__ bsum, uint32_t c,
+                                             uint32_t nwin, uint32_t seg_len, uint32_t j,
+                                             uint32_t s, int q) {
   const uint32_t nb = 1u << (c - 1);
-  uint32_t j = t / nseg, s = t % nseg;
-  uint32_t lo = s * seg_len, hi = min(nb, (s + 1) * seg_len);
+  const uint32_t lo = s * seg_len, hi = min(nb, (s + 1) * seg_len);
   const uint32_t f = window_spread(c, nwin, j);
   xyzz T = xyzz_inf(), R = xyzz_inf();
   for (uint32_t b = hi; b-- > lo;) {
     T = quad_add(T, xyzz_load(bsum + (size_t)j * nb + b), q);
     if ((b & (f - 1)) == 0) R = quad_add(R, T, q);
   }
-  const xyzz res = quad_add(R, quad_mul_small(T, (lo + f - 1) / f, q), q);
-  if (q == 0) xyzz_store(seg_out + t, res);
+  return quad_add(R, quad_mul_small(T, (lo + f - 1) / f, q), q);
 }
 
-// Sums of groups of n consecutive XYZZ points, split over nblk blocks per group:
-// block b of group g adds items [b chunk, (b + 1) chunk) of the group (chunk =
-// ceil(n / nblk)), its 64 quads striding over them, then a tree through LDS, and
-// writes out[g nblk + b]. Two passes (nblk blocks, then one) turn a group of up to
-// 4096 segment sums into its window sum with about 14 dependent additions.
-__global__ void __launch_bounds__(256) k_tree_sum(const xyzz_st* __restrict__ in, uint32_t n,
-                                                  uint32_t nblk, xyzz_st* __restrict__ out) {
-  __shared__ xyzz_st lds[64];
-  const uint32_t g = blockIdx.x / nblk, b = blockIdx.x % nblk, quad = threadIdx.x >> 2;
+// The 64 quads of a block add their points through an LDS tree; thread 0 stores the sum.
+__device__ __forceinline__ void block_quad_sum(xyzz acc, xyzz_st* lds, xyzz_st* out) {
+  const uint32_t quad = threadIdx.x >> 2;
   const int q = (int)(threadIdx.x & 3u);
-  const uint32_t chunk = (n + nblk - 1) / nblk;
-  const uint32_t lo = b * chunk, hi = min(n, lo + chunk);
-  xyzz acc = xyzz_inf();
-  for (uint32_t i = lo + quad; i < hi; i += 64) acc = quad_add(acc, xyzz_load(in + (size_t)g * n + i), q);
   if (q == 0) xyzz_store(&lds[quad], acc);
   __syncthreads();
   for (uint32_t stride = 32; stride > 0; stride >>= 1) {
@@ -714,7 +698,37 @@ __global__ void __launch_bounds__(256) k_tree_sum(const xyzz_st* __restrict__ in
     }
     __syncthreads();
   }
-  if (threadIdx.x == 0) xyzz_store(out + (size_t)g * nblk + b, acc);
+  if (threadIdx.x == 0) xyzz_store(out, acc);
+}
+
+// Running sums and the first tree pass in one launch: block b of window j takes segments
+// [b chunk, (b + 1) chunk) of the window's nseg (chunk = ceil(nseg / nblk)), one quad
+// per segment (64 quads striding over them), and writes their sum to out[j nblk + b].
+__global__ void __launch_bounds__(256) k_rsum_tree(const xyzz_st* __restrict__ bsum, uint32_t c,
+                                                   uint32_t nwin, uint32_t seg_len, uint32_t nseg,
+                                                   uint32_t nblk, xyzz_st* __restrict__ out) {
+  __shared__ xyzz_st lds[64];
+  const uint32_t j = blockIdx.x / nblk, b = blockIdx.x % nblk, quad = threadIdx.x >> 2;
+  const int q = (int)(threadIdx.x & 3u);
+  const uint32_t chunk = (nseg + nblk - 1) / nblk;
+  const uint32_t lo = b * chunk, hi = min(nseg, lo + chunk);
+  xyzz acc = xyzz_inf();
+  for (uint32_t sg = lo + quad; sg < hi; sg += 64)
+    acc = quad_add(acc, rsum_segment(bsum, c, nwin, seg_len, j, sg, q), q);
+  block_quad_sum(acc, lds, out + blockIdx.x);
+}
+
+// Sums of groups of n consecutive XYZZ points, one block per group (64 quads striding
+// over the group, then the LDS tree): the second pass, from the partials of
+// k_rsum_tree to the window sums.
+__global__ void __launch_bounds__(256) k_tree_sum(const xyzz_st* __restrict__ in, uint32_t n,
+                                                  xyzz_st* __restrict__ out) {
+  __shared__ xyzz_st lds[64];
+  const uint32_t g = blockIdx.x, quad = threadIdx.x >> 2;
+  const int q = (int)(threadIdx.x & 3u);
+  xyzz acc = xyzz_inf();
+  for (uint32_t i = quad; i < n; i += 64) acc = quad_add(acc, xyzz_load(in + (size_t)g * n + i), q);
+  block_quad_sum(acc, lds, out + g);
 }
 
 // ---- window combine ----------------------------------------------------------------
@@ -970,11 +984,10 @@ hipError_t launch_level_xyzz(bool in_aff, const void* in, const uint32_t* idx, x
 }
 
 hipError_t launch_reduce(const xyzz_st* bsum, uint32_t c, uint32_t nwin, uint32_t seg_len,
-                         uint32_t nseg, xyzz_st* seg, xyzz_st* part, xyzz_st* win, hipStream_t s) {
-  k_rsum_seg<<<grid_for((size_t)nwin * nseg * 4, 128), 128, 0, s>>>(bsum, c, nwin, seg_len, nseg, seg);
+                         uint32_t nseg, xyzz_st* part, xyzz_st* win, hipStream_t s) {
   const uint32_t nblk = reduce_blocks(nseg);
-  k_tree_sum<<<nwin * nblk, 256, 0, s>>>(seg, nseg, nblk, part);
-  k_tree_sum<<<nwin, 256, 0, s>>>(part, nblk, 1, win);
+  k_rsum_tree<<<nwin * nblk, 256, 0, s>>>(bsum, c, nwin, seg_len, nseg, nblk, part);
+  k_tree_sum<<<nwin, 256, 0, s>>>(part, nblk, win);
   return hipGetLastError();
 }
 
