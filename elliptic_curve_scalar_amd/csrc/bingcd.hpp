@@ -17,10 +17,11 @@
 // shows up as a negative result, which is negated together with its factors) and to
 // u, v, where the division by 2^30 is exact modular division: add the multiple of p
 // that clears the low 30 bits, shift, then bring the result from (-p, 2p) into
-// [0, p). Every lane runs the same fixed number of batches, so a wavefront never
-// diverges. The exact algorithm needs at most 507 steps; random inputs need far fewer
-// (of 40 million sampled, none needed more than 14 batches of 30), so 15 batches are
-// run, and a lane whose b has not reached 1 (y = 0, or an input the batches do not
+// [0, p). Every lane of a wavefront runs the same batches, so the wavefront never
+// diverges; it stops once every lane has reached a = 0, after which a batch would leave
+// v unchanged. The exact algorithm needs at most 507 steps; random inputs need far fewer
+// (of 40 million sampled, none needed more than 14 batches of 30), so at most 15 batches
+// are run, and a lane whose b has not reached 1 (y = 0, or an input the batches do not
 // cover) takes Fermat's inverse instead: the result is exact for every input.
 #pragma once
 #include "fp.hpp"
@@ -208,13 +209,18 @@ __device__ __forceinline__ fp fp_inv_bingcd(const fp& x) {
     uint32_t nu[8], nv[8];
     bg_lin_mod(u, v, f0, g0, nu);
     bg_lin_mod(u, v, f1, g1, nv);
+    uint32_t az = 0;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
       a[i] = na[i];
       b[i] = nb[i];
       u[i] = nu[i];
       v[i] = nv[i];
+      az |= na[i];
     }
+    // Once a = 0 a batch only halves a: its factors are (1, 0) and (0, 2^30), so b and v
+    // stay as they are. The wavefront stops when every lane has got there.
+    if (__all(az == 0)) break;
   }
   uint32_t one = b[0] ^ 1u;
 #pragma unroll
