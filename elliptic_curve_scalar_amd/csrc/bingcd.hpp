@@ -110,26 +110,43 @@ __device__ __forceinline__ void bg_batch(uint64_t xa, uint64_t xb, int32_t& f0, 
   }
 }
 
-// x * f as a two's-complement 64-bit value, for a word x and |f| <= 2^30.
-__device__ __forceinline__ uint64_t bg_smul(uint32_t x, int32_t f) {
-  uint64_t r = (uint64_t)x * (uint32_t)f;
-  return f < 0 ? r - ((uint64_t)x << 32) : r;
+// t = x f + y g (+ k p when KP) as nine words of a two's-complement integer, for x, y
+// below 2^254 and |f| + |g| <= 2^30. The factors are offset to f + 2^30 and g + 2^30
+// (both in [0, 2^31]), so each word is plain chained multiply-adds that stay inside 64
+// bits ((2^32 - 1)(f + g + 2^31 + k) plus a carry is below 2^64 as f + g + 2^31 <= 3 2^30
+// and k < 2^30), and 2^30 (x + y) is subtracted once at the end.
+template <bool KP>
+__device__ __forceinline__ void bg_comb(const uint32_t (&x)[8], const uint32_t (&y)[8], int32_t f,
+                                        int32_t g, uint32_t k, uint32_t (&t)[9]) {
+  const uint32_t fo = (uint32_t)f + (1u << 30), go = (uint32_t)g + (1u << 30);
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    uint64_t s = (uint64_t)x[i] * fo + c;
+    s = (uint64_t)y[i] * go + s;
+    if (KP) s = (uint64_t)k * bg_p(i) + s;
+    t[i] = (uint32_t)s;
+    c = (uint32_t)(s >> 32);
+  }
+  t[8] = c;
+  // subtract (x + y) << 30 (x + y < 2^255: nine words after the shift)
+  uint32_t sum[8], cs = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) sum[i] = __builtin_addc(x[i], y[i], cs, &cs);
+  uint32_t b = 0;
+  t[0] = __builtin_subc(t[0], sum[0] << 30, b, &b);
+#pragma unroll
+  for (int i = 1; i < 8; i++) t[i] = __builtin_subc(t[i], (sum[i] << 30) | (sum[i - 1] >> 2), b, &b);
+  t[8] = __builtin_subc(t[8], (cs << 30) | (sum[7] >> 2), b, &b);
 }
 
 // out = |a f + b g| / 2^30 (the sum is a multiple of 2^30); returns true when the sum
-// was negative. |f| + |g| <= 2^30 keeps every column inside a signed 64-bit value.
+// was negative.
 __device__ __forceinline__ bool bg_lin(const uint32_t (&a)[8], const uint32_t (&b)[8], int32_t f,
                                        int32_t g, uint32_t (&out)[8]) {
   uint32_t t[9];
-  int64_t carry = 0;
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const int64_t s = (int64_t)bg_smul(a[i], f) + (int64_t)bg_smul(b[i], g) + carry;
-    t[i] = (uint32_t)s;
-    carry = s >> 32;
-  }
-  t[8] = (uint32_t)carry;
-  const bool neg = carry < 0;
+  bg_comb<false>(a, b, f, g, 0u, t);
+  const bool neg = (int32_t)t[8] < 0;
   const uint32_t m = neg ? 0xffffffffu : 0u;
   uint32_t c = neg ? 1u : 0u;
 #pragma unroll
@@ -146,15 +163,7 @@ __device__ __forceinline__ void bg_lin_mod(const uint32_t (&u)[8], const uint32_
   const uint32_t lo = u[0] * (uint32_t)f + v[0] * (uint32_t)g;
   const uint32_t k = (lo * BG_NPINV30) & 0x3fffffffu;
   uint32_t t[9];
-  int64_t carry = 0;
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const int64_t s = (int64_t)bg_smul(u[i], f) + (int64_t)bg_smul(v[i], g) +
-                      (int64_t)((uint64_t)k * bg_p(i)) + carry;
-    t[i] = (uint32_t)s;
-    carry = s >> 32;
-  }
-  t[8] = (uint32_t)carry;
+  bg_comb<true>(u, v, f, g, k, t);
   // r = t / 2^30 lies in (-p, 2p): nine words, the top one signed
   uint32_t r[9];
 #pragma unroll
