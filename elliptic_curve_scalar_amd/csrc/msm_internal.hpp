@@ -66,8 +66,8 @@ hipError_t launch_level_xyzz(bool in_aff, const void* in, const uint32_t* idx, x
                              xyzz_st* bsum, const uint32_t* counts, const uint32_t* offsets,
                              const uint32_t* poff, uint32_t K, uint32_t npairs, int level,
                              hipStream_t s);
-// Blocks per window in the first pass of the segment-sum tree: 64 segments per block,
-// at most 64 blocks.
+// Blocks per window in the first pass of the segment-sum tree: 64 segments per block
+// (one per quad), at most 64 blocks; every c has at most 4096 segments per window.
 inline uint32_t reduce_blocks(uint32_t nseg) {
   uint32_t b = (nseg + 63) / 64;
   return b < 1 ? 1 : (b > 64 ? 64 : b);

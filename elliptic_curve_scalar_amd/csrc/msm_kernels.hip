@@ -702,19 +702,18 @@ __device__ __forceinline__ void block_quad_sum(xyzz acc, xyzz_st* lds, xyzz_st* 
 }
 
 // Running sums and the first tree pass in one launch: block b of window j takes segments
-// [b chunk, (b + 1) chunk) of the window's nseg (chunk = ceil(nseg / nblk)), one quad
-// per segment (64 quads striding over them), and writes their sum to out[j nblk + b].
+// [64 b, 64 b + 64) of the window's nseg, one per quad, and writes their sum to
+// out[j nblk + b] (nblk = ceil(nseg / 64); nseg <= 4096 for every c, so a window needs
+// at most 64 blocks).
 __global__ void __launch_bounds__(256) k_rsum_tree(const xyzz_st* __restrict__ bsum, uint32_t c,
                                                    uint32_t nwin, uint32_t seg_len, uint32_t nseg,
                                                    uint32_t nblk, xyzz_st* __restrict__ out) {
   __shared__ xyzz_st lds[64];
   const uint32_t j = blockIdx.x / nblk, b = blockIdx.x % nblk, quad = threadIdx.x >> 2;
   const int q = (int)(threadIdx.x & 3u);
-  const uint32_t chunk = (nseg + nblk - 1) / nblk;
-  const uint32_t lo = b * chunk, hi = min(nseg, lo + chunk);
+  const uint32_t sg = b * 64 + quad;
   xyzz acc = xyzz_inf();
-  for (uint32_t sg = lo + quad; sg < hi; sg += 64)
-    acc = quad_add(acc, rsum_segment(bsum, c, nwin, seg_len, j, sg, q), q);
+  if (sg < nseg) acc = rsum_segment(bsum, c, nwin, seg_len, j, sg, q);
   block_quad_sum(acc, lds, out + blockIdx.x);
 }
 
@@ -986,6 +985,7 @@ hipError_t launch_level_xyzz(bool in_aff, const void* in, const uint32_t* idx, x
 hipError_t launch_reduce(const xyzz_st* bsum, uint32_t c, uint32_t nwin, uint32_t seg_len,
                          uint32_t nseg, xyzz_st* part, xyzz_st* win, hipStream_t s) {
   const uint32_t nblk = reduce_blocks(nseg);
+  if ((size_t)nblk * 64 < nseg) return hipErrorInvalidValue;  // one segment per quad
   k_rsum_tree<<<nwin * nblk, 256, 0, s>>>(bsum, c, nwin, seg_len, nseg, nblk, part);
   k_tree_sum<<<nwin, 256, 0, s>>>(part, nblk, win);
   return hipGetLastError();

@@ -145,61 +145,75 @@ __device__ __forceinline__ xyzz quad_dbl_n(const xyzz& p, uint32_t n, int q) {
   return quad_chain_end(c, p.ZZ, p.ZZZ, q);
 }
 
+// One exit: with several return statements the compiler passes the result through
+// private memory.
 __device__ __forceinline__ xyzz quad_add(const xyzz& p, const xyzz& s, int q) {
-  if (xyzz_is_inf(s)) return p;
-  if (xyzz_is_inf(p)) return s;
-  fp r = fp_mul(quad_pick(q, p.X, s.X, p.Y, s.Y), quad_pick(q, s.ZZ, p.ZZ, s.ZZZ, p.ZZZ));
-  const fp U1 = quad_from<0>(r), U2 = quad_from<1>(r);  // U1 = X1 ZZ2, U2 = X2 ZZ1
-  const fp S1 = quad_from<2>(r), S2 = quad_from<3>(r);  // S1 = Y1 ZZZ2, S2 = Y2 ZZZ1
-  const fp P = fp_sub(U2, U1), R = fp_sub(S2, S1);
-  if (fp_is_zero(P)) {
-    if (fp_is_zero(R)) return quad_dbl(p, q);
-    return xyzz_inf();
-  }
-  r = fp_mul(quad_pick(q, p.ZZ, p.ZZZ, P, R), quad_pick(q, s.ZZ, s.ZZZ, P, R));
-  const fp ZZ12 = quad_from<0>(r), ZZZ12 = quad_from<1>(r);
-  const fp PP = quad_from<2>(r), RR = quad_from<3>(r);
-  r = fp_mul(quad_pick(q, P, U1, ZZ12, P), PP);         // PPP, Q = U1 PP, ZZ3
-  const fp PPP = quad_from<0>(r), Qv = quad_from<1>(r);
   xyzz o;
-  o.ZZ = quad_from<2>(r);
-  o.X = fp_sub(fp_sub(fp_sub(RR, PPP), Qv), Qv);
-  r = fp_mul(quad_pick(q, ZZZ12, S1, R, ZZZ12), quad_pick(q, PPP, PPP, fp_sub(Qv, o.X), PPP));
-  o.ZZZ = quad_from<0>(r);
-  o.Y = fp_sub(quad_from<2>(r), quad_from<1>(r));       // R (Q - X3) - S1 PPP
+  if (xyzz_is_inf(s)) {
+    o = p;
+  } else if (xyzz_is_inf(p)) {
+    o = s;
+  } else {
+    fp r = fp_mul(quad_pick(q, p.X, s.X, p.Y, s.Y), quad_pick(q, s.ZZ, p.ZZ, s.ZZZ, p.ZZZ));
+    const fp U1 = quad_from<0>(r), U2 = quad_from<1>(r);  // U1 = X1 ZZ2, U2 = X2 ZZ1
+    const fp S1 = quad_from<2>(r), S2 = quad_from<3>(r);  // S1 = Y1 ZZZ2, S2 = Y2 ZZZ1
+    const fp P = fp_sub(U2, U1), R = fp_sub(S2, S1);
+    if (fp_is_zero(P)) {
+      if (fp_is_zero(R)) o = quad_dbl(p, q);
+      else o = xyzz_inf();
+    } else {
+      r = fp_mul(quad_pick(q, p.ZZ, p.ZZZ, P, R), quad_pick(q, s.ZZ, s.ZZZ, P, R));
+      const fp ZZ12 = quad_from<0>(r), ZZZ12 = quad_from<1>(r);
+      const fp PP = quad_from<2>(r), RR = quad_from<3>(r);
+      r = fp_mul(quad_pick(q, P, U1, ZZ12, P), PP);         // PPP, Q = U1 PP, ZZ3
+      const fp PPP = quad_from<0>(r), Qv = quad_from<1>(r);
+      o.ZZ = quad_from<2>(r);
+      o.X = fp_sub(fp_sub(fp_sub(RR, PPP), Qv), Qv);
+      r = fp_mul(quad_pick(q, ZZZ12, S1, R, ZZZ12), quad_pick(q, PPP, PPP, fp_sub(Qv, o.X), PPP));
+      o.ZZZ = quad_from<0>(r);
+      o.Y = fp_sub(quad_from<2>(r), quad_from<1>(r));       // R (Q - X3) - S1 PPP
+    }
+  }
   return o;
 }
 
 // P + Q for two affine points (mmadd-2008-s), quad-cooperative: 3 rounds.
 __device__ __forceinline__ xyzz quad_add_aa(const aff& p, const aff& s, int q) {
-  if (aff_is_inf(s)) return xyzz_from_aff(p);
-  if (aff_is_inf(p)) return xyzz_from_aff(s);
-  const fp P = fp_sub(s.x, p.x), R = fp_sub(s.y, p.y);
-  if (fp_is_zero(P)) {
-    if (fp_is_zero(R)) return quad_dbl(xyzz_from_aff(p), q);
-    return xyzz_inf();
-  }
-  fp r = fp_mul(quad_pick(q, P, R, P, R), quad_pick(q, P, R, P, R));  // PP, RR
-  const fp PP = quad_from<0>(r), RR = quad_from<1>(r);
-  r = fp_mul(quad_pick(q, P, p.x, P, p.x), PP);                        // PPP, Q
-  const fp PPP = quad_from<0>(r), Qv = quad_from<1>(r);
   xyzz o;
-  o.X = fp_sub(fp_sub(fp_sub(RR, PPP), Qv), Qv);
-  r = fp_mul(quad_pick(q, R, p.y, R, p.y), quad_pick(q, fp_sub(Qv, o.X), PPP, fp_sub(Qv, o.X), PPP));
-  o.Y = fp_sub(quad_from<0>(r), quad_from<1>(r));                      // R (Q - X3) - Y1 PPP
-  o.ZZ = PP;
-  o.ZZZ = PPP;
+  if (aff_is_inf(s)) {
+    o = xyzz_from_aff(p);
+  } else if (aff_is_inf(p)) {
+    o = xyzz_from_aff(s);
+  } else {
+    const fp P = fp_sub(s.x, p.x), R = fp_sub(s.y, p.y);
+    if (fp_is_zero(P)) {
+      if (fp_is_zero(R)) o = quad_dbl(xyzz_from_aff(p), q);
+      else o = xyzz_inf();
+    } else {
+      fp r = fp_mul(quad_pick(q, P, R, P, R), quad_pick(q, P, R, P, R));  // PP, RR
+      const fp PP = quad_from<0>(r), RR = quad_from<1>(r);
+      r = fp_mul(quad_pick(q, P, p.x, P, p.x), PP);                        // PPP, Q
+      const fp PPP = quad_from<0>(r), Qv = quad_from<1>(r);
+      o.X = fp_sub(fp_sub(fp_sub(RR, PPP), Qv), Qv);
+      r = fp_mul(quad_pick(q, R, p.y, R, p.y), quad_pick(q, fp_sub(Qv, o.X), PPP, fp_sub(Qv, o.X), PPP));
+      o.Y = fp_sub(quad_from<0>(r), quad_from<1>(r));                      // R (Q - X3) - Y1 PPP
+      o.ZZ = PP;
+      o.ZZZ = PPP;
+    }
+  }
   return o;
 }
 
 // k * P for a small non-negative k (MSB-first double-and-add), quad-cooperative.
 __device__ __forceinline__ xyzz quad_mul_small(const xyzz& p, uint32_t k, int q) {
-  if (k == 0) return xyzz_inf();
-  const int top = 31 - __clz(k);
-  xyzz acc = p;
-  for (int b = top - 1; b >= 0; b--) {
-    acc = quad_dbl(acc, q);
-    if ((k >> b) & 1u) acc = quad_add(acc, p, q);
+  xyzz acc = xyzz_inf();
+  if (k != 0) {
+    const int top = 31 - __clz(k);
+    acc = p;
+    for (int b = top - 1; b >= 0; b--) {
+      acc = quad_dbl(acc, q);
+      if ((k >> b) & 1u) acc = quad_add(acc, p, q);
+    }
   }
   return acc;
 }
