@@ -207,11 +207,22 @@ __global__ void __launch_bounds__(256) k_chunk_scan(uint32_t* __restrict__ hist_
   const uint32_t H = 1u << (c - 1);
   if (t >= nwin * H) return;
   const uint32_t j = t >> (c - 1), slot = t & (H - 1);
+  uint32_t* const col = hist_blk + (size_t)j * nchunk * H + slot;  // chunk ch at col[ch H]
   uint32_t run = 0;
-  for (uint32_t ch = 0; ch < nchunk; ch++) {
-    uint32_t* p = hist_blk + ((size_t)j * nchunk + ch) * H + slot;
-    const uint32_t v = *p;
-    *p = run;
+  uint32_t ch = 0;
+  for (; ch + 8 <= nchunk; ch += 8) {  // eight loads in flight, then the running sum
+    uint32_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; e++) v[e] = col[(size_t)(ch + e) * H];
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      col[(size_t)(ch + e) * H] = run;
+      run += v[e];
+    }
+  }
+  for (; ch < nchunk; ch++) {
+    const uint32_t v = col[(size_t)ch * H];
+    col[(size_t)ch * H] = run;
     run += v;
   }
   counts[t] = run;
