@@ -278,9 +278,8 @@ int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scala
   PhaseMark ph_sort(ctx, st, PH_SORT);
   HIP_TRY(launch_fill((uint32_t*)stats, sizeof(msm_stats) / 4, 0, st));
   HIP_TRY(launch_glv_prep((const g1a*)d_points, d_scalars, n32, pts2, halfs, stats, st));
-  HIP_TRY(launch_hist(halfs, m32, c32, L.nwin, L.chunk, L.nchunk, hist_blk, counts, rank, st));
+  HIP_TRY(launch_hist(halfs, m32, c32, L.nwin, L.chunk, L.nchunk, hist_blk, counts, rank, stats, st));
   HIP_TRY(launch_scan(counts, L.K, -1, 1, block_sums, offsets, L.K + 1, nullptr, st));
-  HIP_TRY(launch_stats(counts, L.K, stats, st));
   HIP_TRY(hipMemcpyAsync(ctx->host_stats, stats, sizeof(msm_stats), hipMemcpyDeviceToHost, st));
   HIP_TRY(hipEventRecord(ctx->plan_ready, st));
   HIP_TRY(launch_scatter(halfs, m32, c32, L.nwin, L.chunk, L.nchunk, offsets, hist_blk, rank,

@@ -34,10 +34,11 @@ hipError_t launch_fill(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
 hipError_t launch_glv_prep(const g1a* points, const uint32_t* scalars, uint32_t n, g1a* pts2,
                            uint32_t* halfs, msm_stats* st, hipStream_t s);
 // Counting pass: per (chunk of half-scalars, window) LDS histograms into hist_blk
-// (nwin nchunk 2^(c-1) words), turned into per-chunk prefixes, and the bucket counts.
+// (nwin nchunk 2^(c-1) words), turned into per-chunk prefixes, the bucket counts, and
+// the plan statistics in st (largest bucket, total, pair adds per level).
 hipError_t launch_hist(const uint32_t* halfs, uint32_t m, uint32_t c, uint32_t nwin,
                        uint32_t chunk, uint32_t nchunk, uint32_t* hist_blk, uint32_t* counts,
-                       uint32_t* rank, hipStream_t s);
+                       uint32_t* rank, msm_stats* st, hipStream_t s);
 hipError_t launch_scatter(const uint32_t* halfs, uint32_t m, uint32_t c, uint32_t nwin,
                           uint32_t chunk, uint32_t nchunk, const uint32_t* offsets,
                           const uint32_t* hist_blk, const uint32_t* rank, uint32_t* sorted_idx,
@@ -55,7 +56,6 @@ inline uint32_t scan_blocks(uint32_t n) {
 hipError_t launch_scan(const uint32_t* counts, uint32_t n, int level0, int nlev,
                        uint32_t* block_sums, uint32_t* out, size_t out_stride,
                        const uint32_t* max_count, hipStream_t s);
-hipError_t launch_stats(const uint32_t* counts, uint32_t K, msm_stats* st, hipStream_t s);
 hipError_t launch_bucket_init(const uint32_t* counts, const uint32_t* offsets, uint32_t K,
                               const uint32_t* sorted_idx, const g1a* points, xyzz_st* bsum,
                               hipStream_t s);

@@ -4,9 +4,8 @@
 // half-scalars, 2^(c-1) buckets per window, digit 0 dropped since it adds nothing):
 //   k_glv_prep    scalar -> two half-scalars below 2^127; points [P, phi(P)]
 //   k_hist_tile   per (chunk of half-scalars, window): LDS histogram, rank per entry
-//   k_chunk_scan  per bucket: prefix over the chunks, bucket count
+//   k_chunk_scan  per bucket: prefix over the chunks, bucket count; plan statistics
 //   k_scan_*      exclusive scan of the counts -> bucket offsets
-//   k_stats       largest bucket, number of pair adds at every pair-tree level
 //   -- the plan is copied to the host --
 //   k_scatter     point indices into per-bucket lists (sorted_idx)
 //   k_bucket_init buckets of size 0 / 1 are final at once
@@ -198,34 +197,86 @@ __global__ void __launch_bounds__(1024) k_hist_tile(const uint32_t* __restrict__
   for (uint32_t k = threadIdx.x; k < H; k += blockDim.x) out[k] = lds_hist[k];
 }
 
-// Per bucket (thread t = j 2^(c-1) + slot): the per-chunk counts become each chunk's
-// exclusive prefix within the bucket, and counts[t] the bucket's total.
-__global__ void __launch_bounds__(256) k_chunk_scan(uint32_t* __restrict__ hist_blk, uint32_t c,
-                                                    uint32_t nwin, uint32_t nchunk,
-                                                    uint32_t* __restrict__ counts) {
-  const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
-  const uint32_t H = 1u << (c - 1);
-  if (t >= nwin * H) return;
-  const uint32_t j = t >> (c - 1), slot = t & (H - 1);
-  uint32_t* const col = hist_blk + (size_t)j * nchunk * H + slot;  // chunk ch at col[ch H]
-  uint32_t run = 0;
-  uint32_t ch = 0;
-  for (; ch + 8 <= nchunk; ch += 8) {  // eight loads in flight, then the running sum
-    uint32_t v[8];
+// Entries of a bucket of cnt entries at pair-tree level `level`: ceil(cnt / 2^level).
+__device__ __forceinline__ uint32_t level_count(uint32_t cnt, int level) {
+  return (uint32_t)(((uint64_t)cnt + (1ull << level) - 1) >> level);
+}
+
+// ------------------------------------------------------------------ stats
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
 #pragma unroll
-    for (int e = 0; e < 8; e++) v[e] = col[(size_t)(ch + e) * H];
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 #pragma unroll
-    for (int e = 0; e < 8; e++) {
-      col[(size_t)(ch + e) * H] = run;
-      run += v[e];
+  for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor(v, off, 64));
+  return v;
+}
+
+// Largest bucket, total entries and the pair adds of every pair-tree level, from one
+// bucket count per thread (0 for threads past the last bucket): reduced in registers,
+// then over the block's four waves through LDS, then one atomic per value and block.
+// Every thread of the 256-thread block must call it.
+__device__ __forceinline__ void block_stats(uint32_t cnt, msm_stats* st) {
+  __shared__ uint32_t red[4][MAX_LEVELS + 2];
+  const uint32_t wave = threadIdx.x >> 6;
+  const bool lead = (threadIdx.x & 63) == 0;
+  const uint32_t mx = wave_max(cnt), tot = wave_sum(cnt);
+  if (lead) {
+    red[wave][MAX_LEVELS] = mx;
+    red[wave][MAX_LEVELS + 1] = tot;
+  }
+#pragma unroll
+  for (int l = 0; l < MAX_LEVELS; l++) {
+    const uint32_t v = wave_sum(level_count(cnt, l) >> 1);
+    if (lead) red[wave][l] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < MAX_LEVELS + 2) {
+    const uint32_t i = threadIdx.x;
+    const uint32_t a = red[0][i], b = red[1][i], c = red[2][i], d = red[3][i];
+    if (i == MAX_LEVELS) {
+      atomicMax(&st->max_count, max(max(a, b), max(c, d)));
+    } else {
+      const uint32_t v = a + b + c + d;
+      if (v) atomicAdd(i == MAX_LEVELS + 1 ? &st->total : &st->pairs[i], v);
     }
   }
-  for (; ch < nchunk; ch++) {
-    const uint32_t v = col[(size_t)ch * H];
-    col[(size_t)ch * H] = run;
-    run += v;
+}
+
+// Per bucket (thread t = j 2^(c-1) + slot): the per-chunk counts become each chunk's
+// exclusive prefix within the bucket, counts[t] the bucket's total, and the block's
+// buckets go into the plan statistics (block_stats).
+__global__ void __launch_bounds__(256) k_chunk_scan(uint32_t* __restrict__ hist_blk, uint32_t c,
+                                                    uint32_t nwin, uint32_t nchunk,
+                                                    uint32_t* __restrict__ counts, msm_stats* st) {
+  const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint32_t H = 1u << (c - 1);
+  uint32_t run = 0;
+  if (t < nwin * H) {
+    const uint32_t j = t >> (c - 1), slot = t & (H - 1);
+    uint32_t* const col = hist_blk + (size_t)j * nchunk * H + slot;  // chunk ch at col[ch H]
+    uint32_t ch = 0;
+    for (; ch + 8 <= nchunk; ch += 8) {  // eight loads in flight, then the running sum
+      uint32_t v[8];
+#pragma unroll
+      for (int e = 0; e < 8; e++) v[e] = col[(size_t)(ch + e) * H];
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        col[(size_t)(ch + e) * H] = run;
+        run += v[e];
+      }
+    }
+    for (; ch < nchunk; ch++) {
+      const uint32_t v = col[(size_t)ch * H];
+      col[(size_t)ch * H] = run;
+      run += v;
+    }
+    counts[t] = run;
   }
-  counts[t] = run;
+  block_stats(run, st);
 }
 
 // Bucket lists hold point indices with the sign of (digit x half-scalar) in bit 31,
@@ -269,10 +320,6 @@ __global__ void __launch_bounds__(256) k_scatter(const uint32_t* __restrict__ ha
 // ------------------------------------------------------------------ scan
 // Value scanned for bucket k: its count (level < 0), or the number of pair adds
 // it has at pair-tree level `level`: floor(ceil(count / 2^level) / 2).
-__device__ __forceinline__ uint32_t level_count(uint32_t cnt, int level) {
-  return (uint32_t)(((uint64_t)cnt + (1ull << level) - 1) >> level);
-}
-
 __device__ __forceinline__ uint32_t scan_value(const uint32_t* counts, uint32_t k, uint32_t n,
                                                int level) {
   if (k >= n) return 0;
@@ -370,60 +417,6 @@ __global__ void __launch_bounds__(256) k_scan_down(const uint32_t* __restrict__ 
     run += v[e];
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) out[n] = block_sums[nb];
-}
-
-// ------------------------------------------------------------------ stats
-__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
-__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = max(v, (uint32_t)__shfl_xor(v, off, 64));
-  return v;
-}
-
-__global__ void __launch_bounds__(256) k_stats(const uint32_t* __restrict__ counts, uint32_t K,
-                                               msm_stats* st) {
-  __shared__ uint32_t red[4][MAX_LEVELS + 2];
-  uint32_t mx = 0, tot = 0;
-  uint32_t pt[MAX_LEVELS];
-#pragma unroll
-  for (int l = 0; l < MAX_LEVELS; l++) pt[l] = 0;
-  for (uint32_t k = blockIdx.x * blockDim.x + threadIdx.x; k < K; k += gridDim.x * blockDim.x) {
-    uint32_t c = counts[k];
-    mx = max(mx, c);
-    tot += c;
-#pragma unroll
-    for (int l = 0; l < MAX_LEVELS; l++) pt[l] += level_count(c, l) >> 1;
-  }
-  // wave reductions, then the block's four waves through LDS, then one atomic each
-  const uint32_t wave = threadIdx.x >> 6;
-  const bool lead = (threadIdx.x & 63) == 0;
-  mx = wave_max(mx);
-  tot = wave_sum(tot);
-  if (lead) {
-    red[wave][MAX_LEVELS] = mx;
-    red[wave][MAX_LEVELS + 1] = tot;
-  }
-#pragma unroll
-  for (int l = 0; l < MAX_LEVELS; l++) {
-    uint32_t v = wave_sum(pt[l]);
-    if (lead) red[wave][l] = v;
-  }
-  __syncthreads();
-  if (threadIdx.x < MAX_LEVELS + 2) {
-    const uint32_t i = threadIdx.x;
-    uint32_t a = red[0][i], b = red[1][i], c = red[2][i], d = red[3][i];
-    if (i == MAX_LEVELS) {
-      atomicMax(&st->max_count, max(max(a, b), max(c, d)));
-    } else {
-      uint32_t v = a + b + c + d;
-      if (v) atomicAdd(i == MAX_LEVELS + 1 ? &st->total : &st->pairs[i], v);
-    }
-  }
 }
 
 // ------------------------------------------------------------------ buckets
@@ -899,7 +892,7 @@ hipError_t launch_glv_prep(const g1a* points, const uint32_t* scalars, uint32_t 
 
 hipError_t launch_hist(const uint32_t* halfs, uint32_t m, uint32_t c, uint32_t nwin,
                        uint32_t chunk, uint32_t nchunk, uint32_t* hist_blk, uint32_t* counts,
-                       uint32_t* rank, hipStream_t s) {
+                       uint32_t* rank, msm_stats* st, hipStream_t s) {
   const size_t lds = ((size_t)1 << (c - 1)) * 4;
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)k_hist_tile,
@@ -908,7 +901,7 @@ hipError_t launch_hist(const uint32_t* halfs, uint32_t m, uint32_t c, uint32_t n
   }
   k_hist_tile<<<dim3(nchunk, nwin), 1024, lds, s>>>(halfs, m, c, nwin, chunk, nchunk, hist_blk, rank);
   const uint32_t K = nwin << (c - 1);
-  k_chunk_scan<<<grid_for(K, 256), 256, 0, s>>>(hist_blk, c, nwin, nchunk, counts);
+  k_chunk_scan<<<grid_for(K, 256), 256, 0, s>>>(hist_blk, c, nwin, nchunk, counts, st);
   return hipGetLastError();
 }
 
@@ -937,12 +930,6 @@ hipError_t launch_scan(const uint32_t* counts, uint32_t n, int level0, int nlev,
   return hipGetLastError();
 }
 
-hipError_t launch_stats(const uint32_t* counts, uint32_t K, msm_stats* st, hipStream_t s) {
-  unsigned g = grid_for(K, 256);
-  if (g > 1024) g = 1024;
-  k_stats<<<g, 256, 0, s>>>(counts, K, st);
-  return hipGetLastError();
-}
 
 hipError_t launch_bucket_init(const uint32_t* counts, const uint32_t* offsets, uint32_t K,
                               const uint32_t* sorted_idx, const g1a* points, xyzz_st* bsum,
