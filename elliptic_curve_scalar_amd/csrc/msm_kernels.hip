@@ -670,6 +670,21 @@ __global__ void __launch_bounds__(128) k_level_xyzz_q(const void* __restrict__ i
 }
 
 // ------------------------------------------------------------------ reduction
+// XYZZ point of lane (this lane xor `mask`), for a mask that is a multiple of 4 (a whole
+// other quad); ds_bpermute, no LDS storage.
+__device__ __forceinline__ xyzz xyzz_shfl_xor(const xyzz& a, int mask) {
+  xyzz r;
+  const int src = (((int)(threadIdx.x & 63)) ^ mask) << 2;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    r.X.v[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)a.X.v[i]);
+    r.Y.v[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)a.Y.v[i]);
+    r.ZZ.v[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)a.ZZ.v[i]);
+    r.ZZZ.v[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)a.ZZZ.v[i]);
+  }
+  return r;
+}
+
 // Window j has 2^(c-1) bucket slots; slot b holds points whose digit has magnitude
 // floor(b / f) + 1 (f = window_spread), so W_j = sum_b (floor(b / f) + 1) B_b. Segment s
 // covers slots [lo, hi). Running from the top slot down, T sums the slots so far and R
@@ -721,17 +736,19 @@ __global__ void __launch_bounds__(256) k_rsum_tree(const xyzz_st* __restrict__ b
   block_quad_sum(acc, lds, out + blockIdx.x);
 }
 
-// Sums of groups of n consecutive XYZZ points, one block per group (64 quads striding
-// over the group, then the LDS tree): the second pass, from the partials of
-// k_rsum_tree to the window sums.
-__global__ void __launch_bounds__(256) k_tree_sum(const xyzz_st* __restrict__ in, uint32_t n,
-                                                  xyzz_st* __restrict__ out) {
-  __shared__ xyzz_st lds[64];
+// Sums of groups of n consecutive XYZZ points, one wavefront per group: quad g adds
+// items g, g + 16, ..., then a butterfly over the 16 quads (ds_bpermute, four additions
+// deep) leaves the sum in every quad. The second pass, from the partials of k_rsum_tree
+// to the window sums.
+__global__ void __launch_bounds__(64) k_tree_sum(const xyzz_st* __restrict__ in, uint32_t n,
+                                                 xyzz_st* __restrict__ out) {
   const uint32_t g = blockIdx.x, quad = threadIdx.x >> 2;
   const int q = (int)(threadIdx.x & 3u);
   xyzz acc = xyzz_inf();
-  for (uint32_t i = quad; i < n; i += 64) acc = quad_add(acc, xyzz_load(in + (size_t)g * n + i), q);
-  block_quad_sum(acc, lds, out + g);
+  for (uint32_t i = quad; i < n; i += 16) acc = quad_add(acc, xyzz_load(in + (size_t)g * n + i), q);
+#pragma unroll
+  for (int m = 4; m < 64; m <<= 1) acc = quad_add(acc, xyzz_shfl_xor(acc, m), q);
+  if (threadIdx.x == 0) xyzz_store(out + g, acc);
 }
 
 // ---- window combine ----------------------------------------------------------------
@@ -740,21 +757,6 @@ __global__ void __launch_bounds__(256) k_tree_sum(const xyzz_st* __restrict__ in
 // of doublings with one round of lookahead costs 2.5 product latencies per doubling,
 // an addition 4. Every quad computes its own chain, so every branch is uniform within
 // a quad.
-
-// XYZZ point of lane (this lane xor `mask`), for a mask that is a multiple of 4 (a whole
-// other quad); ds_bpermute, no LDS storage.
-__device__ __forceinline__ xyzz xyzz_shfl_xor(const xyzz& a, int mask) {
-  xyzz r;
-  const int src = (((int)(threadIdx.x & 63)) ^ mask) << 2;
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    r.X.v[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)a.X.v[i]);
-    r.Y.v[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)a.Y.v[i]);
-    r.ZZ.v[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)a.ZZ.v[i]);
-    r.ZZZ.v[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)a.ZZZ.v[i]);
-  }
-  return r;
-}
 
 // Q = sum_j 2^(c j) W_j, then to affine. Two wavefronts: wave 0 doubles the top window's
 // sum c (W - 1) times. In wave 1, quad g doubles W_g c g times (at most c (W - 2)), and a
@@ -985,7 +987,7 @@ hipError_t launch_reduce(const xyzz_st* bsum, uint32_t c, uint32_t nwin, uint32_
   const uint32_t nblk = reduce_blocks(nseg);
   if ((size_t)nblk * 64 < nseg) return hipErrorInvalidValue;  // one segment per quad
   k_rsum_tree<<<nwin * nblk, 256, 0, s>>>(bsum, c, nwin, seg_len, nseg, nblk, part);
-  k_tree_sum<<<nwin, 256, 0, s>>>(part, nblk, win);
+  k_tree_sum<<<nwin, 64, 0, s>>>(part, nblk, win);
   return hipGetLastError();
 }
 
