@@ -102,3 +102,31 @@ def test_batched_binary_gcd_model():
         assert v * y % ref.P == 1
     # y = 0 never converges: the device takes the Fermat path (0 -> 0)
     assert not _bingcd(0, batches)[0]
+
+
+def test_batches_after_convergence_leave_v_unchanged():
+    """The device stops once every lane has a = 0: a later batch only halves a (factors
+    (1, 0) and (0, 2^30)), so b and v, the inverse, must come out of it unchanged."""
+    P = ref.P
+    rng = random.Random(78)
+    inv2k = pow(2, -30, P)
+    for y in [rng.randrange(1, P) for _ in range(60)] + [1, 2, P - 1]:
+        a, b, u, v = y, P, 1, 0
+        stopped = None
+        for it in range(18):
+            f0, g0, f1, g1 = _batch(*_approx(a, b), 30)
+            na, nb = f0 * a + g0 * b, f1 * a + g1 * b
+            if na < 0:
+                na, f0, g0 = -na, -f0, -g0
+            if nb < 0:
+                nb, f1, g1 = -nb, -f1, -g1
+            if a == 0:
+                assert (f0, g0, f1, g1) == (1, 0, 0, 1 << 30)
+            a, b = na >> 30, nb >> 30
+            u, v = (f0 * u + g0 * v) * inv2k % P, (f1 * u + g1 * v) * inv2k % P
+            if stopped is None and a == 0:
+                stopped = (it, b, v)
+            elif stopped is not None:
+                assert (b, v) == stopped[1:]  # unchanged by every later batch
+        assert stopped is not None and stopped[0] < _define("BG_BATCHES")
+        assert stopped[1] == 1 and stopped[2] * y % P == 1
