@@ -246,4 +246,7 @@ __device__ __forceinline__ fp fp_inv_bingcd(const fp& x) {
   return r;
 }
 
+// The field inverse every kernel uses.
+__device__ __forceinline__ fp fp_inv(const fp& x) { return fp_inv_bingcd(x); }
+
 }  // namespace msmk

@@ -13,7 +13,7 @@
 // The point at infinity is (0, 0) in affine storage (not on the curve, since
 // 0 != 0^3 + 3) and ZZ = ZZZ = 0 in XYZZ.
 #pragma once
-#include "inv.hpp"
+#include "bingcd.hpp"
 
 namespace msmk {
 
@@ -66,6 +66,16 @@ __device__ __forceinline__ aff aff_inf() {
   r.x = fp_zero();
   r.y = fp_zero();
   return r;
+}
+
+// Coordinates below p, and y^2 = x^3 + 3 (both sides in Montgomery form), or the
+// infinity encoding (0, 0).
+__device__ __forceinline__ bool aff_valid(const aff& a) {
+  if (aff_is_inf(a)) return true;
+  if (!fp_is_reduced(a.x) || !fp_is_reduced(a.y)) return false;
+  const fp one = fp_one();
+  const fp b = fp_add(fp_add(one, one), one);  // 3 in Montgomery form
+  return fp_eq(fp_sqr(a.y), fp_add(fp_mul(fp_sqr(a.x), a.x), b));
 }
 
 __device__ __forceinline__ xyzz xyzz_inf() {

@@ -11,10 +11,9 @@
 //   * the product is coarsely integrated operand scanning with 32x32->64
 //     multiply-adds (v_mad_u64_u32 on gfx950, issued at half the rate of plain 32-bit
 //     ALU ops); p < 2^254 keeps every partial sum inside 288 bits and the result
-//     before the final subtraction below 2p. A carry-free form on nine 29-bit limbs
-//     is kept behind MSMK_MONT29 (off);
+//     before the final subtraction below 2p;
 //   * Fermat's x^(p-2) (fp_inv_fermat) is here; the inverse the kernels use is the
-//     binary GCD of bingcd.hpp (Fermat remains its fallback), selected in inv.hpp.
+//     binary GCD of bingcd.hpp (Fermat remains its fallback).
 //
 // Everything is branch-free except where noted, so a wavefront never diverges on
 // field values.
@@ -90,6 +89,14 @@ __device__ __forceinline__ bool fp_eq(const fp& a, const fp& b) {
   return x == 0;
 }
 
+// a < p (a canonical element).
+__device__ __forceinline__ bool fp_is_reduced(const fp& a) {
+  uint32_t borrow = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) (void)__builtin_subc(a.v[i], p_limb(i), borrow, &borrow);
+  return borrow != 0;
+}
+
 // r = t - p if t >= p else t, for t < 2^256 given as 8 limbs.
 __device__ __forceinline__ fp fp_reduce_once(const fp& t) {
   // 32-bit borrow chain (clang's subtract-with-borrow builtin, v_sub_co / v_subb_co):
@@ -146,7 +153,7 @@ __device__ __forceinline__ fp fp_half(const fp& a) {
 }
 
 // Montgomery product a * b * 2^-256 mod p, coarsely integrated operand scanning on
-// 32-bit limbs (the default product; see MSMK_MONT29 below).
+// 32-bit limbs.
 // 64-bit value kept whole through code generation: the empty asm stops the compiler
 // from re-associating a * b + (t + c) into (a * b + t) + c, which costs two 64-bit
 // adds and the register moves that widen t and c, where the form below costs one
@@ -202,127 +209,9 @@ __device__ __forceinline__ fp fp_mul_cios(const fp& a, const fp& b) {
   return fp_reduce_once(r);
 }
 
-// ---- Montgomery product on nine 29-bit limbs ----------------------------------
-// Operands are split into 29-bit limbs so that every partial product (< 2^58, or
-// 2^59 for the doubled cross terms of a square) is one v_mad_u64_u32 into a 64-bit
-// column accumulator with no carry handling: a column never sums more than 18 such
-// products, which stays below 2^63. Reduction by R = 2^256 runs as eight 29-bit
-// digit steps plus one 24-bit step (8 * 29 + 24 = 256), so the result is the usual
-// a * b * 2^-256 mod p and the 8 x 32-bit interchange form is kept.
-
-#define MSM_P29_0 0x187cfd47u
-#define MSM_P29_1 0x010460b6u
-#define MSM_P29_2 0x1c72a34fu
-#define MSM_P29_3 0x02d522d0u
-#define MSM_P29_4 0x1585d978u
-#define MSM_P29_5 0x02db40c0u
-#define MSM_P29_6 0x00a6e141u
-#define MSM_P29_7 0x0e5c2634u
-#define MSM_P29_8 0x0030644eu
-#define MSM_PINV29 0x04866389u  // -p^{-1} mod 2^29
-#define MSM_PINV24 0x00866389u  // -p^{-1} mod 2^24
-#define MSM_M29 0x1fffffffu
-
-__device__ __forceinline__ uint32_t p29_limb(int i) {
-  switch (i) {
-    case 0: return MSM_P29_0;
-    case 1: return MSM_P29_1;
-    case 2: return MSM_P29_2;
-    case 3: return MSM_P29_3;
-    case 4: return MSM_P29_4;
-    case 5: return MSM_P29_5;
-    case 6: return MSM_P29_6;
-    case 7: return MSM_P29_7;
-    default: return MSM_P29_8;
-  }
-}
-
-// r[k] = bits [29k, 29k + 29) of a (a < 2^256).
-__device__ __forceinline__ void split29(const fp& a, uint32_t r[9]) {
-#pragma unroll
-  for (int k = 0; k < 9; k++) {
-    const int o = 29 * k, w = o >> 5, sh = o & 31;
-    const uint64_t pair = ((uint64_t)(w + 1 < 8 ? a.v[w + 1] : 0u) << 32) | a.v[w];
-    r[k] = (uint32_t)(pair >> sh) & MSM_M29;
-  }
-}
-
-template <bool SQR>
-__device__ __forceinline__ fp mont29(const fp& a, const fp& b) {
-  uint32_t x[9], y[9];
-  split29(a, x);
-  if (SQR) {
-#pragma unroll
-    for (int k = 0; k < 9; k++) y[k] = x[k] << 1;
-  } else {
-    split29(b, y);
-  }
-  uint64_t T[18];
-#pragma unroll
-  for (int k = 0; k < 18; k++) T[k] = 0;
-  if (SQR) {
-#pragma unroll
-    for (int i = 0; i < 9; i++) {
-      T[2 * i] += (uint64_t)x[i] * x[i];
-#pragma unroll
-      for (int j = i + 1; j < 9; j++) T[i + j] += (uint64_t)x[i] * y[j];
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 9; i++)
-#pragma unroll
-      for (int j = 0; j < 9; j++) T[i + j] += (uint64_t)x[i] * y[j];
-  }
-  // eight 29-bit reduction digits
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const uint32_t m = ((uint32_t)T[i] * MSM_PINV29) & MSM_M29;
-#pragma unroll
-    for (int j = 0; j < 9; j++) T[i + j] += (uint64_t)m * p29_limb(j);
-    T[i + 1] += T[i] >> 29;
-  }
-  // last digit: 24 bits, completing the division by 2^256
-  {
-    const uint32_t m = ((uint32_t)T[8] * MSM_PINV24) & 0x00ffffffu;
-#pragma unroll
-    for (int j = 0; j < 9; j++) T[8 + j] += (uint64_t)m * p29_limb(j);
-  }
-  // normalise columns 8..17 into 29-bit limbs N; the result is (sum N_k 2^29k) >> 24
-  uint32_t N[10];
-#pragma unroll
-  for (int k = 0; k < 9; k++) {
-    N[k] = (uint32_t)T[8 + k] & MSM_M29;
-    T[9 + k] += T[8 + k] >> 29;
-  }
-  N[9] = (uint32_t)T[17];
-  fp r;
-#pragma unroll
-  for (int w = 0; w < 8; w++) {
-    const int b = 32 * w + 24, k0 = b / 29, r0 = b % 29;
-    uint32_t word = (N[k0] >> r0) | (N[k0 + 1] << (29 - r0));
-    if (r0 > 26) word |= N[k0 + 2] << (58 - r0);
-    r.v[w] = word;
-  }
-  // inputs < p give a result < 2p
-  return fp_reduce_once(r);
-}
-
-// MSMK_MONT29 selects the 29-bit product for fp_mul / fp_sqr. It is off: with it on,
-// the first GPU field test stalled and no cause has been found yet (the same code
-// matches Python integers bit for bit in a host build under ASan and UBSan).
-#ifndef MSMK_MONT29
-#define MSMK_MONT29 0
-#endif
-
-#if MSMK_MONT29
 // Montgomery product a * b * 2^-256 mod p; inputs and output fully reduced.
-__device__ __forceinline__ fp fp_mul(const fp& a, const fp& b) { return mont29<false>(a, b); }
-// Montgomery square, 45 limb products for a * a instead of 81.
-__device__ __forceinline__ fp fp_sqr(const fp& a) { return mont29<true>(a, a); }
-#else
 __device__ __forceinline__ fp fp_mul(const fp& a, const fp& b) { return fp_mul_cios(a, b); }
 __device__ __forceinline__ fp fp_sqr(const fp& a) { return fp_mul_cios(a, a); }
-#endif
 
 // Small constant c (< 2^32) in Montgomery form.
 __device__ __forceinline__ fp fp_from_u32(uint32_t c) {

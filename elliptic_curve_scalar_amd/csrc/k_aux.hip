@@ -1,0 +1,132 @@
+// Input generator and unit-test hooks of libmsm (gfx950): the same device code as the
+// MSM kernels, exposed for the tests and for building synthetic inputs.
+#include <hip/hip_runtime.h>
+
+#include "batch_add.hpp"
+#include "glv.hpp"
+#include "kern_util.hpp"
+
+namespace msmk {
+
+__global__ void __launch_bounds__(128) k_from_scalars(const uint32_t* __restrict__ ks, uint32_t n,
+                                                      g1a* __restrict__ out) {
+  uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  sc256 k = load_scalar(ks, i);
+  aff g;
+  g.x = fp_from_u32(1);
+  g.y = fp_from_u32(2);
+  xyzz acc = xyzz_inf();
+  for (int w = 7; w >= 0; w--) {
+    uint32_t word = k.w[w];
+    for (int b = 31; b >= 0; b--) {
+      acc = xyzz_dbl(acc);
+      if ((word >> b) & 1u) acc = xyzz_add_aff(acc, g);
+    }
+  }
+  aff_store(out + i, xyzz_to_aff(acc));
+}
+
+// ------------------------------------------------------------------ test hooks
+__device__ __forceinline__ fp fp_load_words(const uint32_t* p) {
+  fp r;
+#pragma unroll
+  for (int i = 0; i < 8; i++) r.v[i] = p[i];
+  return r;
+}
+
+__global__ void k_test_fp(int op, const uint32_t* a, const uint32_t* b, uint32_t* out, uint32_t n) {
+  uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  fp x = fp_load_words(a + 8 * (size_t)i), y = fp_zero(), r;
+  if (b) y = fp_load_words(b + 8 * (size_t)i);
+  switch (op) {
+    case 0: r = fp_mul(x, y); break;
+    case 1: r = fp_add(x, y); break;
+    case 2: r = fp_sub(x, y); break;
+    case 3: r = fp_sqr(x); break;
+    case 4: r = fp_is_zero(x) ? fp_zero() : fp_inv(x); break;
+    case 5: r = fp_mul(x, fp_r2()); break;
+    case 7: r = fp_inv_fermat(x); break;
+    case 8: r = fp_inv_bingcd(x); break;
+    default: {
+      fp one = fp_zero();
+      one.v[0] = 1;
+      r = fp_mul(x, one);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 8; k++) out[8 * (size_t)i + k] = r.v[k];
+}
+
+template <int S>
+struct PairSrc {
+  const g1a* a_;
+  const g1a* b_;
+  g1a* out;
+  uint32_t base;
+  __device__ __forceinline__ aff a(int s) const { return aff_load(a_ + base + s); }
+  __device__ __forceinline__ aff b(int s) const { return aff_load(b_ + base + s); }
+  __device__ __forceinline__ fp ax(int s) const { return fp_load_x(a_ + base + s); }
+  __device__ __forceinline__ fp bx(int s) const { return fp_load_x(b_ + base + s); }
+  __device__ __forceinline__ void put(int s, const aff& r) const { aff_store(out + base + s, r); }
+};
+
+__global__ void __launch_bounds__(128) k_test_glv(const uint32_t* __restrict__ scalars, uint32_t n,
+                                                  uint32_t* __restrict__ halfs) {
+  uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const sc256 sc = load_scalar(scalars, i);
+  uint32_t s[8], k1[4], k2[4];
+#pragma unroll
+  for (int w = 0; w < 8; w++) s[w] = sc.w[w];
+  bool bad = false;
+  glv_split(s, k1, k2, bad);
+  reinterpret_cast<uint4*>(halfs)[i] = make_uint4(k1[0], k1[1], k1[2], k1[3]);
+  reinterpret_cast<uint4*>(halfs)[n + i] = make_uint4(k2[0], k2[1], k2[2], k2[3]);
+}
+
+template <int S>
+__global__ void __launch_bounds__(256) k_test_pair_add(const g1a* a, const g1a* b, g1a* out,
+                                                       uint32_t n) {
+  uint64_t p0 = (uint64_t)(blockIdx.x * blockDim.x + threadIdx.x) * S;
+  if (p0 >= n) return;
+  int cnt = (int)min((uint64_t)S, (uint64_t)n - p0);
+  PairSrc<S> src{a, b, out, (uint32_t)p0};
+  batch_affine_add<S>(src, cnt);
+}
+
+// ------------------------------------------------------------------ launchers
+hipError_t launch_from_scalars(const uint32_t* ks, uint32_t n, g1a* out, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  k_from_scalars<<<grid_for(n, 128), 128, 0, s>>>(ks, n, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_test_fp(int op, const uint32_t* a, const uint32_t* b, uint32_t* out, uint32_t n,
+                          hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  k_test_fp<<<grid_for(n, 128), 128, 0, s>>>(op, a, b, out, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_test_glv(const uint32_t* scalars, uint32_t n, uint32_t* halfs, hipStream_t s) {
+  k_test_glv<<<grid_for(n, 128), 128, 0, s>>>(scalars, n, halfs);
+  return hipGetLastError();
+}
+
+hipError_t launch_test_pair_add(int S, const g1a* a, const g1a* b, g1a* out, uint32_t n,
+                                hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  size_t threads;
+  switch (S) {
+    case 4: threads = (n + 3) / 4; k_test_pair_add<4><<<grid_for(threads, 256), 256, 0, s>>>(a, b, out, n); break;
+    case 8: threads = (n + 7) / 8; k_test_pair_add<8><<<grid_for(threads, 256), 256, 0, s>>>(a, b, out, n); break;
+    case 16: threads = (n + 15) / 16; k_test_pair_add<16><<<grid_for(threads, 256), 256, 0, s>>>(a, b, out, n); break;
+    case 32: threads = (n + 31) / 32; k_test_pair_add<32><<<grid_for(threads, 256), 256, 0, s>>>(a, b, out, n); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace msmk

@@ -98,9 +98,12 @@ Layout plan(size_t n, int c) {
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 int check_run_args(const msm_g1_affine* pts, const uint32_t* sc, size_t n, int c, int S,
-                   const msm_g1_affine* out) {
+                   int sched, int verify, const msm_g1_affine* out) {
   if (c < 1 || c > 16) return fail(MSM_ERR_ARG, "window c must be in 1..16%s");
   if (S != 4 && S != 8 && S != 16 && S != 32) return fail(MSM_ERR_ARG, "S must be 4, 8, 16 or 32%s");
+  if (sched != MSM_SCHED_PAIR_TREE && sched != MSM_SCHED_WALKER)
+    return fail(MSM_ERR_ARG, "sched must be MSM_SCHED_PAIR_TREE (0) or MSM_SCHED_WALKER (1)%s");
+  if (verify != 0 && verify != 1) return fail(MSM_ERR_ARG, "verify must be 0 or 1%s");
   if (n > MSM_MAX_N) return fail(MSM_ERR_ARG, "n exceeds MSM_MAX_N%s");
   if ((uint64_t)2 * n * (uint64_t)num_windows(c) >= ((uint64_t)1 << 32))
     return fail(MSM_ERR_ARG, "2 n ceil(128 / c) bucket entries exceed 32-bit offsets; raise c%s");
@@ -125,8 +128,11 @@ struct msm_ctx {
   int affine_levels = 1;  // leading pair-tree levels done with batched affine adds
   void* ws = nullptr;
   size_t ws_bytes = 0;
-  msm_stats* host_stats = nullptr;  // pinned
+  msm_stats* host_stats = nullptr;  // pinned: the plan, then the result's verify flag
+  msm_g1_affine* d_result = nullptr;  // device result buffer of the synchronous msm()
   hipEvent_t plan_ready = nullptr;   // the plan's copy to host_stats has completed
+  hipEvent_t done = nullptr;         // the last kernel of the previous call has run
+  bool has_done = false;
   // phase timing: 0 off, 1 the batched-affine level kernels only, 2 every phase
   int timing = 0;
   std::vector<hipEvent_t> events;
@@ -171,83 +177,19 @@ struct PhaseMark {
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-int msm_version(void) { return 200; }
-
-const char* msm_last_error(void) { return g_err; }
-
-size_t msm_workspace_bytes(size_t n, int c, int S) {
-  (void)S;
-  if (c < 1 || c > 16 || n > MSM_MAX_N) return 0;
-  if ((uint64_t)2 * n * (uint64_t)num_windows(c) >= ((uint64_t)1 << 32)) return 0;
-  return plan(n, c).total;
-}
-
-int msm_ctx_create(int device, msm_ctx** out) {
-  if (!out) return fail(MSM_ERR_ARG, "out is NULL%s");
-  *out = nullptr;
-  int ndev = 0;
-  HIP_TRY(hipGetDeviceCount(&ndev));
-  if (device < 0 || device >= ndev) return fail(MSM_ERR_ARG, "no such device%s");
-  msm_ctx* ctx = new (std::nothrow) msm_ctx;
-  if (!ctx) return fail(MSM_ERR_OOM, "host allocation failed%s");
-  ctx->device = device;
-  HIP_TRY(hipSetDevice(device));
-  if (hipHostMalloc((void**)&ctx->host_stats, sizeof(msm_stats), hipHostMallocDefault) != hipSuccess) {
-    delete ctx;
-    return fail(MSM_ERR_OOM, "pinned host allocation failed%s");
-  }
-  if (hipEventCreateWithFlags(&ctx->plan_ready, hipEventDisableTiming) != hipSuccess) {
-    (void)hipHostFree(ctx->host_stats);
-    delete ctx;
-    return fail(MSM_ERR_HIP, "event creation failed%s");
-  }
-  *out = ctx;
-  return MSM_OK;
-}
-
-void msm_ctx_destroy(msm_ctx* ctx) {
-  if (!ctx) return;
-  (void)hipSetDevice(ctx->device);
-  for (hipEvent_t e : ctx->events) (void)hipEventDestroy(e);
-  if (ctx->plan_ready) (void)hipEventDestroy(ctx->plan_ready);
-  if (ctx->ws) (void)hipFree(ctx->ws);
-  if (ctx->host_stats) (void)hipHostFree(ctx->host_stats);
-  delete ctx;
-}
-
-int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scalars, size_t n,
-            int c, int S, void* d_workspace, size_t workspace_bytes, void* stream,
-            msm_g1_affine* d_out) {
-  if (!ctx) return fail(MSM_ERR_ARG, "ctx is NULL%s");
-  int rc = check_run_args(d_points, d_scalars, n, c, S, d_out);
-  if (rc) return rc;
-  Layout L = plan(n, c);
-  if (d_workspace && (workspace_bytes < L.total || !aligned(d_workspace, 256)))
-    return fail(MSM_ERR_ARG, "workspace smaller than msm_workspace_bytes() or not 256-byte aligned%s");
-  hipStream_t st = (hipStream_t)stream;
-  HIP_TRY(hipSetDevice(ctx->device));
+// The whole MSM on stream st with workspace ws (laid out by L); arguments checked.
+int run_pipeline(msm_ctx* ctx, const g1a* d_points, const uint32_t* d_scalars, size_t n, int c,
+                 int S, int sched, int verify, char* ws, const Layout& L, hipStream_t st,
+                 g1a* d_out) {
+  // calls on one context are ordered even across streams: wait for the previous one
+  if (ctx->has_done) HIP_TRY(hipStreamWaitEvent(st, ctx->done, 0));
   if (n == 0) {
-    HIP_TRY(hipMemsetAsync(d_out, 0, sizeof(msm_g1_affine), st));
+    HIP_TRY(launch_fill((uint32_t*)d_out, sizeof(msm_g1_affine) / 4, 0, st));
+    HIP_TRY(hipEventRecord(ctx->done, st));
+    ctx->has_done = true;
     return MSM_OK;
-  }
-  char* ws = (char*)d_workspace;
-  if (!ws) {
-    if (ctx->ws_bytes < L.total) {
-      if (ctx->ws) {
-        HIP_TRY(hipStreamSynchronize(st));
-        HIP_TRY(hipFree(ctx->ws));
-        ctx->ws = nullptr;
-        ctx->ws_bytes = 0;
-      }
-      if (hipMalloc(&ctx->ws, L.total) != hipSuccess) {
-        ctx->ws = nullptr;
-        return fail(MSM_ERR_OOM, "workspace allocation failed%s");
-      }
-      ctx->ws_bytes = L.total;
-    }
-    ws = (char*)ctx->ws;
   }
   msm_stats* stats = (msm_stats*)(ws + L.stats);
   uint32_t* halfs = (uint32_t*)(ws + L.halfs);
@@ -277,7 +219,7 @@ int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scala
   // waits for the plan
   PhaseMark ph_sort(ctx, st, PH_SORT);
   HIP_TRY(launch_fill((uint32_t*)stats, sizeof(msm_stats) / 4, 0, st));
-  HIP_TRY(launch_glv_prep((const g1a*)d_points, d_scalars, n32, pts2, halfs, stats, st));
+  HIP_TRY(launch_glv_prep(d_points, d_scalars, n32, pts2, halfs, stats, verify, st));
   HIP_TRY(launch_hist(halfs, m32, c32, L.nwin, L.chunk, L.nchunk, hist_blk, counts, rank, stats, st));
   HIP_TRY(launch_scan(counts, L.K, -1, 1, block_sums, offsets, L.K + 1, nullptr, st));
   HIP_TRY(hipMemcpyAsync(ctx->host_stats, stats, sizeof(msm_stats), hipMemcpyDeviceToHost, st));
@@ -291,13 +233,18 @@ int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scala
   uint32_t* const poff_all = poff;
   HIP_TRY(launch_scan(counts, L.K, 0, level_bound, block_sums, poff_all, (size_t)L.K + 1,
                       &stats->max_count, st));
+  HIP_TRY(hipEventRecord(ctx->done, st));
+  ctx->has_done = true;
   HIP_TRY(hipEventSynchronize(ctx->plan_ready));
   const msm_stats hs = *ctx->host_stats;
   if (hs.range_flag) return fail(MSM_ERR_RANGE, "GLV half-scalar out of bound (internal error)%s");
+  if (hs.bad_point)
+    return fail(MSM_ERR_OFF_CURVE, "an input point is not on the curve or not reduced below p%s");
 
   // accumulate: pair-tree levels until every bucket holds one point
   int levels = 0;
   while (levels < level_bound && ((uint64_t)1 << levels) < hs.max_count) levels++;
+  (void)sched;
   for (int l = 0; l < levels; l++) {
     uint32_t np = hs.pairs[l];
     if (np == 0) continue;
@@ -333,10 +280,110 @@ int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scala
   HIP_TRY(launch_reduce(bsum, c32, L.nwin, L.seg_len, L.nseg, part, win, st));
   ph_red.end();
   PhaseMark ph_fin(ctx, st, PH_FINAL);
-  HIP_TRY(launch_final(win, L.nwin, c32, (g1a*)d_out, st));
+  HIP_TRY(launch_final(win, L.nwin, c32, d_out, st));
   ph_fin.end();
+  if (verify) HIP_TRY(launch_verify_point(d_out, &stats->bad_out, st));
+  HIP_TRY(hipEventRecord(ctx->done, st));
   if (ctx->timing) ctx->runs++;
+  if (verify) {
+    HIP_TRY(hipMemcpyAsync(&ctx->host_stats->bad_out, &stats->bad_out, 4, hipMemcpyDeviceToHost, st));
+    HIP_TRY(hipStreamSynchronize(st));
+    if (ctx->host_stats->bad_out) return fail(MSM_ERR_OFF_CURVE, "the result is not on the curve%s");
+  }
   return MSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int msm_version(void) { return 300; }
+
+const char* msm_last_error(void) { return g_err; }
+
+size_t msm_workspace_bytes(size_t n, int c, int S) {
+  (void)S;
+  if (c < 1 || c > 16 || n > MSM_MAX_N) return 0;
+  if ((uint64_t)2 * n * (uint64_t)num_windows(c) >= ((uint64_t)1 << 32)) return 0;
+  return plan(n, c).total;
+}
+
+int msm_ctx_create(int device, msm_ctx** out) {
+  if (!out) return fail(MSM_ERR_ARG, "out is NULL%s");
+  *out = nullptr;
+  int ndev = 0;
+  HIP_TRY(hipGetDeviceCount(&ndev));
+  if (device < 0 || device >= ndev) return fail(MSM_ERR_ARG, "no such device%s");
+  msm_ctx* ctx = new (std::nothrow) msm_ctx;
+  if (!ctx) return fail(MSM_ERR_OOM, "host allocation failed%s");
+  ctx->device = device;
+  int rc = MSM_OK;
+  if (hipSetDevice(device) != hipSuccess) {
+    rc = fail(MSM_ERR_HIP, "hipSetDevice failed%s");
+  } else if (hipHostMalloc((void**)&ctx->host_stats, sizeof(msm_stats), hipHostMallocDefault) !=
+             hipSuccess) {
+    ctx->host_stats = nullptr;
+    rc = fail(MSM_ERR_OOM, "pinned host allocation failed%s");
+  } else if (hipMalloc((void**)&ctx->d_result, 256) != hipSuccess) {
+    ctx->d_result = nullptr;
+    rc = fail(MSM_ERR_OOM, "device allocation failed%s");
+  } else if (hipEventCreateWithFlags(&ctx->plan_ready, hipEventDisableTiming) != hipSuccess ||
+             hipEventCreateWithFlags(&ctx->done, hipEventDisableTiming) != hipSuccess) {
+    rc = fail(MSM_ERR_HIP, "event creation failed%s");
+  }
+  if (rc != MSM_OK) {
+    msm_ctx_destroy(ctx);
+    return rc;
+  }
+  *out = ctx;
+  return MSM_OK;
+}
+
+void msm_ctx_destroy(msm_ctx* ctx) {
+  if (!ctx) return;
+  (void)hipSetDevice(ctx->device);
+  if (ctx->has_done) (void)hipEventSynchronize(ctx->done);
+  for (hipEvent_t e : ctx->events) (void)hipEventDestroy(e);
+  if (ctx->plan_ready) (void)hipEventDestroy(ctx->plan_ready);
+  if (ctx->done) (void)hipEventDestroy(ctx->done);
+  if (ctx->ws) (void)hipFree(ctx->ws);
+  if (ctx->d_result) (void)hipFree(ctx->d_result);
+  if (ctx->host_stats) (void)hipHostFree(ctx->host_stats);
+  delete ctx;
+}
+
+int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scalars, size_t n,
+            int c, int S, int sched, int verify, void* d_workspace, size_t workspace_bytes,
+            void* stream, msm_g1_affine* d_out) {
+  if (!ctx) return fail(MSM_ERR_ARG, "ctx is NULL%s");
+  int rc = check_run_args(d_points, d_scalars, n, c, S, sched, verify, d_out);
+  if (rc) return rc;
+  if (sched == MSM_SCHED_WALKER) return fail(MSM_ERR_ARG, "the stream-walker schedule is not built%s");
+  const Layout L = plan(n, c);
+  if (d_workspace && (workspace_bytes < L.total || !aligned(d_workspace, 256)))
+    return fail(MSM_ERR_ARG, "workspace smaller than msm_workspace_bytes() or not 256-byte aligned%s");
+  hipStream_t st = (hipStream_t)stream;
+  HIP_TRY(hipSetDevice(ctx->device));
+  char* ws = (char*)d_workspace;
+  if (!ws && n) {
+    if (ctx->ws_bytes < L.total) {
+      if (ctx->ws) {
+        // the previous call may still be using the old workspace on another stream
+        if (ctx->has_done) HIP_TRY(hipEventSynchronize(ctx->done));
+        HIP_TRY(hipFree(ctx->ws));
+        ctx->ws = nullptr;
+        ctx->ws_bytes = 0;
+      }
+      if (hipMalloc(&ctx->ws, L.total) != hipSuccess) {
+        ctx->ws = nullptr;
+        return fail(MSM_ERR_OOM, "workspace allocation failed%s");
+      }
+      ctx->ws_bytes = L.total;
+    }
+    ws = (char*)ctx->ws;
+  }
+  return run_pipeline(ctx, (const g1a*)d_points, d_scalars, n, c, S, sched, verify, ws, L, st,
+                      (g1a*)d_out);
 }
 
 int msm_ctx_set_affine_levels(msm_ctx* ctx, int levels) {
@@ -379,31 +426,26 @@ int msm_ctx_timing_read(msm_ctx* ctx, msm_timing* out) {
 int msm(const msm_g1_affine* d_points, const uint32_t* d_scalars, size_t n, int c,
         msm_g1_affine* h_out) {
   if (!h_out) return fail(MSM_ERR_ARG, "h_out is NULL%s");
-  int rc = check_run_args(d_points, d_scalars, n, c, 8, (const msm_g1_affine*)16);
+  int rc = check_run_args(d_points, d_scalars, n, c, 8, MSM_SCHED_PAIR_TREE, 0,
+                          (const msm_g1_affine*)16);
   if (rc) return rc;
   static std::mutex mu;
   static msm_ctx* ctxs[64] = {};
   int dev = 0;
   HIP_TRY(hipGetDevice(&dev));
   if (dev < 0 || dev >= 64) return fail(MSM_ERR_ARG, "device index out of range%s");
-  msm_ctx* ctx;
-  {
-    std::lock_guard<std::mutex> g(mu);
-    if (!ctxs[dev]) {
-      rc = msm_ctx_create(dev, &ctxs[dev]);
-      if (rc) return rc;
-    }
-    ctx = ctxs[dev];
-  }
-  msm_g1_affine* d_out = nullptr;
-  if (hipMalloc(&d_out, sizeof(msm_g1_affine)) != hipSuccess) return fail(MSM_ERR_OOM, "allocation failed%s");
   std::lock_guard<std::mutex> g(mu);
-  rc = msm_run(ctx, d_points, d_scalars, n, c, 8, nullptr, 0, nullptr, d_out);
+  if (!ctxs[dev]) {
+    rc = msm_ctx_create(dev, &ctxs[dev]);
+    if (rc) return rc;
+  }
+  msm_ctx* ctx = ctxs[dev];
+  rc = msm_run(ctx, d_points, d_scalars, n, c, 8, MSM_SCHED_PAIR_TREE, 0, nullptr, 0, nullptr,
+               ctx->d_result);
   if (rc == MSM_OK) {
-    hipError_t e = hipMemcpy(h_out, d_out, sizeof(msm_g1_affine), hipMemcpyDeviceToHost);
+    hipError_t e = hipMemcpy(h_out, ctx->d_result, sizeof(msm_g1_affine), hipMemcpyDeviceToHost);
     if (e != hipSuccess) rc = fail(MSM_ERR_HIP, "HIP error: %s (copy result)", hipGetErrorString(e));
   }
-  (void)hipFree(d_out);
   return rc;
 }
 
@@ -417,12 +459,34 @@ int msm_g1_from_scalars(const uint32_t* d_k, size_t n, msm_g1_affine* d_out, voi
 
 int msm_test_fp(int op, const uint32_t* d_a, const uint32_t* d_b, uint32_t* d_out, size_t n,
                 void* stream) {
-  if (op < 0 || op > 6) return fail(MSM_ERR_ARG, "op must be in 0..6%s");
+  if (op < 0 || op > 8) return fail(MSM_ERR_ARG, "op must be in 0..8%s");
   if (n > MSM_MAX_N) return fail(MSM_ERR_ARG, "n exceeds MSM_MAX_N%s");
   bool binary = (op <= 2);
   if (n && (!d_a || !d_out || (binary && !d_b))) return fail(MSM_ERR_ARG, "NULL pointer%s");
+  if (!aligned(d_a, 4) || !aligned(d_b, 4) || !aligned(d_out, 4))
+    return fail(MSM_ERR_ARG, "pointers must be 4-byte aligned%s");
   HIP_TRY(launch_test_fp(op, d_a, binary ? d_b : nullptr, d_out, (uint32_t)n, (hipStream_t)stream));
   return MSM_OK;
+}
+
+int msm_test_fp_mul(const uint32_t* d_a, const uint32_t* d_b, uint32_t* d_out, size_t n, void* stream) {
+  return msm_test_fp(0, d_a, d_b, d_out, n, stream);
+}
+
+int msm_test_fp_add(const uint32_t* d_a, const uint32_t* d_b, uint32_t* d_out, size_t n, void* stream) {
+  return msm_test_fp(1, d_a, d_b, d_out, n, stream);
+}
+
+int msm_test_fp_sub(const uint32_t* d_a, const uint32_t* d_b, uint32_t* d_out, size_t n, void* stream) {
+  return msm_test_fp(2, d_a, d_b, d_out, n, stream);
+}
+
+int msm_test_fp_sqr(const uint32_t* d_a, uint32_t* d_out, size_t n, void* stream) {
+  return msm_test_fp(3, d_a, nullptr, d_out, n, stream);
+}
+
+int msm_test_fp_inv(const uint32_t* d_a, uint32_t* d_out, size_t n, void* stream) {
+  return msm_test_fp(4, d_a, nullptr, d_out, n, stream);
 }
 
 int msm_test_glv(const uint32_t* d_scalars, size_t n, uint32_t* d_halfs, void* stream) {
@@ -434,8 +498,8 @@ int msm_test_glv(const uint32_t* d_scalars, size_t n, uint32_t* d_halfs, void* s
   return MSM_OK;
 }
 
-int msm_test_pair_add(const msm_g1_affine* d_a, const msm_g1_affine* d_b, msm_g1_affine* d_out,
-                      size_t n, int S, void* stream) {
+int msm_test_batched_add(const msm_g1_affine* d_a, const msm_g1_affine* d_b,
+                         msm_g1_affine* d_out, size_t n, int S, void* stream) {
   if (S != 4 && S != 8 && S != 16 && S != 32) return fail(MSM_ERR_ARG, "S must be 4, 8, 16 or 32%s");
   if (n > MSM_MAX_N) return fail(MSM_ERR_ARG, "n exceeds MSM_MAX_N%s");
   if (n && (!d_a || !d_b || !d_out)) return fail(MSM_ERR_ARG, "NULL pointer%s");

@@ -21,8 +21,10 @@ struct msm_stats {
   uint32_t range_flag;          // a GLV half-scalar came out >= 2^127 (never expected)
   uint32_t max_count;           // largest bucket
   uint32_t total;               // bucket entries E (non-zero digits)
-  uint32_t pad;
+  uint32_t bad_point;           // verify: some input point is off the curve or not reduced
   uint32_t pairs[MAX_LEVELS];   // pair adds at pair-tree level l
+  uint32_t bad_out;             // verify: the result is off the curve (read after the MSM)
+  uint32_t pad[3];
 };
 
 // XYZZ point as stored in device memory (X, Y, ZZ, ZZZ; 128 bytes).
@@ -31,8 +33,12 @@ struct xyzz_st {
 };
 
 hipError_t launch_fill(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
+// verify != 0 also checks every input point (reduced coordinates, on the curve or
+// (0, 0)) and sets st->bad_point when one fails.
 hipError_t launch_glv_prep(const g1a* points, const uint32_t* scalars, uint32_t n, g1a* pts2,
-                           uint32_t* halfs, msm_stats* st, hipStream_t s);
+                           uint32_t* halfs, msm_stats* st, int verify, hipStream_t s);
+// *flag |= 1 when the affine point p is neither (0, 0) nor a reduced point on the curve.
+hipError_t launch_verify_point(const g1a* p, uint32_t* flag, hipStream_t s);
 // Counting pass: per (chunk of half-scalars, window) LDS histograms into hist_blk
 // (nwin nchunk 2^(c-1) words), turned into per-chunk prefixes, the bucket counts, and
 // the plan statistics in st (largest bucket, total, pair adds per level).

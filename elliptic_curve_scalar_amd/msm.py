@@ -16,7 +16,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmsm.so")
 
-MSM_OK, MSM_ERR_ARG, MSM_ERR_HIP, MSM_ERR_OOM, MSM_ERR_RANGE = 0, -1, -2, -3, -4
+MSM_OK, MSM_ERR_ARG, MSM_ERR_HIP, MSM_ERR_OOM, MSM_ERR_RANGE, MSM_ERR_OFF_CURVE = 0, -1, -2, -3, -4, -5
+MSM_SCHED_PAIR_TREE, MSM_SCHED_WALKER = 0, 1
 MSM_MAX_N = 1 << 26
 VALID_S = (4, 8, 16, 32)
 
@@ -28,14 +29,19 @@ SYMBOLS = {
     "msm_ctx_create": (_I, [_I, ctypes.POINTER(_P)]),
     "msm_ctx_destroy": (None, [_P]),
     "msm_workspace_bytes": (_S, [_S, _I, _I]),
-    "msm_run": (_I, [_P, _P, _P, _S, _I, _I, _P, _S, _P, _P]),
+    "msm_run": (_I, [_P, _P, _P, _S, _I, _I, _I, _I, _P, _S, _P, _P]),
     "msm": (_I, [_P, _P, _S, _I, _P]),
     "msm_g1_from_scalars": (_I, [_P, _S, _P, _P]),
     "msm_ctx_set_affine_levels": (_I, [_P, _I]),
     "msm_ctx_set_timing": (_I, [_P, _I]),
     "msm_ctx_timing_read": (_I, [_P, _P]),
     "msm_test_fp": (_I, [_I, _P, _P, _P, _S, _P]),
-    "msm_test_pair_add": (_I, [_P, _P, _P, _S, _I, _P]),
+    "msm_test_fp_mul": (_I, [_P, _P, _P, _S, _P]),
+    "msm_test_fp_add": (_I, [_P, _P, _P, _S, _P]),
+    "msm_test_fp_sub": (_I, [_P, _P, _P, _S, _P]),
+    "msm_test_fp_sqr": (_I, [_P, _P, _S, _P]),
+    "msm_test_fp_inv": (_I, [_P, _P, _S, _P]),
+    "msm_test_batched_add": (_I, [_P, _P, _P, _S, _I, _P]),
     "msm_test_glv": (_I, [_P, _S, _P, _P]),
 }
 
@@ -102,7 +108,13 @@ def workspace_bytes(n: int, c: int, S: int = 8) -> int:
 
 
 class Context:
-    """A libmsm context on one device. Workspace comes from torch's allocator."""
+    """A libmsm context on one device. Workspace comes from torch's allocator.
+
+    The C context orders consecutive runs on the device even across streams, so one
+    workspace serves every stream; the workspace tensor is also marked as in use on
+    each run's stream, so torch's allocator does not hand it out again (after it has
+    grown, say) before the kernels queued there have finished with it.
+    """
 
     def __init__(self, device=None):
         self.device = torch.device("cuda", torch.cuda.current_device() if device is None else
@@ -142,25 +154,32 @@ class Context:
         need = workspace_bytes(n, c, S)
         if need == 0:
             raise MsmError(MSM_ERR_ARG, "invalid n or c")
-        if self._ws is None or self._ws.numel() < need:
+        if self._ws is None or self._ws.numel() < need + 256:
+            self._ws = None  # the old block returns to the allocator, guarded by record_stream
             self._ws = torch.empty(need + 256, dtype=torch.uint8, device=self.device)
         return self._ws
 
     def run(self, points: torch.Tensor, scalars: torch.Tensor, c: int, S: int = 8,
-            out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+            out: torch.Tensor | None = None, stream=None, sched: int = MSM_SCHED_PAIR_TREE,
+            verify: bool = False) -> torch.Tensor:
         """Q = sum_i s_i P_i on the current (or given) stream; returns a [16] device
         tensor (affine x, y in Montgomery form; zeros for infinity)."""
         n = points.shape[0]
         if scalars.shape[0] != n:
             raise ValueError("points and scalars differ in length")
+        s = stream if stream is not None else torch.cuda.current_stream(self.device)
         if out is None:
             out = torch.empty(16, dtype=torch.uint32, device=self.device)
         ws = self.workspace(n, c, S)
         base = ws.data_ptr()
         aligned = (base + 255) // 256 * 256
-        _check(lib().msm_run(self._h, _dev_ptr(points, 16, "points"), _dev_ptr(scalars, 8, "scalars"),
-                             n, c, S, ctypes.c_void_p(aligned), ws.numel() - (aligned - base),
-                             _stream_handle(self.device, stream), _dev_ptr(out, None, "out")))
+        rc = lib().msm_run(self._h, _dev_ptr(points, 16, "points"), _dev_ptr(scalars, 8, "scalars"),
+                           n, c, S, int(sched), int(bool(verify)), ctypes.c_void_p(aligned),
+                           ws.numel() - (aligned - base), ctypes.c_void_p(s.cuda_stream),
+                           _dev_ptr(out, None, "out"))
+        for t in (ws, out, points, scalars):
+            t.record_stream(s)
+        _check(rc)
         return out
 
 
@@ -174,8 +193,10 @@ def context(device=None) -> Context:
     return _contexts[idx]
 
 
-def msm(points: torch.Tensor, scalars: torch.Tensor, c: int, S: int = 8, stream=None) -> torch.Tensor:
-    return context(points.device).run(points, scalars, c, S, stream=stream)
+def msm(points: torch.Tensor, scalars: torch.Tensor, c: int, S: int = 8, stream=None,
+        sched: int = MSM_SCHED_PAIR_TREE, verify: bool = False) -> torch.Tensor:
+    return context(points.device).run(points, scalars, c, S, stream=stream, sched=sched,
+                                      verify=verify)
 
 
 def msm_sync(points: torch.Tensor, scalars: torch.Tensor, c: int):
@@ -196,9 +217,23 @@ def g1_from_scalars(k: torch.Tensor, stream=None) -> torch.Tensor:
 
 
 def test_fp(op: int, a: torch.Tensor, b: torch.Tensor | None = None) -> torch.Tensor:
+    """Element-wise F_p operation ``op`` of msm_test_fp on [n, 8] device tensors."""
     out = torch.empty_like(a)
     _check(lib().msm_test_fp(op, _dev_ptr(a, 8, "a"), _dev_ptr(b, 8, "b"), _dev_ptr(out, 8, "out"),
                              a.shape[0], _stream_handle(a.device)))
+    return out
+
+
+def test_fp_named(name: str, a: torch.Tensor, b: torch.Tensor | None = None) -> torch.Tensor:
+    """The named hooks msm_test_fp_{mul, sqr, add, sub, inv}."""
+    out = torch.empty_like(a)
+    fn = getattr(lib(), "msm_test_fp_" + name)
+    if name in ("sqr", "inv"):
+        rc = fn(_dev_ptr(a, 8, "a"), _dev_ptr(out, 8, "out"), a.shape[0], _stream_handle(a.device))
+    else:
+        rc = fn(_dev_ptr(a, 8, "a"), _dev_ptr(b, 8, "b"), _dev_ptr(out, 8, "out"), a.shape[0],
+                _stream_handle(a.device))
+    _check(rc)
     return out
 
 
@@ -211,8 +246,10 @@ def test_glv(scalars: torch.Tensor) -> torch.Tensor:
     return out
 
 
-def test_pair_add(a: torch.Tensor, b: torch.Tensor, S: int = 8) -> torch.Tensor:
+def test_batched_add(a: torch.Tensor, b: torch.Tensor, S: int = 8) -> torch.Tensor:
+    """a[i] + b[i] by the batched-affine adder, S slots per lane."""
     out = torch.empty_like(a)
-    _check(lib().msm_test_pair_add(_dev_ptr(a, 16, "a"), _dev_ptr(b, 16, "b"),
-                                   _dev_ptr(out, 16, "out"), a.shape[0], S, _stream_handle(a.device)))
+    _check(lib().msm_test_batched_add(_dev_ptr(a, 16, "a"), _dev_ptr(b, 16, "b"),
+                                      _dev_ptr(out, 16, "out"), a.shape[0], S,
+                                      _stream_handle(a.device)))
     return out

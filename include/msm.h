@@ -47,10 +47,17 @@ typedef struct msm_ctx msm_ctx;
 
 enum {
   MSM_OK = 0,
-  MSM_ERR_ARG = -1,   /* bad pointer, alignment, size, c or S; workspace too small */
-  MSM_ERR_HIP = -2,   /* a HIP runtime call or kernel launch failed */
-  MSM_ERR_OOM = -3,   /* device or pinned host allocation failed */
-  MSM_ERR_RANGE = -4  /* internal: a GLV half-scalar came out >= 2^127 (not expected) */
+  MSM_ERR_ARG = -1,        /* bad pointer, alignment, size, c, S or sched; workspace too small */
+  MSM_ERR_HIP = -2,        /* a HIP runtime call or kernel launch failed */
+  MSM_ERR_OOM = -3,        /* device or pinned host allocation failed */
+  MSM_ERR_RANGE = -4,      /* internal: a GLV half-scalar came out >= 2^127 (not expected) */
+  MSM_ERR_OFF_CURVE = -5   /* verify = 1 only: an input point or the result is not on the curve */
+};
+
+/* Accumulate schedules (the sched argument of msm_run). */
+enum {
+  MSM_SCHED_PAIR_TREE = 0, /* level 0 of a per-bucket pair tree, S pairs per lane */
+  MSM_SCHED_WALKER = 1     /* stream walker: S slots per lane walk equal chunks of the lists */
 };
 
 /* Largest n accepted. Bucket lists are indexed with 32-bit offsets, so in addition
@@ -64,9 +71,11 @@ int msm_version(void);
 const char* msm_last_error(void);
 
 /*
- * Context: binds a device and owns a growable workspace and a pinned host buffer
- * for the one mid-pipeline read-back. One context per host thread; calls on one
- * context must not overlap. Returns MSM_ERR_ARG for a bad device or NULL out.
+ * Context: binds a device and owns a growable workspace, a pinned host buffer for the
+ * one mid-pipeline read-back, a small device result buffer and the event that orders
+ * its calls. Calls on one context must not be made from several host threads at once.
+ * Returns MSM_ERR_ARG for a bad device or NULL out, MSM_ERR_OOM if the pinned or
+ * device buffers cannot be allocated.
  */
 int msm_ctx_create(int device, msm_ctx** out);
 void msm_ctx_destroy(msm_ctx* ctx);
@@ -81,7 +90,7 @@ size_t msm_workspace_bytes(size_t n, int c, int S);
 /*
  * Q = sum_i s_i * P_i on `stream` (a hipStream_t; NULL is the null stream).
  *   d_points   device, n msm_g1_affine, 16-byte aligned; every point on the curve or
- *              (0, 0); the library does not check curve membership.
+ *              (0, 0). Without verify the library does not check curve membership.
  *   d_scalars  device, n * 8 uint32 words, 16-byte aligned; any 256-bit integers
  *              (reduced mod r on the device).
  *   n          0 .. MSM_MAX_N with 2 n ceil(128 / c) < 2^32; n = 0 gives the point
@@ -89,26 +98,47 @@ size_t msm_workspace_bytes(size_t n, int c, int S);
  *   c          window width in bits, 1 .. 16; W = ceil(128 / c) windows of signed
  *              digits in [-2^(c-1), 2^(c-1)] over the 2n half-scalars (2^(c-1)
  *              buckets per window, -P is free).
- *   S          affine additions sharing one inversion: 4, 8, 16 or 32.
+ *   S          affine additions sharing one field inversion: 4, 8, 16 or 32
+ *              (PR #23738 "TL;DR"; PR #23736 "Goal & lever").
+ *   sched      MSM_SCHED_PAIR_TREE: each lane adds S pairs of one or more bucket lists
+ *              at pair-tree level 0 (PR #23520 "Summary"); deeper levels follow.
+ *              MSM_SCHED_WALKER: each lane owns S slots, each walking an equal chunk of
+ *              the sorted lists with one batched inversion per step; finished buckets
+ *              are flushed and chunk-boundary partial sums combined afterwards
+ *              (PR #23736 "Change"; PR #23738 "What would actually win").
+ *   verify     0 or 1. With 1, every input point is checked on the device (coordinates
+ *              below p, y^2 = x^3 + 3, or (0, 0)) and so is the result, the failure
+ *              signal of PR #23736 ("Correctness-harness fix"); the call then waits
+ *              for the stream to read the result's flag. An off-curve input returns
+ *              MSM_ERR_OFF_CURVE before the accumulate is enqueued (d_out is not
+ *              written); an off-curve result returns it after d_out is written.
  *   d_workspace device scratch of msm_workspace_bytes(n, c, S) bytes (256-byte
  *              aligned), or NULL to use the context's own (grown on demand).
+ *   workspace_bytes  size of d_workspace (ignored when it is NULL); the library
+ *              checks it against msm_workspace_bytes before any launch.
  *   d_out      device, one msm_g1_affine: Q in affine Montgomery form, (0, 0) if
  *              Q is the point at infinity.
  * The call enqueues the decompose/count/sort kernels, then blocks once on `stream`
  * to read back a small plan (largest bucket, split range flag), then enqueues the
  * accumulate, reduction and combine kernels and returns; d_out is valid once the
- * stream reaches that point. Points must lie in the prime-order group (every
- * BN254 G1 point does: the cofactor is 1). MSM_ERR_RANGE only if the split's bound
- * failed, which the constants rule out (nothing further is enqueued then).
+ * stream reaches that point. Consecutive calls on one context are ordered on the
+ * device even when they use different streams (each call waits for the previous
+ * call's last kernel), so the context's workspace is never shared by two calls in
+ * flight. Points must lie in the prime-order group (every BN254 G1 point does: the
+ * cofactor is 1). MSM_ERR_RANGE only if the split's bound failed, which the
+ * constants rule out (nothing further is enqueued then).
  */
 int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scalars, size_t n,
-            int c, int S, void* d_workspace, size_t workspace_bytes, void* stream,
-            msm_g1_affine* d_out);
+            int c, int S, int sched, int verify, void* d_workspace, size_t workspace_bytes,
+            void* stream, msm_g1_affine* d_out);
 
 /*
  * Synchronous convenience form, the shape msm(points_affine, scalars, n, c) -> point:
  * device inputs, result written to host memory h_out. Uses a per-device default
- * context, S = 8 and the null stream.
+ * context (created on first use), S = 8, the pair-tree schedule, no verify and the
+ * null stream; the result travels through a small device buffer the context owns,
+ * so a call allocates nothing after the context's workspace has grown to n.
+ * Calls from several host threads are serialized.
  */
 int msm(const msm_g1_affine* d_points, const uint32_t* d_scalars, size_t n, int c,
         msm_g1_affine* h_out);
@@ -158,25 +188,42 @@ int msm_ctx_set_timing(msm_ctx* ctx, int enable);
 int msm_ctx_timing_read(msm_ctx* ctx, msm_timing* out);
 
 /*
- * Test hooks (the same device code as the MSM, exposed for unit tests).
+ * Test hooks (the same device code as the MSM, exposed for unit tests). All take
+ * device pointers to n field elements of eight words each (Montgomery form, < p) and
+ * run asynchronously on `stream`.
  *
- * msm_test_fp: element-wise F_p operation on n Montgomery-form elements (8 words
- * each, device pointers; d_b unused for unary ops): op 0 a*b, 1 a+b, 2 a-b, 3 a^2,
- * 4 a^-1 (0 -> 0), 5 to Montgomery (a * 2^256), 6 from Montgomery (a * 2^-256).
+ * msm_test_fp_mul / _sqr / _add / _sub: d_out = a*b, a^2, a+b, a-b (Montgomery
+ * products a*b*2^-256 mod p for mul and sqr).
+ * msm_test_fp_inv: d_out = a^-1 (the Montgomery form of the inverse) by the binary-GCD
+ * inverse every kernel uses; 0 gives 0.
  *
- * msm_test_pair_add: d_out[i] = d_a[i] + d_b[i] for n affine points, computed by
- * the batched-affine adder with S slots per lane (one inversion per S sums).
+ * msm_test_fp: the same operations by number, plus conversions and the inverse's
+ * parts: op 0 a*b, 1 a+b, 2 a-b, 3 a^2, 4 a^-1 (0 -> 0), 5 to Montgomery (a * 2^256),
+ * 6 from Montgomery (a * 2^-256), 7 Fermat's a^(p-2) alone, 8 the binary-GCD inverse
+ * with no special case for 0 (its own fallback handles it). d_b unused for unary ops.
+ *
+ * msm_test_batched_add: d_out[i] = d_a[i] + d_b[i] for n affine points, computed by
+ * the batched-affine adder with S slots per lane (one inversion per S sums, PR #23520
+ * "Summary"); every special case (infinity, doubling, P + (-P)) is allowed.
  *
  * msm_test_glv: the scalar split of msm_run for n scalars (8 words each, any
  * 256-bit value): d_halfs[i] = |k1| and d_halfs[n + i] = |k2| of scalar i, four
  * words each with the sign in bit 127, where s = k1 + k2 lambda (mod r).
  * d_halfs holds 2 n * 4 words.
+ *
+ * Errors: MSM_ERR_ARG for an unknown op or S, n > MSM_MAX_N, NULL or misaligned
+ * pointers with n > 0; MSM_ERR_HIP if the launch fails.
  */
 int msm_test_fp(int op, const uint32_t* d_a, const uint32_t* d_b, uint32_t* d_out, size_t n,
                 void* stream);
+int msm_test_fp_mul(const uint32_t* d_a, const uint32_t* d_b, uint32_t* d_out, size_t n, void* stream);
+int msm_test_fp_sqr(const uint32_t* d_a, uint32_t* d_out, size_t n, void* stream);
+int msm_test_fp_add(const uint32_t* d_a, const uint32_t* d_b, uint32_t* d_out, size_t n, void* stream);
+int msm_test_fp_sub(const uint32_t* d_a, const uint32_t* d_b, uint32_t* d_out, size_t n, void* stream);
+int msm_test_fp_inv(const uint32_t* d_a, uint32_t* d_out, size_t n, void* stream);
 int msm_test_glv(const uint32_t* d_scalars, size_t n, uint32_t* d_halfs, void* stream);
-int msm_test_pair_add(const msm_g1_affine* d_a, const msm_g1_affine* d_b, msm_g1_affine* d_out,
-                      size_t n, int S, void* stream);
+int msm_test_batched_add(const msm_g1_affine* d_a, const msm_g1_affine* d_b,
+                         msm_g1_affine* d_out, size_t n, int S, void* stream);
 
 #ifdef __cplusplus
 }

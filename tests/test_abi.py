@@ -23,8 +23,9 @@ def _declared_functions():
 def test_header_declares_expected_entry_points():
     names = _declared_functions()
     for want in ("msm", "msm_run", "msm_ctx_create", "msm_ctx_destroy", "msm_workspace_bytes",
-                 "msm_last_error", "msm_g1_from_scalars", "msm_test_fp", "msm_test_pair_add",
-                 "msm_version"):
+                 "msm_last_error", "msm_g1_from_scalars", "msm_test_fp", "msm_test_fp_mul",
+                 "msm_test_fp_sqr", "msm_test_fp_add", "msm_test_fp_sub", "msm_test_fp_inv",
+                 "msm_test_batched_add", "msm_version"):
         assert want in names
     assert set(names) == set(M.SYMBOLS), "binding and header disagree"
 
@@ -60,7 +61,7 @@ def test_argument_errors_without_gpu():
     out = ctypes.c_void_p(256)
     p = ctypes.c_void_p(512)
     # NULL context
-    assert L.msm_run(None, p, p, 16, 13, 8, None, 0, None, out) == M.MSM_ERR_ARG
+    assert L.msm_run(None, p, p, 16, 13, 8, 0, 0, None, 0, None, out) == M.MSM_ERR_ARG
     assert "ctx" in _err(L)
     # NULL h_out / bad c / bad S / misaligned pointers on the synchronous form
     assert L.msm(p, p, 16, 13, None) == M.MSM_ERR_ARG
@@ -76,13 +77,47 @@ def test_argument_errors_without_gpu():
     # generator and test hooks
     assert L.msm_g1_from_scalars(None, 4, p, None) == M.MSM_ERR_ARG
     assert L.msm_g1_from_scalars(ctypes.c_void_p(4), 4, p, None) == M.MSM_ERR_ARG
-    assert L.msm_test_fp(7, p, p, p, 4, None) == M.MSM_ERR_ARG
+    assert L.msm_test_fp(9, p, p, p, 4, None) == M.MSM_ERR_ARG
+    assert L.msm_test_fp(-1, p, p, p, 4, None) == M.MSM_ERR_ARG
     assert L.msm_test_fp(0, p, None, p, 4, None) == M.MSM_ERR_ARG
-    assert L.msm_test_pair_add(p, p, p, 4, 5, None) == M.MSM_ERR_ARG
+    assert L.msm_test_fp_mul(p, None, p, 4, None) == M.MSM_ERR_ARG
+    assert L.msm_test_fp_sub(None, p, p, 4, None) == M.MSM_ERR_ARG
+    assert L.msm_test_fp_inv(p, None, 4, None) == M.MSM_ERR_ARG
+    assert L.msm_test_fp_sqr(p, p, M.MSM_MAX_N + 1, None) == M.MSM_ERR_ARG
+    assert L.msm_test_batched_add(p, p, p, 4, 5, None) == M.MSM_ERR_ARG
+    assert L.msm_test_batched_add(p, ctypes.c_void_p(8), p, 4, 8, None) == M.MSM_ERR_ARG
     assert L.msm_test_glv(None, 4, p, None) == M.MSM_ERR_ARG
     assert L.msm_test_glv(p, 4, ctypes.c_void_p(4), None) == M.MSM_ERR_ARG
     # context creation with a NULL out pointer
     assert L.msm_ctx_create(0, None) == M.MSM_ERR_ARG
+
+
+def test_run_argument_errors_without_gpu():
+    """msm_run checks S, sched, verify, c and the workspace before any HIP call; a
+    dummy context pointer is never dereferenced on these paths."""
+    L = M.lib()
+    out = ctypes.c_void_p(256)
+    p = ctypes.c_void_p(512)
+    ctx = ctypes.c_void_p(4096)
+    assert L.msm_run(ctx, p, p, 16, 13, 5, 0, 0, None, 0, None, out) == M.MSM_ERR_ARG
+    assert "S must be" in _err(L)
+    for sched in (-1, 2, 7):
+        assert L.msm_run(ctx, p, p, 16, 13, 8, sched, 0, None, 0, None, out) == M.MSM_ERR_ARG
+        assert "sched" in _err(L)
+    for verify in (-1, 2):
+        assert L.msm_run(ctx, p, p, 16, 13, 8, 0, verify, None, 0, None, out) == M.MSM_ERR_ARG
+        assert "verify" in _err(L)
+    assert L.msm_run(ctx, p, p, 16, 0, 8, 0, 0, None, 0, None, out) == M.MSM_ERR_ARG
+    assert L.msm_run(ctx, p, p, 16, 13, 8, 1, 1, None, 0, None, None) == M.MSM_ERR_ARG
+    assert L.msm_run(ctx, ctypes.c_void_p(520), p, 16, 13, 8, 0, 0, None, 0, None, out) == M.MSM_ERR_ARG
+    # a caller workspace below msm_workspace_bytes, or misaligned, is refused
+    need = M.workspace_bytes(16, 13)
+    ws = ctypes.c_void_p(1 << 20)
+    assert L.msm_run(ctx, p, p, 16, 13, 8, 0, 0, ws, need - 1, None, out) == M.MSM_ERR_ARG
+    assert "workspace" in _err(L)
+    assert L.msm_run(ctx, p, p, 16, 13, 8, 0, 0, ctypes.c_void_p((1 << 20) + 16), need, None,
+                     out) == M.MSM_ERR_ARG
+    assert M.MSM_ERR_OFF_CURVE == -5 and (M.MSM_SCHED_PAIR_TREE, M.MSM_SCHED_WALKER) == (0, 1)
 
 
 def test_binding_refuses_host_tensors():

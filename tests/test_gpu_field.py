@@ -56,6 +56,38 @@ def test_fp_ops_match_python(op):
     assert got == want
 
 
+def test_named_field_hooks():
+    """msm_test_fp_{mul, sqr, add, sub, inv} against Python integers."""
+    from elliptic_curve_scalar_amd import msm as M
+    rng = random.Random(17)
+    xs = EDGE + [rng.randrange(P) for _ in range(777)]
+    ys = list(reversed(EDGE)) + [rng.randrange(P) for _ in range(777)]
+    a, b = to_dev(_words(xs)), to_dev(_words(ys))
+    rinv = pow(1 << 256, -1, P)
+    want = {"mul": [x * y * rinv % P for x, y in zip(xs, ys)],
+            "sqr": [x * x * rinv % P for x in xs],
+            "add": [(x + y) % P for x, y in zip(xs, ys)],
+            "sub": [(x - y) % P for x, y in zip(xs, ys)],
+            "inv": [0 if x == 0 else pow(x, P - 2, P) * (1 << 512) % P for x in xs]}
+    for name, w in want.items():
+        say("named hook", name, "n", len(xs))
+        got = wl.to_ints(to_host(M.test_fp_named(name, a, b if name not in ("sqr", "inv") else None)))
+        assert got == w, name
+
+
+@pytest.mark.parametrize("op", [7, 8])
+def test_inverse_parts(op):
+    """Fermat's inverse alone (op 7) and the binary-GCD inverse with no special case for
+    0 (op 8): its fallback must map 0 to 0 and every other input to the inverse."""
+    from elliptic_curve_scalar_amd import msm as M
+    rng = random.Random(300 + op)
+    xs = [0, 1, 2, P - 1, P - 2] + [1 << k for k in range(0, 254, 7)] + \
+        [P - (1 << k) for k in range(1, 254, 11)] + [rng.randrange(1, P) for _ in range(300)]
+    say("fp op", op, "n", len(xs))
+    got = wl.to_ints(to_host(M.test_fp(op, to_dev(_words(xs)))))
+    assert got == [0 if x == 0 else pow(x, P - 2, P) * (1 << 512) % P for x in xs]
+
+
 def _rand_dlogs(rng, n):
     return [rng.randrange(1, ref.R) for _ in range(n)]
 
@@ -100,8 +132,8 @@ def test_batched_affine_add_all_cases(S):
         B.append(b)
         kinds.append(k)
     A, B = np.array(A), np.array(B)
-    say("pair_add S", S, "n", len(A))
-    got = to_host(M.test_pair_add(to_dev(A), to_dev(B), S))
+    say("batched_add S", S, "n", len(A))
+    got = to_host(M.test_batched_add(to_dev(A), to_dev(B), S))
     for i in range(len(A)):
         want = ref.add(ref.decode_point(A[i]), ref.decode_point(B[i]))
         assert ref.decode_point(got[i]) == want, (i, kinds[i])

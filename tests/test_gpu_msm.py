@@ -220,3 +220,56 @@ def test_timing_levels():
             ctx.set_timing(3)
     finally:
         ctx.close()
+
+
+def test_verify_flags_off_curve_points():
+    """verify = 1: a good input gives the right point and MSM_OK; one point off the
+    curve, or with a coordinate not reduced below p, gives MSM_ERR_OFF_CURVE (the
+    pages' failure signal, PR #23736 "Correctness-harness fix") as an ordinary error."""
+    M = _msm()
+    w = wl.generate("n65536_c13", n=2000)
+    pts = oracle.g1_from_scalars(w["dlogs"])
+    want = oracle.msm_pippenger(pts, w["scalars"], 13)
+    say("verify good input")
+    got = to_host(M.msm(to_dev(pts), to_dev(w["scalars"]), 13, 8, verify=True))
+    assert np.array_equal(got, want)
+    bad = pts.copy()
+    y = wl.to_ints(bad[777:778, 8:16])[0]
+    bad[777, 8:16] = wl.from_ints([(y + 1) % ref.P])[0]          # y + 1: off the curve
+    unreduced = pts.copy()
+    x = wl.to_ints(unreduced[5:6, 0:8])[0]
+    unreduced[5, 0:8] = wl.from_ints([x + ref.P])[0] if x + ref.P < (1 << 256) else unreduced[5, 0:8]
+    for name, p in (("off-curve y", bad), ("x + p", unreduced)):
+        say("verify", name)
+        with pytest.raises(M.MsmError) as ei:
+            M.msm(to_dev(p), to_dev(w["scalars"]), 13, 8, verify=True)
+        assert ei.value.code == M.MSM_ERR_OFF_CURVE, name
+    # the context stays usable after the error
+    say("verify after error")
+    assert np.array_equal(to_host(M.msm(to_dev(pts), to_dev(w["scalars"]), 13, 8)), want)
+
+
+def test_two_streams_growing_n():
+    """One context used alternately from two streams with growing n: every run sees
+    its own workspace contents (the context orders its calls across streams)."""
+    import torch
+    M = _msm()
+    ctx = M.Context(0)
+    s1, s2 = torch.cuda.Stream(DEV), torch.cuda.Stream(DEV)
+    try:
+        outs = []
+        for k, n in enumerate((500, 1200, 3000, 7000)):
+            w = wl.generate("n65536_c13", n=n)
+            pts = oracle.g1_from_scalars(w["dlogs"])
+            s = s1 if k % 2 == 0 else s2
+            with torch.cuda.stream(s):
+                dp, ds = to_dev(pts), to_dev(w["scalars"])
+                say("two streams n", n, "stream", k % 2)
+                out = ctx.run(dp, ds, 13, 8, stream=s)
+            outs.append((out, oracle.msm_pippenger(pts, w["scalars"], 13)))
+        torch.cuda.synchronize()
+        for out, want in outs:
+            assert np.array_equal(out.cpu().numpy().astype(np.uint32), want)
+    finally:
+        torch.cuda.synchronize()
+        ctx.close()
