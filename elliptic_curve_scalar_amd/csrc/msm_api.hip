@@ -114,6 +114,37 @@ int check_run_args(const msm_g1_affine* pts, const uint32_t* sc, size_t n, int c
   return MSM_OK;
 }
 
+// Workspace of msm_run_noalloc: a fixed device array, one copy per GPU the library
+// runs on, held until the process ends. Host code never uses its name as an address:
+// each device's copy is looked up once with hipGetSymbolAddress (noalloc_scratch_of).
+constexpr size_t NOALLOC_MAX_BYTES = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_MAX_BYTES];
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[NOALLOC_MAX_DEVICES] = {};
+hipError_t g_scratch_err[NOALLOC_MAX_DEVICES] = {};
+bool g_scratch_done[NOALLOC_MAX_DEVICES] = {};
+
+// Device address of this device's copy of scratch, looked up on the first call per
+// device (with that device current); nullptr and *err set when the lookup failed.
+void* noalloc_scratch_of(int device, hipError_t* err) {
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (device < 0 || device >= NOALLOC_MAX_DEVICES) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  if (!g_scratch_done[device]) {
+    void* ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_err[device] = e;
+    g_scratch_ptr[device] = (e == hipSuccess) ? ptr : nullptr;
+    g_scratch_done[device] = true;
+  }
+  *err = g_scratch_err[device];
+  return g_scratch_ptr[device];
+}
+
 }  // namespace
 
 enum Phase { PH_SORT = 0, PH_ACCUM = 1, PH_LEVEL = 2, PH_REDUCE = 3, PH_FINAL = 4, PH_XYZZ = 5 };
@@ -133,6 +164,7 @@ struct msm_ctx {
   hipEvent_t plan_ready = nullptr;   // the plan's copy to host_stats has completed
   hipEvent_t done = nullptr;         // the last kernel of the previous call has run
   bool has_done = false;
+  void* noalloc_ws = nullptr;        // this device's fixed workspace of msm_run_noalloc
   // phase timing: 0 off, 1 the batched-affine level kernels only, 2 every phase
   int timing = 0;
   std::vector<hipEvent_t> events;
@@ -160,10 +192,11 @@ struct PhaseMark {
   msm_ctx* ctx;
   hipStream_t st;
   int phase;
+  int level;  // the context's timing level, or 0 where no event may be created
   size_t e0 = SIZE_MAX;
   // level 1 brackets only the batched-affine level kernels, level 2 every phase
-  bool on() const { return ctx->timing >= 2 || (ctx->timing == 1 && phase == PH_LEVEL); }
-  PhaseMark(msm_ctx* c, hipStream_t s, int ph) : ctx(c), st(s), phase(ph) {
+  bool on() const { return level >= 2 || (level == 1 && phase == PH_LEVEL); }
+  PhaseMark(msm_ctx* c, hipStream_t s, int ph, int lvl) : ctx(c), st(s), phase(ph), level(lvl) {
     if (on()) e0 = mark(ctx, st);
   }
   void end() {
@@ -182,7 +215,8 @@ namespace {
 // The whole MSM on stream st with workspace ws (laid out by L); arguments checked.
 int run_pipeline(msm_ctx* ctx, const g1a* d_points, const uint32_t* d_scalars, size_t n, int c,
                  int S, int sched, int verify, char* ws, const Layout& L, hipStream_t st,
-                 g1a* d_out) {
+                 g1a* d_out, bool timed) {
+  const int tl = timed ? ctx->timing : 0;
   // calls on one context are ordered even across streams: wait for the previous one
   if (ctx->has_done) HIP_TRY(hipStreamWaitEvent(st, ctx->done, 0));
   if (n == 0) {
@@ -217,7 +251,7 @@ int run_pipeline(msm_ctx* ctx, const g1a* d_points, const uint32_t* d_scalars, s
   // counts are known, and the scatter, bucket init and the pair offsets of every level
   // the plan can require are queued behind it, so the GPU keeps working while the host
   // waits for the plan
-  PhaseMark ph_sort(ctx, st, PH_SORT);
+  PhaseMark ph_sort(ctx, st, PH_SORT, tl);
   HIP_TRY(launch_fill((uint32_t*)stats, sizeof(msm_stats) / 4, 0, st));
   HIP_TRY(launch_glv_prep(d_points, d_scalars, n32, pts2, halfs, stats, verify, st));
   HIP_TRY(launch_hist(halfs, m32, c32, L.nwin, L.chunk, L.nchunk, hist_blk, counts, rank, stats, st));
@@ -227,7 +261,7 @@ int run_pipeline(msm_ctx* ctx, const g1a* d_points, const uint32_t* d_scalars, s
   HIP_TRY(launch_scatter(halfs, m32, c32, L.nwin, L.chunk, L.nchunk, offsets, hist_blk, rank,
                          sorted_idx, st));
   ph_sort.end();
-  PhaseMark ph_acc(ctx, st, PH_ACCUM);
+  PhaseMark ph_acc(ctx, st, PH_ACCUM, tl);
   HIP_TRY(launch_bucket_init(counts, offsets, L.K, sorted_idx, pts, bsum, st));
   // pair offsets of every level at once: level l at poff_all + l (K + 1)
   uint32_t* const poff_all = poff;
@@ -254,10 +288,10 @@ int run_pipeline(msm_ctx* ctx, const g1a* d_points, const uint32_t* d_scalars, s
     if (l < La) {
       // batched affine adds, S per lane sharing one inversion
       const g1a* in = (l == 0) ? pts : aff[(l - 1) & 1];
-      PhaseMark ph_lvl(ctx, st, PH_LEVEL);
+      PhaseMark ph_lvl(ctx, st, PH_LEVEL, tl);
       HIP_TRY(launch_level(S, in, idx, aff[l & 1], bsum, counts, offsets, lvl_poff, L.K, np, l, st));
       ph_lvl.end();
-      if (ctx->timing) {
+      if (tl) {
         ctx->level_launches++;
         ctx->level_pairs += np;
         ctx->level_lanes += (np + S - 1) / S;
@@ -267,7 +301,7 @@ int run_pipeline(msm_ctx* ctx, const g1a* d_points, const uint32_t* d_scalars, s
       const bool in_aff = (l == La) || l == 0;
       const void* in = (l == 0) ? (const void*)pts
                        : in_aff ? (const void*)aff[(l - 1) & 1] : (const void*)xz[(l - 1) & 1];
-      PhaseMark ph_lvl(ctx, st, PH_XYZZ);
+      PhaseMark ph_lvl(ctx, st, PH_XYZZ, tl);
       HIP_TRY(launch_level_xyzz(in_aff, in, idx, xz[l & 1], bsum, counts, offsets, lvl_poff, L.K,
                                 np, l, st));
       ph_lvl.end();
@@ -276,15 +310,15 @@ int run_pipeline(msm_ctx* ctx, const g1a* d_points, const uint32_t* d_scalars, s
   ph_acc.end();
 
   // running sum per window, window combine
-  PhaseMark ph_red(ctx, st, PH_REDUCE);
+  PhaseMark ph_red(ctx, st, PH_REDUCE, tl);
   HIP_TRY(launch_reduce(bsum, c32, L.nwin, L.seg_len, L.nseg, part, win, st));
   ph_red.end();
-  PhaseMark ph_fin(ctx, st, PH_FINAL);
+  PhaseMark ph_fin(ctx, st, PH_FINAL, tl);
   HIP_TRY(launch_final(win, L.nwin, c32, d_out, st));
   ph_fin.end();
   if (verify) HIP_TRY(launch_verify_point(d_out, &stats->bad_out, st));
   HIP_TRY(hipEventRecord(ctx->done, st));
-  if (ctx->timing) ctx->runs++;
+  if (tl) ctx->runs++;
   if (verify) {
     HIP_TRY(hipMemcpyAsync(&ctx->host_stats->bad_out, &stats->bad_out, 4, hipMemcpyDeviceToHost, st));
     HIP_TRY(hipStreamSynchronize(st));
@@ -330,6 +364,11 @@ int msm_ctx_create(int device, msm_ctx** out) {
   } else if (hipEventCreateWithFlags(&ctx->plan_ready, hipEventDisableTiming) != hipSuccess ||
              hipEventCreateWithFlags(&ctx->done, hipEventDisableTiming) != hipSuccess) {
     rc = fail(MSM_ERR_HIP, "event creation failed%s");
+  } else {
+    // set-up of msm_run_noalloc: this device's copy of its fixed workspace; a failed
+    // lookup only disables that entry point (it reports the error)
+    hipError_t e;
+    ctx->noalloc_ws = noalloc_scratch_of(device, &e);
   }
   if (rc != MSM_OK) {
     msm_ctx_destroy(ctx);
@@ -383,7 +422,29 @@ int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scala
     ws = (char*)ctx->ws;
   }
   return run_pipeline(ctx, (const g1a*)d_points, d_scalars, n, c, S, sched, verify, ws, L, st,
-                      (g1a*)d_out);
+                      (g1a*)d_out, true);
+}
+
+int msm_run_noalloc(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scalars,
+                    size_t n, int c, int S, int sched, int verify, void* stream,
+                    msm_g1_affine* d_out) {
+  if (!ctx) return fail(MSM_ERR_ARG, "ctx is NULL%s");
+  int rc = check_run_args(d_points, d_scalars, n, c, S, sched, verify, d_out);
+  if (rc) return rc;
+  if (sched == MSM_SCHED_WALKER) return fail(MSM_ERR_ARG, "the stream-walker schedule is not built%s");
+  const Layout L = plan(n, c);
+  if (L.total > NOALLOC_MAX_BYTES)
+    return fail(MSM_ERR_ARG,
+                "msm_workspace_bytes(n, c, S) exceeds the fixed workspace of msm_run_noalloc "
+                "(MSM_NOALLOC_MAX_BYTES); use msm_run%s");
+  if (!ctx->noalloc_ws) {
+    hipError_t e;
+    (void)noalloc_scratch_of(ctx->device, &e);
+    return fail(MSM_ERR_HIP, "HIP error: %s (looking up the fixed workspace)", hipGetErrorString(e));
+  }
+  HIP_TRY(hipSetDevice(ctx->device));
+  return run_pipeline(ctx, (const g1a*)d_points, d_scalars, n, c, S, sched, verify,
+                      (char*)ctx->noalloc_ws, L, (hipStream_t)stream, (g1a*)d_out, false);
 }
 
 int msm_ctx_set_affine_levels(msm_ctx* ctx, int levels) {

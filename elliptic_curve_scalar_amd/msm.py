@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libmsm.so")
 MSM_OK, MSM_ERR_ARG, MSM_ERR_HIP, MSM_ERR_OOM, MSM_ERR_RANGE, MSM_ERR_OFF_CURVE = 0, -1, -2, -3, -4, -5
 MSM_SCHED_PAIR_TREE, MSM_SCHED_WALKER = 0, 1
 MSM_MAX_N = 1 << 26
+MSM_NOALLOC_MAX_BYTES = 64 << 20
 VALID_S = (4, 8, 16, 32)
 
 # Exported C symbols, each with (restype, argtypes).
@@ -31,6 +32,7 @@ SYMBOLS = {
     "msm_workspace_bytes": (_S, [_S, _I, _I]),
     "msm_run": (_I, [_P, _P, _P, _S, _I, _I, _I, _I, _P, _S, _P, _P]),
     "msm": (_I, [_P, _P, _S, _I, _P]),
+    "msm_run_noalloc": (_I, [_P, _P, _P, _S, _I, _I, _I, _I, _P, _P]),
     "msm_g1_from_scalars": (_I, [_P, _S, _P, _P]),
     "msm_ctx_set_affine_levels": (_I, [_P, _I]),
     "msm_ctx_set_timing": (_I, [_P, _I]),

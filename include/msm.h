@@ -133,6 +133,27 @@ int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scala
             void* stream, msm_g1_affine* d_out);
 
 /*
+ * msm_run without allocation, for callers that cannot allocate device memory while
+ * they run (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same arguments and results as msm_run with d_workspace = NULL, except
+ * that the workspace is a fixed device array of MSM_NOALLOC_MAX_BYTES built into the
+ * library (one copy per GPU, held until the process ends) instead of the context's
+ * growable one, and the context's phase timing is not recorded. The call allocates
+ * nothing: no hipMalloc, no pinned memory, no events (the context made those when it
+ * was created). Limits: msm_workspace_bytes(n, c, S) must not exceed
+ * MSM_NOALLOC_MAX_BYTES, else MSM_ERR_ARG (c = 8 or 13 allows n up to about 10,000;
+ * c = 16 needs more than the array at any n). All calls on one GPU share the one
+ * array: calls that overlap on a GPU (from two contexts, or two host threads) race
+ * and give wrong results; calls on one context are ordered as for msm_run. Like
+ * msm_run it blocks once on `stream` for the plan, so it cannot itself be captured
+ * into a graph. MSM_ERR_HIP if the array's address could not be looked up.
+ */
+#define MSM_NOALLOC_MAX_BYTES ((size_t)64 << 20)
+int msm_run_noalloc(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scalars,
+                    size_t n, int c, int S, int sched, int verify, void* stream,
+                    msm_g1_affine* d_out);
+
+/*
  * Synchronous convenience form, the shape msm(points_affine, scalars, n, c) -> point:
  * device inputs, result written to host memory h_out. Uses a per-device default
  * context (created on first use), S = 8, the pair-tree schedule, no verify and the

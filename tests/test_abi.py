@@ -118,6 +118,10 @@ def test_run_argument_errors_without_gpu():
     assert L.msm_run(ctx, p, p, 16, 13, 8, 0, 0, ctypes.c_void_p((1 << 20) + 16), need, None,
                      out) == M.MSM_ERR_ARG
     assert M.MSM_ERR_OFF_CURVE == -5 and (M.MSM_SCHED_PAIR_TREE, M.MSM_SCHED_WALKER) == (0, 1)
+    # the no-allocation entry point checks the same arguments
+    assert L.msm_run_noalloc(None, p, p, 16, 13, 8, 0, 0, None, out) == M.MSM_ERR_ARG
+    assert L.msm_run_noalloc(ctx, p, p, 16, 13, 8, 3, 0, None, out) == M.MSM_ERR_ARG
+    assert L.msm_run_noalloc(ctx, p, p, 16, 17, 8, 0, 0, None, out) == M.MSM_ERR_ARG
 
 
 def test_binding_refuses_host_tensors():
