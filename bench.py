@@ -84,6 +84,10 @@ def main() -> int:
     ap.add_argument("--S", type=int, default=None, help="override the workload's S")
     ap.add_argument("--affine-levels", type=int, default=None,
                     help="pair-tree levels done with batched affine adds (-1: all)")
+    ap.add_argument("--sched", type=int, default=0,
+                    help="accumulate schedule: 0 pair tree, 1 stream walker")
+    ap.add_argument("--walker-state", type=int, default=1,
+                    help="stream walker slot state: 1 device buffer, 0 private memory")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0,
                     help="CPU seconds for the oracle baseline (0 disables it)")
     ap.add_argument("--copy-mb", type=int, default=0,
@@ -116,9 +120,10 @@ def main() -> int:
     ctx = M.context(dev)
     if args.affine_levels is not None:
         ctx.set_affine_levels(args.affine_levels)
+    ctx.set_walker_state(args.walker_state)
     out = torch.empty(16, dtype=torch.uint32, device=dev)
     for _ in range(args.warmup):
-        ctx.run(points, scalars, c, S, out=out)
+        ctx.run(points, scalars, c, S, out=out, sched=args.sched)
     torch.cuda.synchronize()
     log(f"[bench] warmup done ({args.warmup})")
 
@@ -131,7 +136,7 @@ def main() -> int:
     t0 = time.perf_counter()
     for _ in range(args.steps):
         ts = time.perf_counter()
-        ctx.run(points, scalars, c, S, out=out)
+        ctx.run(points, scalars, c, S, out=out, sched=args.sched)
         torch.cuda.synchronize()
         lat.append((time.perf_counter() - ts) * 1e3)
     torch.cuda.synchronize()
@@ -140,7 +145,7 @@ def main() -> int:
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     ctx.set_timing(2)
     for _ in range(3):
-        ctx.run(points, scalars, c, S, out=out)
+        ctx.run(points, scalars, c, S, out=out, sched=args.sched)
     torch.cuda.synchronize()
     tm_phases = ctx.timing_read()
     ctx.set_timing(0)
@@ -219,7 +224,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": f"BN254 G1 MSM, n={n}, c={c}, S={S}, independent random points "
                                f"r_i*G, scalars uniform in [0, r) ({args.workload})",
-                   "n": n, "c": c, "S": S},
+                   "n": n, "c": c, "S": S, "sched": ["pair_tree", "walker"][args.sched]},
         "latency_ms": {"median": statistics.median(lat), "min": min(lat)},
         "phases_ms_per_step": phases,
         "roofline": roofline,

@@ -1,33 +1,95 @@
 // Bucket reduction and window combine of the BN254 G1 bucket MSM (gfx950), and their
-// launchers:
-//   k_rsum_tree   per window, segments of buckets: sum_b b * B_b by running sums,
-//                 summed per block through an LDS tree
-//   k_tree_sum    per window: the blocks' partial sums -> W_j
-//   k_final       Q = sum_j 2^(c j) W_j by doubling, then affine
+// launchers.
+//
+// After the accumulate, window j (W windows of c bits over the GLV half-scalars) holds
+// 2^(c-1) bucket sums B_{j,b}; slot b carries the weight w_b = floor(b / f_j) + 1 (f_j =
+// window_spread), and the result is
+//     Q = sum_j 2^(c j) W_j,   W_j = sum_b w_b B_{j,b}.
+// A running sum over all slots of a window would be one chain of 2^c additions. Instead
+// the slots are cut into segments of L = 2^lambda slots, s = 0 .. nseg - 1:
+//     T_s = sum_{b in s} B_b,   R_s = sum_{b in s} (w_b - w_lo(s)) B_b,
+// where w_lo(s) is the weight of the segment's first slot (R_s is a running sum over at
+// most L slots), so that
+//     W_j = sum_s (R_s + T_s) + sum_s (w_lo(s) - 1) T_s,
+// and w_lo(s) - 1 = (s L) >> log2(f_j) is a bit field of s. Writing it out bit by bit,
+//     Q = sum_j 2^(c j) sum_s (R_s + T_s) + sum_{j, kappa} 2^(c j + kappa) sum_{s : bit kappa
+//         of w_lo(s) - 1 is set} T_s.
+// Each term is a plane: a plain sum of segment values (no weights), which a tree adds in
+// log depth, times a power of two e <= 126, which a run of e doublings gives. Every plane
+// is summed and doubled in parallel, and the planes are then added in groups. The
+// longest chain is one plane's doublings instead of a running sum per window followed
+// by c (W - 1) doublings of the top window.
+//
+//   k_seg_sums     one quad per (window, segment): T_s and P_s = R_s + T_s
+//   k_plane_sums   one block per 256 elements of a plane: their sum (LDS tree)
+//   k_plane_chain  one wavefront per plane: the plane's partial sums (butterfly),
+//                  2^e S by a run of doublings; the last wavefront of each group of 16
+//                  planes adds the group, the last group adds the groups and converts
+//                  the result to affine
 #include <hip/hip_runtime.h>
+#include <string.h>
 
 #include "glv.hpp"
 #include "kern_util.hpp"
 
 namespace msmk {
 
-// Window j has 2^(c-1) bucket slots; slot b holds points whose digit has magnitude
-// floor(b / f) + 1 (f = window_spread), so W_j = sum_b (floor(b / f) + 1) B_b. Segment s
-// covers slots [lo, hi). Running from the top slot down, T sums the slots so far and R
-// adds T at every slot that is a multiple of f; then R = sum_b (floor(b / f) -
-// ceil(lo / f) + 1) B_b, and the segment's share of W_j is R + ceil(lo / f) T.
-__device__ __forceinline__ xyzz rsum_segment(const xyzz_st* __restrict__ bsum, uint32_t c,
-                                             uint32_t nwin, uint32_t seg_len, uint32_t j,
-                                             uint32_t s, int q) {
-  const uint32_t nb = 1u << (c - 1);
-  const uint32_t lo = s * seg_len, hi = min(nb, (s + 1) * seg_len);
+// Element i of a plane: its segment index. sel 0 (the (R + T) plane) takes every
+// segment; sel = beta + 1 takes the segments with bit beta set, in increasing order.
+__device__ __forceinline__ uint32_t plane_segment(uint32_t sel, uint32_t i) {
+  if (sel == 0) return i;
+  const uint32_t beta = sel - 1;
+  return ((i >> beta) << (beta + 1)) | (1u << beta) | (i & ((1u << beta) - 1u));
+}
+
+// Coherent 128-byte load of a point another block has just written (after the fence
+// that followed its counter's atomic): device-scope atomic loads bypass this CU's cache.
+__device__ __forceinline__ xyzz xyzz_load_coherent(const xyzz_st* p) {
+  xyzz a;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    a.X.v[i] = __hip_atomic_load(&p->w[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    a.Y.v[i] = __hip_atomic_load(&p->w[8 + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    a.ZZ.v[i] = __hip_atomic_load(&p->w[16 + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    a.ZZZ.v[i] = __hip_atomic_load(&p->w[24 + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return a;
+}
+
+// Sum over the first `used` quads of a wavefront (1 <= used <= 16; the others hold the
+// point at infinity): a ds_bpermute butterfly over the smallest power-of-two group of quads
+// that covers them, ceil(log2 used) additions deep. Quad 0 ends with the total.
+__device__ __forceinline__ xyzz wave_quad_sum(xyzz acc, uint32_t used, int q) {
+#pragma unroll 1
+  for (uint32_t m = 4; m < 4 * used; m <<= 1) acc = quad_add(acc, xyzz_shfl_xor(acc, (int)m), q);
+  return acc;
+}
+
+// Segment sums, one quad per (window j, segment s) at g = j nseg + s. Running from the
+// segment's top slot down, T adds each slot and R adds T after the lowest slot of every
+// weight group except the segment's lowest, so R = sum (w_b - w_lo) B_b.
+__global__ void __launch_bounds__(256) k_seg_sums(const xyzz_st* __restrict__ bsum, uint32_t c,
+                                                  uint32_t nwin, uint32_t lambda, uint32_t nseg,
+                                                  xyzz_st* __restrict__ tseg,
+                                                  xyzz_st* __restrict__ pseg) {
+  const uint32_t g = (blockIdx.x * blockDim.x + threadIdx.x) >> 2;
+  const int q = (int)(threadIdx.x & 3u);
+  if (g >= nwin * nseg) return;  // whole quads leave together; no barrier follows
+  const uint32_t j = g / nseg, s = g % nseg;
+  const uint32_t slots = 1u << (c - 1);
+  const uint32_t lo = s << lambda, hi = min(slots, (s + 1) << lambda);
   const uint32_t f = window_spread(c, nwin, j);
+  const xyzz_st* B = bsum + (size_t)j * slots;
   xyzz T = xyzz_inf(), R = xyzz_inf();
   for (uint32_t b = hi; b-- > lo;) {
-    T = quad_add(T, xyzz_load(bsum + (size_t)j * nb + b), q);
-    if ((b & (f - 1)) == 0) R = quad_add(R, T, q);
+    T = quad_add(T, xyzz_load(B + b), q);
+    if (b > lo && (b & (f - 1u)) == 0) R = quad_add(R, T, q);
   }
-  return quad_add(R, quad_mul_small(T, (lo + f - 1) / f, q), q);
+  const xyzz P = quad_add(R, T, q);
+  if (q == 0) {
+    xyzz_store(tseg + g, T);
+    xyzz_store(pseg + g, P);
+  }
 }
 
 // The 64 quads of a block add their points through an LDS tree; thread 0 stores the sum.
@@ -46,88 +108,129 @@ __device__ __forceinline__ void block_quad_sum(xyzz acc, xyzz_st* lds, xyzz_st* 
   if (threadIdx.x == 0) xyzz_store(out, acc);
 }
 
-// Running sums and the first tree pass in one launch: block b of window j takes segments
-// [64 b, 64 b + 64) of the window's nseg, one per quad, and writes their sum to
-// out[j nblk + b] (nblk = ceil(nseg / 64); nseg <= 4096 for every c, so a window needs
-// at most 64 blocks).
-__global__ void __launch_bounds__(256) k_rsum_tree(const xyzz_st* __restrict__ bsum, uint32_t c,
-                                                   uint32_t nwin, uint32_t seg_len, uint32_t nseg,
-                                                   uint32_t nblk, xyzz_st* __restrict__ out) {
+// Elements of a plane, and its blocks of partial sums (PLANE_PER_BLOCK elements each).
+constexpr uint32_t PLANE_PER_QUAD = 4;
+constexpr uint32_t PLANE_PER_BLOCK = 64 * PLANE_PER_QUAD;
+
+__device__ __forceinline__ uint32_t plane_count(const plane_table& pt, uint32_t sel) {
+  return sel ? pt.nseg >> 1 : pt.nseg;
+}
+
+// Block (p, k) of plane p adds the plane's elements [256 k, 256 k + 256): four per quad,
+// then the block's LDS tree; the sum goes to part[p nb + k]. A plane of segment totals has
+// half as many elements as one of R + T values, so its upper blocks have nothing to do
+// and leave at once (before any barrier, all threads together).
+__global__ void __launch_bounds__(256) k_plane_sums(const xyzz_st* __restrict__ tseg,
+                                                    const xyzz_st* __restrict__ pseg,
+                                                    plane_table pt, xyzz_st* __restrict__ part) {
   __shared__ xyzz_st lds[64];
-  const uint32_t j = blockIdx.x / nblk, b = blockIdx.x % nblk, quad = threadIdx.x >> 2;
+  const uint32_t p = blockIdx.x / pt.nb, k = blockIdx.x % pt.nb;
+  const uint32_t ent = pt.e[p];
+  const uint32_t j = (ent >> 8) & 0xffu, sel = ent >> 16;
+  const uint32_t cnt = plane_count(pt, sel);
+  if (k * PLANE_PER_BLOCK >= cnt) return;
+  const xyzz_st* src = (sel ? tseg : pseg) + (size_t)j * pt.nseg;
+  const uint32_t quad = threadIdx.x >> 2;
   const int q = (int)(threadIdx.x & 3u);
-  const uint32_t sg = b * 64 + quad;
+  const uint32_t i0 = k * PLANE_PER_BLOCK + PLANE_PER_QUAD * quad;
   xyzz acc = xyzz_inf();
-  if (sg < nseg) acc = rsum_segment(bsum, c, nwin, seg_len, j, sg, q);
-  block_quad_sum(acc, lds, out + blockIdx.x);
+  for (uint32_t i = i0; i < i0 + PLANE_PER_QUAD && i < cnt; i++)
+    acc = quad_add(acc, xyzz_load(src + plane_segment(sel, i)), q);
+  block_quad_sum(acc, lds, part + blockIdx.x);
 }
 
-// Sums of groups of n consecutive XYZZ points, one wavefront per group: quad g adds
-// items g, g + 16, ..., then a butterfly over the 16 quads (ds_bpermute, four additions
-// deep) leaves the sum in every quad. The second pass, from the partials of k_rsum_tree
-// to the window sums.
-__global__ void __launch_bounds__(64) k_tree_sum(const xyzz_st* __restrict__ in, uint32_t n,
-                                                 xyzz_st* __restrict__ out) {
-  const uint32_t g = blockIdx.x, quad = threadIdx.x >> 2;
+// One wavefront per plane p: S = sum of the plane's nb partials, then 2^e S (e = the
+// plane's exponent) by a run of doublings (quad.hpp). Planes are in order of decreasing
+// e, so the long runs start first. The last wavefront to finish in each group of 16
+// planes (counted by join[group]) adds the group's results; the last group to finish
+// (join[MAX_PLANE_GROUPS]) adds the group sums and writes the affine result. The counters
+// start at zero (cleared with the plan statistics before the MSM).
+__global__ void __launch_bounds__(64) k_plane_chain(const xyzz_st* __restrict__ part,
+                                                    plane_table pt, xyzz_st* res, xyzz_st* gres,
+                                                    uint32_t* join, g1a* out) {
+  const uint32_t p = blockIdx.x, quad = threadIdx.x >> 2;
   const int q = (int)(threadIdx.x & 3u);
+  const uint32_t e = pt.e[p] & 0xffu;
+  const uint32_t nblk = (plane_count(pt, pt.e[p] >> 16) + PLANE_PER_BLOCK - 1) / PLANE_PER_BLOCK;
   xyzz acc = xyzz_inf();
-  for (uint32_t i = quad; i < n; i += 16) acc = quad_add(acc, xyzz_load(in + (size_t)g * n + i), q);
-#pragma unroll
-  for (int m = 4; m < 64; m <<= 1) acc = quad_add(acc, xyzz_shfl_xor(acc, m), q);
-  if (threadIdx.x == 0) xyzz_store(out + g, acc);
+  for (uint32_t i = quad; i < nblk; i += 16) acc = quad_add(acc, xyzz_load(part + (size_t)p * pt.nb + i), q);
+  acc = wave_quad_sum(acc, min(nblk, 16u), q);
+  acc = quad_dbl_n(acc, e, q);
+  if (threadIdx.x == 0) xyzz_store(res + p, acc);
+  __threadfence();
+  const uint32_t grp = p >> 4, ngroups = (pt.n + 15u) >> 4;
+  const uint32_t gsize = min(16u, pt.n - 16u * grp);
+  uint32_t old = 0;
+  if (threadIdx.x == 0) old = atomicAdd(&join[grp], 1u);
+  old = (uint32_t)__shfl((int)old, 0, 64);
+  if (old + 1u != gsize) return;
+  __threadfence();
+  acc = (quad < gsize) ? xyzz_load_coherent(res + 16u * grp + quad) : xyzz_inf();
+  acc = wave_quad_sum(acc, gsize, q);
+  if (threadIdx.x == 0) xyzz_store(gres + grp, acc);
+  __threadfence();
+  if (threadIdx.x == 0) old = atomicAdd(&join[MAX_PLANE_GROUPS], 1u);
+  old = (uint32_t)__shfl((int)old, 0, 64);
+  if (old + 1u != ngroups) return;
+  __threadfence();
+  acc = (quad < ngroups) ? xyzz_load_coherent(gres + quad) : xyzz_inf();
+  acc = wave_quad_sum(acc, ngroups, q);
+  const aff a = xyzz_to_aff(acc);
+  if (threadIdx.x == 0) aff_store(out, a);
 }
 
-// ---- window combine ----------------------------------------------------------------
-// The combine is one long chain (c (W - 1) doublings), so its time is latency, not
-// throughput. The four lanes of a quad split each round of products (quad.hpp): a run
-// of doublings with one round of lookahead costs 2.5 product latencies per doubling,
-// an addition 4. Every quad computes its own chain, so every branch is uniform within
-// a quad.
+// ------------------------------------------------------------------ host side
+// log2 of the segment length: segments of 4 slots up to c = 14, 8 at c = 15 and 16, so a
+// window has at most 4096 segments and a plane at most 16 blocks of partial sums.
+static uint32_t seg_log2(uint32_t c) { return c >= 15 ? 3u : 2u; }
 
-// Q = sum_j 2^(c j) W_j, then to affine. Two wavefronts: wave 0 doubles the top window's
-// sum c (W - 1) times. In wave 1, quad g doubles W_g c g times (at most c (W - 2)), and a
-// tree over the quads adds the results (four additions deep), so no addition sits on the
-// longest chain; with more than 17 windows (c <= 7) wave 1 runs Horner over the lower
-// windows instead. One addition joins the two waves. W >= 8 for every c <= 16.
-__global__ void __launch_bounds__(128) k_final(const xyzz_st* __restrict__ win, uint32_t nwin,
-                                               uint32_t c, g1a* out) {
-  __shared__ xyzz_st low;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane & 3;
-  const uint32_t g = (uint32_t)lane >> 2;
-  xyzz acc;
-  if (wave == 0) {
-    acc = quad_dbl_n(xyzz_load(win + nwin - 1), c * (nwin - 1), q);
-  } else {
-    if (nwin - 1 <= 16) {
-      acc = (g < nwin - 1) ? quad_dbl_n(xyzz_load(win + g), c * g, q) : xyzz_inf();
-#pragma unroll
-      for (int m = 4; m < 64; m <<= 1) acc = quad_add(acc, xyzz_shfl_xor(acc, m), q);
-    } else {
-      acc = xyzz_load(win + nwin - 2);
-      for (int j = (int)nwin - 3; j >= 0; j--) acc = quad_add(quad_dbl_n(acc, c, q), xyzz_load(win + j), q);
+plane_table make_planes(uint32_t c, uint32_t nwin) {
+  plane_table pt;
+  memset(&pt, 0, sizeof pt);
+  const uint32_t lambda = seg_log2(c);
+  const uint32_t slots = 1u << (c - 1);
+  const uint32_t nseg = slots > (1u << lambda) ? slots >> lambda : 1u;
+  uint32_t lgseg = 0;
+  while ((1u << lgseg) < nseg) lgseg++;
+  pt.nseg = nseg;
+  pt.lambda = lambda;
+  pt.nb = (nseg + PLANE_PER_BLOCK - 1) / PLANE_PER_BLOCK;
+  // (exponent, window, selector) of every plane
+  uint32_t tmp[MAX_PLANES];
+  uint32_t n = 0;
+  for (uint32_t j = 0; j < nwin; j++) {
+    const uint32_t phi = (j + 1 == nwin) ? c * nwin - 128 : 0;  // log2 of window_spread
+    tmp[n++] = (c * j) | (j << 8);                               // the (R + T) plane
+    for (uint32_t beta = 0; beta < lgseg; beta++) {
+      // bit kappa of w_lo(s) - 1 = (s << lambda) >> phi is bit kappa + phi - lambda of s
+      if (beta + lambda < phi) continue;
+      const uint32_t kappa = beta + lambda - phi;
+      tmp[n++] = (c * j + kappa) | (j << 8) | ((beta + 1) << 16);
     }
-    if (lane == 0) xyzz_store(&low, acc);
   }
-  __syncthreads();
-  if (wave == 0) {
-    acc = quad_add(acc, xyzz_load(&low), q);
-    const aff a = xyzz_to_aff(acc);
-    if (lane == 0) aff_store(out, a);
-  }
+  // decreasing exponent: the longest runs of doublings are dispatched first
+  for (uint32_t a = 1; a < n; a++)
+    for (uint32_t b = a; b > 0 && (tmp[b] & 0xffu) > (tmp[b - 1] & 0xffu); b--) {
+      const uint32_t t = tmp[b];
+      tmp[b] = tmp[b - 1];
+      tmp[b - 1] = t;
+    }
+  pt.n = n;
+  for (uint32_t i = 0; i < n; i++) pt.e[i] = tmp[i];
+  return pt;
 }
 
-// ------------------------------------------------------------------ launchers
-hipError_t launch_reduce(const xyzz_st* bsum, uint32_t c, uint32_t nwin, uint32_t seg_len,
-                         uint32_t nseg, xyzz_st* part, xyzz_st* win, hipStream_t s) {
-  const uint32_t nblk = reduce_blocks(nseg);
-  if ((size_t)nblk * 64 < nseg) return hipErrorInvalidValue;  // one segment per quad
-  k_rsum_tree<<<nwin * nblk, 256, 0, s>>>(bsum, c, nwin, seg_len, nseg, nblk, part);
-  k_tree_sum<<<nwin, 64, 0, s>>>(part, nblk, win);
+hipError_t launch_reduce(const xyzz_st* bsum, uint32_t c, uint32_t nwin, const plane_table& pt,
+                         xyzz_st* tseg, xyzz_st* pseg, xyzz_st* part, hipStream_t s) {
+  const size_t quads = (size_t)nwin * pt.nseg;
+  k_seg_sums<<<grid_for(quads * 4, 256), 256, 0, s>>>(bsum, c, nwin, pt.lambda, pt.nseg, tseg, pseg);
+  k_plane_sums<<<pt.n * pt.nb, 256, 0, s>>>(tseg, pseg, pt, part);
   return hipGetLastError();
 }
 
-hipError_t launch_final(const xyzz_st* win, uint32_t nwin, uint32_t c, g1a* out, hipStream_t s) {
-  k_final<<<1, 128, 0, s>>>(win, nwin, c, out);
+hipError_t launch_final(const xyzz_st* part, const plane_table& pt, xyzz_st* res, xyzz_st* gres,
+                        uint32_t* join, g1a* out, hipStream_t s) {
+  k_plane_chain<<<pt.n, 64, 0, s>>>(part, pt, res, gres, join, out);
   return hipGetLastError();
 }
 

@@ -93,6 +93,43 @@ __device__ __forceinline__ xyzz xyzz_shfl_xor(const xyzz& a, int mask) {
   return r;
 }
 
+// Bucket of a pair: the largest k in [0, n) with a[k] <= x, for the non-decreasing pair
+// offsets a of a level (n + 1 entries, a[0] = 0 <= x < a[n]). Each read is a dependent
+// load, so rather than bisecting all n buckets the search first tests, with two loads
+// issued together, whether the answer lies within GUESS_SPAN buckets of a guess, and
+// then bisects that bracket (about log2(2 GUESS_SPAN) reads) or, when it does not (skewed
+// bucket sizes), the whole array. Every lane runs the same code path, so a wavefront
+// waits for its slowest lane's reads and for nothing else.
+constexpr uint32_t GUESS_SPAN = 128;
+
+// Largest k in [lo, hi) with a[k] <= x, given a[lo] <= x < a[hi].
+__device__ __forceinline__ uint32_t bisect_le(const uint32_t* a, uint32_t lo, uint32_t hi, uint32_t x) {
+  while (hi - lo > 1) {
+    const uint32_t mid = lo + ((hi - lo) >> 1);
+    if (a[mid] <= x) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// The bucket of x, searched from the guess g.
+__device__ __forceinline__ uint32_t bucket_of(const uint32_t* a, uint32_t n, uint32_t x, uint32_t g) {
+  if (g >= n) g = n - 1;
+  uint32_t lo = g > GUESS_SPAN ? g - GUESS_SPAN : 0u;
+  uint32_t hi = min(g + GUESS_SPAN, n);
+  const bool in = (a[lo] <= x) & (a[hi] > x);
+  if (!in) {
+    lo = 0;
+    hi = n;
+  }
+  return bisect_le(a, lo, hi, x);
+}
+
+// Guess for the bucket of pair p: pairs spread evenly over the K buckets.
+__device__ __forceinline__ uint32_t bucket_guess(uint32_t p, uint32_t K, uint32_t npairs) {
+  return (uint32_t)(((uint64_t)p * K) / npairs);
+}
+
 inline unsigned grid_for(size_t n, unsigned block) { return (unsigned)((n + block - 1) / block); }
 
 }  // namespace msmk

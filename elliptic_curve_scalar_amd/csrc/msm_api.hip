@@ -33,30 +33,24 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Signed c-bit digits of the GLV half-scalars (magnitudes below 2^127) need W c >= 128.
 int num_windows(int c) { return (128 + c - 1) / c; }
 
-// Buckets per running-sum segment: enough segments to spread the reduction over the
-// chip, never fewer than 4 buckets per segment.
-uint32_t segment_length(int c, int nwin) {
-  size_t total = ((size_t)nwin) << (c - 1);
-  uint32_t g = 4;
-  while ((size_t)g * 32768 < total && g < 256) g <<= 1;
-  if (g > (1u << (c - 1))) g = 1u << (c - 1);
-  return g;
-}
-
 struct Layout {
   size_t stats, halfs, pts2, counts, offsets, rank, hist_blk, poff, block_sums, sorted_idx, aff_a, aff_b,
-      xz_a, xz_b, bsum, part, win;
+      xz_a, xz_b, bsum, tseg, pseg, part, res, gres;
+  // stream-walker buffers, sharing the pair-tree level buffers' region (one or the other
+  // runs): device slot state, partial sums and their buckets, for up to Zmax slots
+  size_t w_acc, w_kst, w_head, w_tail, w_head_k, w_tail_k;
+  size_t Zmax;
   size_t total;
-  uint32_t K, nwin, seg_len, nseg, chunk, nchunk;
+  uint32_t K, nwin, chunk, nchunk;
   size_t E_max, half;
+  plane_table planes;
 };
 
-Layout plan(size_t n, int c) {
+Layout plan(size_t n, int c, int S) {
   Layout L;
   L.nwin = (uint32_t)num_windows(c);
   L.K = L.nwin << (c - 1);  // 2^(c-1) bucket slots per window (signed digits)
-  L.seg_len = segment_length(c, (int)L.nwin);
-  L.nseg = ((1u << (c - 1)) + L.seg_len - 1) / L.seg_len;
+  L.planes = make_planes((uint32_t)c, L.nwin);
   L.E_max = 2 * n * L.nwin;  // 2n GLV points
   L.half = (L.E_max + L.K) / 2 + 1;  // elements of a level >= 1 buffer
   size_t off = 0;
@@ -84,13 +78,27 @@ Layout plan(size_t n, int c) {
   L.poff = take((size_t)MAX_LEVELS * ((size_t)L.K + 1) * 4);  // pair offsets of every level
   L.block_sums = take((size_t)MAX_LEVELS * (scan_blocks(L.K) + 1) * 4);
   L.sorted_idx = take(L.E_max * 4);
+  const size_t region = off;
   L.aff_a = take(L.half * sizeof(g1a));
   L.aff_b = take(L.half * sizeof(g1a));
   L.xz_a = take(L.half * sizeof(xyzz_st));
   L.xz_b = take(L.half * sizeof(xyzz_st));
+  const size_t levels_end = off;
+  off = region;
+  L.Zmax = (size_t)walk_lanes(L.E_max, S) * (size_t)S;
+  L.w_acc = take(L.Zmax * 64);
+  L.w_kst = take(L.Zmax * 4);
+  L.w_head = take(L.Zmax * sizeof(xyzz_st));
+  L.w_tail = take(L.Zmax * sizeof(xyzz_st));
+  L.w_head_k = take(L.Zmax * 4);
+  L.w_tail_k = take(L.Zmax * 4);
+  if (off < levels_end) off = levels_end;
   L.bsum = take((size_t)L.K * sizeof(xyzz_st));
-  L.part = take((size_t)L.nwin * reduce_blocks(L.nseg) * sizeof(xyzz_st));
-  L.win = take((size_t)L.nwin * sizeof(xyzz_st));
+  L.tseg = take((size_t)L.nwin * L.planes.nseg * sizeof(xyzz_st));
+  L.pseg = take((size_t)L.nwin * L.planes.nseg * sizeof(xyzz_st));
+  L.part = take((size_t)L.planes.n * L.planes.nb * sizeof(xyzz_st));
+  L.res = take((size_t)L.planes.n * sizeof(xyzz_st));
+  L.gres = take((size_t)MAX_PLANE_GROUPS * sizeof(xyzz_st));
   L.total = off;
   return L;
 }
@@ -157,6 +165,7 @@ struct Span {
 struct msm_ctx {
   int device = 0;
   int affine_levels = 1;  // leading pair-tree levels done with batched affine adds
+  int walker_device_state = 1;  // stream walker: accumulators on the device (1) or private (0)
   void* ws = nullptr;
   size_t ws_bytes = 0;
   msm_stats* host_stats = nullptr;  // pinned: the plan, then the result's verify flag
@@ -238,8 +247,11 @@ int run_pipeline(msm_ctx* ctx, const g1a* d_points, const uint32_t* d_scalars, s
   g1a* aff[2] = {(g1a*)(ws + L.aff_a), (g1a*)(ws + L.aff_b)};
   xyzz_st* xz[2] = {(xyzz_st*)(ws + L.xz_a), (xyzz_st*)(ws + L.xz_b)};
   xyzz_st* bsum = (xyzz_st*)(ws + L.bsum);
+  xyzz_st* tseg = (xyzz_st*)(ws + L.tseg);
+  xyzz_st* pseg = (xyzz_st*)(ws + L.pseg);
   xyzz_st* part = (xyzz_st*)(ws + L.part);
-  xyzz_st* win = (xyzz_st*)(ws + L.win);
+  xyzz_st* res = (xyzz_st*)(ws + L.res);
+  xyzz_st* gres = (xyzz_st*)(ws + L.gres);
   const g1a* pts = pts2;  // 2n points: P_i and phi(P_i)
   uint32_t n32 = (uint32_t)n, m32 = 2 * (uint32_t)n, c32 = (uint32_t)c;
 
@@ -265,8 +277,9 @@ int run_pipeline(msm_ctx* ctx, const g1a* d_points, const uint32_t* d_scalars, s
   HIP_TRY(launch_bucket_init(counts, offsets, L.K, sorted_idx, pts, bsum, st));
   // pair offsets of every level at once: level l at poff_all + l (K + 1)
   uint32_t* const poff_all = poff;
-  HIP_TRY(launch_scan(counts, L.K, 0, level_bound, block_sums, poff_all, (size_t)L.K + 1,
-                      &stats->max_count, st));
+  if (sched == MSM_SCHED_PAIR_TREE)
+    HIP_TRY(launch_scan(counts, L.K, 0, level_bound, block_sums, poff_all, (size_t)L.K + 1,
+                        &stats->max_count, st));
   HIP_TRY(hipEventRecord(ctx->done, st));
   ctx->has_done = true;
   HIP_TRY(hipEventSynchronize(ctx->plan_ready));
@@ -275,10 +288,43 @@ int run_pipeline(msm_ctx* ctx, const g1a* d_points, const uint32_t* d_scalars, s
   if (hs.bad_point)
     return fail(MSM_ERR_OFF_CURVE, "an input point is not on the curve or not reduced below p%s");
 
+  if (sched == MSM_SCHED_WALKER) {
+    // accumulate: the stream walker over the E sorted entries
+    walk_args wa;
+    wa.pts = pts;
+    wa.idx = sorted_idx;
+    wa.offsets = offsets;
+    wa.K = L.K;
+    wa.E = hs.total;
+    wa.T = walk_lanes(hs.total, S);
+    wa.L = (uint32_t)(((uint64_t)hs.total + (uint64_t)wa.T * S - 1) / ((uint64_t)wa.T * S));
+    wa.acc = (uint32_t*)(ws + L.w_acc);
+    wa.kst = (uint32_t*)(ws + L.w_kst);
+    wa.bsum = bsum;
+    wa.head = (xyzz_st*)(ws + L.w_head);
+    wa.tail = (xyzz_st*)(ws + L.w_tail);
+    wa.head_k = (uint32_t*)(ws + L.w_head_k);
+    wa.tail_k = (uint32_t*)(ws + L.w_tail_k);
+    // pair passes for the most split bucket: it covers at most ceil(max / L) + 1 chunks
+    const uint64_t span = ((uint64_t)hs.max_count + wa.L - 1) / (wa.L ? wa.L : 1) + 1;
+    uint32_t passes = 0;
+    while (((uint64_t)1 << passes) < span) passes++;
+    if (hs.total) {
+      PhaseMark ph_lvl(ctx, st, PH_LEVEL, tl);
+      HIP_TRY(launch_walk(S, ctx->walker_device_state != 0, wa, st));
+      ph_lvl.end();
+      HIP_TRY(launch_walk_merge(S, wa, passes, st));
+      if (tl) {
+        ctx->level_launches++;
+        ctx->level_pairs += hs.total;  // entries walked (one add each, or a bucket start)
+        ctx->level_lanes += (uint64_t)wa.T * wa.L;  // one inversion per lane and step
+      }
+    }
+  }
   // accumulate: pair-tree levels until every bucket holds one point
   int levels = 0;
-  while (levels < level_bound && ((uint64_t)1 << levels) < hs.max_count) levels++;
-  (void)sched;
+  while (sched == MSM_SCHED_PAIR_TREE && levels < level_bound && ((uint64_t)1 << levels) < hs.max_count)
+    levels++;
   for (int l = 0; l < levels; l++) {
     uint32_t np = hs.pairs[l];
     if (np == 0) continue;
@@ -309,12 +355,12 @@ int run_pipeline(msm_ctx* ctx, const g1a* d_points, const uint32_t* d_scalars, s
   }
   ph_acc.end();
 
-  // running sum per window, window combine
+  // segment and plane sums, doubling runs, plane sum
   PhaseMark ph_red(ctx, st, PH_REDUCE, tl);
-  HIP_TRY(launch_reduce(bsum, c32, L.nwin, L.seg_len, L.nseg, part, win, st));
+  HIP_TRY(launch_reduce(bsum, c32, L.nwin, L.planes, tseg, pseg, part, st));
   ph_red.end();
   PhaseMark ph_fin(ctx, st, PH_FINAL, tl);
-  HIP_TRY(launch_final(win, L.nwin, c32, d_out, st));
+  HIP_TRY(launch_final(part, L.planes, res, gres, stats->join, d_out, st));
   ph_fin.end();
   if (verify) HIP_TRY(launch_verify_point(d_out, &stats->bad_out, st));
   HIP_TRY(hipEventRecord(ctx->done, st));
@@ -336,10 +382,10 @@ int msm_version(void) { return 300; }
 const char* msm_last_error(void) { return g_err; }
 
 size_t msm_workspace_bytes(size_t n, int c, int S) {
-  (void)S;
   if (c < 1 || c > 16 || n > MSM_MAX_N) return 0;
   if ((uint64_t)2 * n * (uint64_t)num_windows(c) >= ((uint64_t)1 << 32)) return 0;
-  return plan(n, c).total;
+  if (S != 4 && S != 8 && S != 16 && S != 32) return 0;
+  return plan(n, c, S).total;
 }
 
 int msm_ctx_create(int device, msm_ctx** out) {
@@ -397,8 +443,7 @@ int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scala
   if (!ctx) return fail(MSM_ERR_ARG, "ctx is NULL%s");
   int rc = check_run_args(d_points, d_scalars, n, c, S, sched, verify, d_out);
   if (rc) return rc;
-  if (sched == MSM_SCHED_WALKER) return fail(MSM_ERR_ARG, "the stream-walker schedule is not built%s");
-  const Layout L = plan(n, c);
+  const Layout L = plan(n, c, S);
   if (d_workspace && (workspace_bytes < L.total || !aligned(d_workspace, 256)))
     return fail(MSM_ERR_ARG, "workspace smaller than msm_workspace_bytes() or not 256-byte aligned%s");
   hipStream_t st = (hipStream_t)stream;
@@ -431,8 +476,7 @@ int msm_run_noalloc(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t*
   if (!ctx) return fail(MSM_ERR_ARG, "ctx is NULL%s");
   int rc = check_run_args(d_points, d_scalars, n, c, S, sched, verify, d_out);
   if (rc) return rc;
-  if (sched == MSM_SCHED_WALKER) return fail(MSM_ERR_ARG, "the stream-walker schedule is not built%s");
-  const Layout L = plan(n, c);
+  const Layout L = plan(n, c, S);
   if (L.total > NOALLOC_MAX_BYTES)
     return fail(MSM_ERR_ARG,
                 "msm_workspace_bytes(n, c, S) exceeds the fixed workspace of msm_run_noalloc "
@@ -451,6 +495,13 @@ int msm_ctx_set_affine_levels(msm_ctx* ctx, int levels) {
   if (!ctx) return fail(MSM_ERR_ARG, "ctx is NULL%s");
   if (levels < -1 || levels > MAX_LEVELS) return fail(MSM_ERR_ARG, "levels must be -1 .. 32%s");
   ctx->affine_levels = levels;
+  return MSM_OK;
+}
+
+int msm_ctx_set_walker_state(msm_ctx* ctx, int device_state) {
+  if (!ctx) return fail(MSM_ERR_ARG, "ctx is NULL%s");
+  if (device_state != 0 && device_state != 1) return fail(MSM_ERR_ARG, "device_state must be 0 or 1%s");
+  ctx->walker_device_state = device_state;
   return MSM_OK;
 }
 

@@ -16,7 +16,10 @@ constexpr int MAX_LEVELS = 32;                       // pair-tree levels tracked
 constexpr unsigned LEVEL_BLOCK = 128;                // lanes per block in k_level
 constexpr uint32_t XYZZ_QUAD_MAX_PAIRS = 65536;      // XYZZ levels this small use 4 lanes per add
 
-// Plan read back to the host after the sort (one 16 + 4 * MAX_LEVELS byte copy).
+constexpr int MAX_PLANES = 160;                      // reduction planes (at most 128 occur)
+constexpr int MAX_PLANE_GROUPS = (MAX_PLANES + 15) / 16;
+
+// Plan read back to the host after the sort (one small copy).
 struct msm_stats {
   uint32_t range_flag;          // a GLV half-scalar came out >= 2^127 (never expected)
   uint32_t max_count;           // largest bucket
@@ -24,7 +27,18 @@ struct msm_stats {
   uint32_t bad_point;           // verify: some input point is off the curve or not reduced
   uint32_t pairs[MAX_LEVELS];   // pair adds at pair-tree level l
   uint32_t bad_out;             // verify: the result is off the curve (read after the MSM)
-  uint32_t pad[3];
+  uint32_t join[MAX_PLANE_GROUPS + 1];  // reduction: finished planes per group, groups
+};
+
+// The planes of the bucket reduction (k_reduce.hip): plane i has exponent e[i] & 0xff,
+// window (e[i] >> 8) & 0xff and selector e[i] >> 16 (0: every segment's R + T; beta + 1:
+// the segment totals T of segments with bit beta set). Passed to kernels by value.
+struct plane_table {
+  uint32_t n;       // planes, in order of decreasing exponent
+  uint32_t nseg;    // segments per window
+  uint32_t lambda;  // log2 of the slots per segment
+  uint32_t nb;      // blocks of partial sums per plane: ceil(nseg / 256)
+  uint32_t e[MAX_PLANES];
 };
 
 // XYZZ point as stored in device memory (X, Y, ZZ, ZZZ; 128 bytes).
@@ -72,15 +86,49 @@ hipError_t launch_level_xyzz(bool in_aff, const void* in, const uint32_t* idx, x
                              xyzz_st* bsum, const uint32_t* counts, const uint32_t* offsets,
                              const uint32_t* poff, uint32_t K, uint32_t npairs, int level,
                              hipStream_t s);
-// Blocks per window in the first pass of the segment-sum tree: 64 segments per block
-// (one per quad), at most 64 blocks; every c has at most 4096 segments per window.
-inline uint32_t reduce_blocks(uint32_t nseg) {
-  uint32_t b = (nseg + 63) / 64;
-  return b < 1 ? 1 : (b > 64 ? 64 : b);
+// Stream-walker accumulate (k_walk.hip): T lanes of S slots walk chunks of L entries of
+// the E sorted entries. acc (16 Z words) and kst (Z words) are the device-side slot state
+// (used when dev_state), head / tail (Z points) and head_k / tail_k (Z words) the partial
+// sums of split buckets, Z = T S.
+struct walk_args {
+  const g1a* pts;
+  const uint32_t* idx;
+  const uint32_t* offsets;
+  uint32_t K, E, T, L;
+  uint32_t* acc;
+  uint32_t* kst;
+  xyzz_st* bsum;
+  xyzz_st* head;
+  xyzz_st* tail;
+  uint32_t* head_k;
+  uint32_t* tail_k;
+};
+constexpr uint32_t WALK_MAX_LANES = 65536;
+constexpr uint32_t WALK_MIN_CHUNK = 16;  // aim for at least this many entries per slot
+// Lanes of a walk over E entries with S slots per lane: enough for chunks of about
+// WALK_MIN_CHUNK entries, a multiple of 64, at most WALK_MAX_LANES.
+inline uint32_t walk_lanes(uint64_t E, int S) {
+  uint64_t t = (E + (uint64_t)S * WALK_MIN_CHUNK - 1) / ((uint64_t)S * WALK_MIN_CHUNK);
+  t = (t + 63) / 64 * 64;
+  if (t < 64) t = 64;
+  if (t > WALK_MAX_LANES) t = WALK_MAX_LANES;
+  return (uint32_t)t;
 }
-hipError_t launch_reduce(const xyzz_st* bsum, uint32_t c, uint32_t nwin, uint32_t seg_len,
-                         uint32_t nseg, xyzz_st* part, xyzz_st* win, hipStream_t s);
-hipError_t launch_final(const xyzz_st* win, uint32_t nwin, uint32_t c, g1a* out, hipStream_t s);
+// The walk kernel alone (slot state private, or on the device when dev_state).
+hipError_t launch_walk(int S, bool dev_state, const walk_args& a, hipStream_t s);
+// merge_passes pair passes over the partial sums, then the split buckets' sums.
+hipError_t launch_walk_merge(int S, const walk_args& a, uint32_t merge_passes, hipStream_t s);
+
+// Planes of the reduction for window width c and nwin windows.
+plane_table make_planes(uint32_t c, uint32_t nwin);
+// Segment sums (tseg, pseg: nwin nseg points each) and per-plane partial sums (part:
+// n nb points).
+hipError_t launch_reduce(const xyzz_st* bsum, uint32_t c, uint32_t nwin, const plane_table& pt,
+                         xyzz_st* tseg, xyzz_st* pseg, xyzz_st* part, hipStream_t s);
+// Doubling runs of every plane and their sum, in affine form, to out (res: n points,
+// gres: MAX_PLANE_GROUPS points, join: the zeroed counters of msm_stats).
+hipError_t launch_final(const xyzz_st* part, const plane_table& pt, xyzz_st* res, xyzz_st* gres,
+                        uint32_t* join, g1a* out, hipStream_t s);
 hipError_t launch_from_scalars(const uint32_t* ks, uint32_t n, g1a* out, hipStream_t s);
 hipError_t launch_test_fp(int op, const uint32_t* a, const uint32_t* b, uint32_t* out, uint32_t n,
                           hipStream_t s);

@@ -35,6 +35,7 @@ SYMBOLS = {
     "msm_run_noalloc": (_I, [_P, _P, _P, _S, _I, _I, _I, _I, _P, _P]),
     "msm_g1_from_scalars": (_I, [_P, _S, _P, _P]),
     "msm_ctx_set_affine_levels": (_I, [_P, _I]),
+    "msm_ctx_set_walker_state": (_I, [_P, _I]),
     "msm_ctx_set_timing": (_I, [_P, _I]),
     "msm_ctx_timing_read": (_I, [_P, _P]),
     "msm_test_fp": (_I, [_I, _P, _P, _P, _S, _P]),
@@ -140,6 +141,10 @@ class Context:
     def set_affine_levels(self, levels: int):
         """Leading pair-tree levels done with batched affine adds (-1: all)."""
         _check(lib().msm_ctx_set_affine_levels(self._h, int(levels)))
+
+    def set_walker_state(self, device_state: int):
+        """Stream walker's accumulators: 1 in a device buffer, 0 in private memory."""
+        _check(lib().msm_ctx_set_walker_state(self._h, int(device_state)))
 
     def set_timing(self, level: int = 2):
         """0 off, 1 the batched-affine level kernels only, 2 every phase (True = 2)."""

@@ -81,9 +81,10 @@ int msm_ctx_create(int device, msm_ctx** out);
 void msm_ctx_destroy(msm_ctx* ctx);
 
 /*
- * Device workspace bytes msm_run needs for n points with window c (the analogue of
- * the pages' estimateMem, PR #23520 "Summary"). S does not change the size.
- * Returns 0 for invalid n or c.
+ * Device workspace bytes msm_run needs for n points with window c and S slots (the
+ * analogue of the pages' estimateMem, PR #23520 "Summary"); the same size serves both
+ * schedules. S changes it only for small n, where the stream walker's slot state is the
+ * larger part. Returns 0 for invalid n, c or S.
  */
 size_t msm_workspace_bytes(size_t n, int c, int S);
 
@@ -180,6 +181,16 @@ int msm_g1_from_scalars(const uint32_t* d_k, size_t n, msm_g1_affine* d_out, voi
  * Returns MSM_ERR_ARG for a NULL ctx or levels outside -1 .. 32.
  */
 int msm_ctx_set_affine_levels(msm_ctx* ctx, int levels);
+
+/*
+ * Where the stream walker (MSM_SCHED_WALKER) keeps each slot's accumulator (acc_x,
+ * acc_y) and current bucket: 1 (default) in a device buffer, word-major over slots, as
+ * PR #23738 ("What would actually win") proposes; 0 in per-lane arrays that the compiler
+ * places in private memory, as the pages' walker does (PR #23738 "TL;DR"). The batch's
+ * prefix products are private either way. The result does not depend on it. Returns
+ * MSM_ERR_ARG for a NULL ctx or a value other than 0 or 1.
+ */
+int msm_ctx_set_walker_state(msm_ctx* ctx, int device_state);
 
 /*
  * Phase timing. msm_ctx_set_timing(ctx, level) makes msm_run record HIP events on its

@@ -27,9 +27,9 @@ def _msm():
     return M
 
 
-def _gpu_msm(pts, sc, c, S=8):
+def _gpu_msm(pts, sc, c, S=8, sched=0):
     M = _msm()
-    return to_host(M.msm(to_dev(pts), to_dev(sc), c, S))
+    return to_host(M.msm(to_dev(pts), to_dev(sc), c, S, sched=sched))
 
 
 @pytest.mark.parametrize("name,n", [("n256_c8", 256), ("n256_c8", 1000), ("n65536_c13", 4097),
@@ -71,14 +71,63 @@ def test_full_size_workloads(name):
 
 
 def test_knob_invariance():
-    """Same inputs, every S and several c: one answer (the sum is unique)."""
+    """Same inputs, every S, several c and both schedules: one answer (the sum is
+    unique)."""
     w = wl.generate("n65536_c13", n=3000)
     pts = oracle.g1_from_scalars(w["dlogs"])
     want = oracle.msm_pippenger(pts, w["scalars"], 13)
-    for c in (1, 5, 8, 11, 13, 16):
-        for S in (4, 8, 16, 32):
-            say("knobs c", c, "S", S)
-            assert np.array_equal(_gpu_msm(pts, w["scalars"], c, S), want), (c, S)
+    for sched in (0, 1):
+        for c in (1, 5, 8, 11, 13, 16):
+            for S in (4, 8, 16, 32):
+                say("knobs sched", sched, "c", c, "S", S)
+                assert np.array_equal(_gpu_msm(pts, w["scalars"], c, S, sched), want), (sched, c, S)
+
+
+@pytest.mark.parametrize("device_state", [1, 0])
+def test_walker_schedules(device_state):
+    """The stream walker, slot state on the device or private, against the oracle: every
+    S on uniform inputs, the edge-case mix, a giant bucket split over many chunks (the
+    pair passes over partial sums) and all-equal points (every add a doubling)."""
+    M = _msm()
+    ctx = M.Context(0)
+    try:
+        ctx.set_walker_state(device_state)
+        cases = []
+        w = wl.generate("n65536_c13", n=5000)
+        cases.append(("uniform", oracle.g1_from_scalars(w["dlogs"]), w["scalars"], 13))
+        w = wl.generate("n262144_c13_edge", n=6000)
+        cases.append(("edge", oracle.g1_from_scalars(w["dlogs"]), w["scalars"], 13))
+        w = wl.generate("n65536_c13", n=6000)
+        sc = w["scalars"].copy()
+        sc[::2] = wl.from_ints([ref.R - 1])[0]
+        cases.append(("giant", oracle.g1_from_scalars(w["dlogs"]), sc, 13))
+        cases.append(("equal", np.repeat(_pts([987654321]), 700, axis=0),
+                      wl.from_ints([ref.R - 5] * 700), 13))
+        w = wl.generate("n4194304_c16_skew", n=5000)
+        cases.append(("skew", oracle.g1_from_scalars(w["dlogs"]), w["scalars"], 16))
+        for name, pts, sc, c in cases:
+            want = oracle.msm_pippenger(pts, sc, c)
+            for S in (4, 8, 16, 32):
+                say("walker", name, "state", device_state, "c", c, "S", S)
+                got = to_host(ctx.run(to_dev(pts), to_dev(sc), c, S, sched=1))
+                assert np.array_equal(got, want), (name, S)
+    finally:
+        ctx.close()
+
+
+@pytest.mark.parametrize("name", ["n65536_c13", "n1048576_c16", "n4194304_c16_skew"])
+def test_walker_full_size(name):
+    """The stream walker at full size (the S sweep at n = 2^20), against the oracle."""
+    M = _msm()
+    w = wl.generate(name)
+    say("walker full size", name, "generate points n", w["n"])
+    pts_gpu = M.g1_from_scalars(to_dev(w["dlogs"]))
+    pts = oracle.g1_from_scalars(w["dlogs"])
+    want = oracle.msm_pippenger(pts, w["scalars"], w["c"])
+    sc = to_dev(w["scalars"])
+    for S in wl.CONFIGS[name].get("S_sweep", (w["S"],)):
+        say("walker full size", name, "c", w["c"], "S", S)
+        assert np.array_equal(to_host(M.msm(pts_gpu, sc, w["c"], S, sched=1)), want), S
 
 
 def test_pair_tree_schedule_invariance():

@@ -1,12 +1,12 @@
 """Models, on exact Python integers, of arithmetic rearrangements inside the HIP kernels,
 each checked against the plain definition it replaces:
 
-* the top-window spread (msm_kernels.hip, window_spread / digit_slot): with 127-bit
+* the top-window spread (kern_util.hpp, window_spread; k_sort.hip, digit_slot): with 127-bit
   half-scalar magnitudes the top window's digit never exceeds 2^(127 - c (W - 1)), so
   spreading each digit over 2^(c W - 128) slots stays inside the window's 2^(c-1) slots;
-* the running-sum segments with that spread (rsum_segment): R adds T at every slot that
-  is a multiple of f, and a segment's share is R + ceil(lo / f) T, which must equal the
-  weighted sum sum_b (floor(b / f) + 1) B_b over the segment;
+* the bucket reduction by planes (k_reduce.hip: make_planes, k_seg_sums, plane_segment):
+  segment running sums plus bit planes of the segment weights, each plane doubled by its
+  exponent, must add up to sum_j 2^(c j) sum_b (floor(b / f_j) + 1) B_{j,b} for every c;
 * the runs of doublings with lookahead (quad.hpp, quad_dbl_n): the (X, U = 2Y, M = 3X^2, z)
   recurrence against repeated XYZZ doubling (dbl-2008-s-1) on curve points, odd and even
   run lengths, and the point at infinity;
@@ -54,35 +54,96 @@ def test_top_window_spread_fits_every_c():
                     assert (d[-1] - 1) * f + i < 1 << (c - 1)
 
 
-# ---- running-sum segments ------------------------------------------------------------
-def _segment_share(B, lo, hi, f):
+# ---- bucket reduction by planes -------------------------------------------------------
+def _seg_log2(c):
+    return 3 if c >= 15 else 2
+
+
+def _planes(c, nwin):
+    """make_planes (k_reduce.hip): (exponent, window, selector) of every plane, in order
+    of decreasing exponent, plus the segment count and log2 segment length."""
+    lam = _seg_log2(c)
+    slots = 1 << (c - 1)
+    nseg = slots >> lam if slots > (1 << lam) else 1
+    lgseg = (nseg - 1).bit_length()
+    out = []
+    for j in range(nwin):
+        phi = c * nwin - 128 if j + 1 == nwin else 0
+        out.append((c * j, j, 0))
+        for beta in range(lgseg):
+            if beta + lam < phi:
+                continue
+            out.append((c * j + beta + lam - phi, j, beta + 1))
+    out.sort(key=lambda e: -e[0])
+    return out, nseg, lam
+
+
+def _plane_segment(sel, i):
+    if sel == 0:
+        return i
+    beta = sel - 1
+    return ((i >> beta) << (beta + 1)) | (1 << beta) | (i & ((1 << beta) - 1))
+
+
+def _seg_sums(B, lo, hi, f):
+    """k_seg_sums: T and P = R + T of one segment, R by a running sum from the top."""
     T = R = 0
     for b in range(hi - 1, lo - 1, -1):
         T += B[b]
-        if b % f == 0:
+        if b > lo and b % f == 0:
             R += T
-    return R + (-(-lo // f)) * T
+    return T, R + T
 
 
-def test_segment_shares_sum_to_weighted_bucket_sum():
+def _reduce_by_planes(buckets, c, nwin, mistake=None):
+    planes, nseg, lam = _planes(c, nwin)
+    slots = 1 << (c - 1)
+    T, Pv = {}, {}
+    for j in range(nwin):
+        f = 1 << (c * nwin - 128) if j + 1 == nwin else 1
+        for s in range(nseg):
+            lo, hi = s << lam, min(slots, (s + 1) << lam)
+            T[j, s], Pv[j, s] = _seg_sums(buckets[j], lo, hi, f)
+    total = 0
+    for e, j, sel in planes:
+        cnt = nseg >> 1 if sel else nseg
+        segs = [_plane_segment(sel, i) for i in range(cnt)]
+        if mistake == "selector":
+            segs = [_plane_segment(sel + 1 if sel else 0, i) % nseg for i in range(cnt)]
+        v = sum((T if sel else Pv)[j, s] for s in segs)
+        total += v << (e + (1 if mistake == "exponent" and sel == 1 else 0))
+    return total, planes
+
+
+def test_plane_reduction_equals_weighted_window_sum():
+    """Every c: the planes' doubled sums add up to sum_j 2^(c j) sum_b w_b B_{j,b}, with
+    w_b = floor(b / f_j) + 1, for random integers standing in for the bucket sums."""
     rng = random.Random(12)
-    for _ in range(400):
-        f = 1 << rng.randrange(0, 8)
-        nb = 1 << rng.randrange(1, 12)
-        seg = (1 << rng.randrange(0, 9)) if rng.random() < 0.7 else rng.randrange(1, 40)
-        B = [rng.randrange(1 << 20) for _ in range(nb)]
-        want = sum((b // f + 1) * B[b] for b in range(nb))
-        got = sum(_segment_share(B, lo, min(nb, lo + seg), f) for lo in range(0, nb, seg))
-        assert got == want, (f, nb, seg)
+    for c in range(1, 17):
+        nwin = _num_windows(c)
+        for trial in range(3):
+            buckets = [[rng.randrange(1 << 40) for _ in range(1 << (c - 1))] for _ in range(nwin)]
+            want = 0
+            for j in range(nwin):
+                f = 1 << (c * nwin - 128) if j + 1 == nwin else 1
+                want += sum((b // f + 1) * B for b, B in enumerate(buckets[j])) << (c * j)
+            got, planes = _reduce_by_planes(buckets, c, nwin)
+            assert got == want, (c, trial)
+        # table limits the kernels rely on: exponent below 128 in 8 bits, at most 160
+        # planes (10 groups of 16), segment selector and window in their fields
+        assert max(e for e, _, _ in planes) <= 127
+        assert len(planes) <= 160
+        assert all(j < 256 and sel < 256 for _, j, sel in planes)
+        assert [e for e, _, _ in planes] == sorted((e for e, _, _ in planes), reverse=True)
 
 
-def test_segment_share_catches_a_wrong_weight():
-    # a planted mistake (floor instead of ceil) must show up
-    B = [3, 5, 7, 11, 13, 17, 19, 23]
-    lo, hi, f = 1, 3, 4
-    T = sum(B[lo:hi])
-    wrong = _segment_share(B, lo, hi, f) - (-(-lo // f)) * T + (lo // f) * T
-    assert wrong != sum((b // f + 1) * B[b] for b in range(lo, hi))
+def test_plane_reduction_catches_planted_mistakes():
+    rng = random.Random(13)
+    c, nwin = 13, _num_windows(13)
+    buckets = [[rng.randrange(1 << 40) for _ in range(1 << (c - 1))] for _ in range(nwin)]
+    good, _ = _reduce_by_planes(buckets, c, nwin)
+    for mistake in ("exponent", "selector"):
+        assert _reduce_by_planes(buckets, c, nwin, mistake)[0] != good, mistake
 
 
 # ---- doubling runs -------------------------------------------------------------------
