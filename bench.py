@@ -88,6 +88,8 @@ def main() -> int:
                     help="accumulate schedule: 0 pair tree, 1 stream walker")
     ap.add_argument("--walker-state", type=int, default=1,
                     help="stream walker slot state: 1 device buffer, 0 private memory")
+    ap.add_argument("--prefix-store", type=int, default=0,
+                    help="pair-tree level slot state: 0 private, 1 LDS; +2 caches denominators")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0,
                     help="CPU seconds for the oracle baseline (0 disables it)")
     ap.add_argument("--copy-mb", type=int, default=0,
@@ -121,6 +123,7 @@ def main() -> int:
     if args.affine_levels is not None:
         ctx.set_affine_levels(args.affine_levels)
     ctx.set_walker_state(args.walker_state)
+    ctx.set_prefix_store(args.prefix_store)
     out = torch.empty(16, dtype=torch.uint32, device=dev)
     for _ in range(args.warmup):
         ctx.run(points, scalars, c, S, out=out, sched=args.sched)
@@ -224,7 +227,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": f"BN254 G1 MSM, n={n}, c={c}, S={S}, independent random points "
                                f"r_i*G, scalars uniform in [0, r) ({args.workload})",
-                   "n": n, "c": c, "S": S, "sched": ["pair_tree", "walker"][args.sched]},
+                   "n": n, "c": c, "S": S, "sched": ["pair_tree", "walker"][args.sched],
+                   "prefix_store": args.prefix_store, "walker_state": args.walker_state},
         "latency_ms": {"median": statistics.median(lat), "min": min(lat)},
         "phases_ms_per_step": phases,
         "roofline": roofline,

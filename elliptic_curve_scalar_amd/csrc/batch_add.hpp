@@ -12,8 +12,9 @@
 //   backward: for s = S-1 .. 0:  1/d_s = inv * pref_{s-1} (inv itself for s = 0),
 //             then inv = inv * d_s; lambda = numerator_s / d_s; finish the add.
 //
-// Slot state is pref_s (8 words per slot) and the operands' element indices;
-// operands are re-read in the backward pass instead of being held.
+// Slot state is pref_s (8 words per slot), optionally d_s, and the operands' element
+// indices; operands are re-read in the backward pass instead of being held. Where the
+// prefix products live (private memory or LDS) is the Store policy below.
 //
 // Special cases (the pages only report that x-collisions break an affine add,
 // PR #23736 "Correctness-harness fix"; the handling below is this library's):
@@ -60,14 +61,63 @@ __device__ __forceinline__ aff add_finish(const aff& A, const aff& B, int cs, co
   return r;
 }
 
+// Where a batch keeps its slot state: the prefix products pref_s and, with DX (the
+// cached-denominator option of PR #23520 "Summary"), each slot's denominator d_s so the
+// backward pass need not form it again.
+//   PrefPrivate: per-lane arrays, which the compiler places in private memory (scratch)
+//                because the slot loops are too large to unroll;
+//   PrefLds:     the block's LDS, word w of slot s of lane l at base[(8 s + w) lanes + l]
+//                (lanes = threads per block), so the 64 lanes of a wavefront touch 64
+//                consecutive words of one row: no bank conflicts.
+template <int S, bool DX>
+struct PrefPrivate {
+  fp pref[S];
+  fp dx[S];
+  __device__ __forceinline__ fp get(int s) const { return pref[s]; }
+  __device__ __forceinline__ void set(int s, const fp& v) { pref[s] = v; }
+  __device__ __forceinline__ fp get_dx(int s) const { return dx[s]; }
+  __device__ __forceinline__ void set_dx(int s, const fp& v) { dx[s] = v; }
+};
+
+template <int S>
+struct PrefPrivate<S, false> {
+  fp pref[S];
+  __device__ __forceinline__ fp get(int s) const { return pref[s]; }
+  __device__ __forceinline__ void set(int s, const fp& v) { pref[s] = v; }
+  __device__ __forceinline__ fp get_dx(int) const { return fp_zero(); }  // not used
+  __device__ __forceinline__ void set_dx(int, const fp&) {}
+};
+
+template <int S, bool DX>
+struct PrefLds {
+  uint32_t* base;  // the block's LDS: (DX ? 2 : 1) * 8 S words per lane
+  uint32_t lanes, lane;
+  __device__ __forceinline__ fp ld(int row) const {
+    fp r;
+#pragma unroll
+    for (int w = 0; w < 8; w++) r.v[w] = base[(size_t)(8 * row + w) * lanes + lane];
+    return r;
+  }
+  __device__ __forceinline__ void st(int row, const fp& v) const {
+#pragma unroll
+    for (int w = 0; w < 8; w++) base[(size_t)(8 * row + w) * lanes + lane] = v.v[w];
+  }
+  __device__ __forceinline__ fp get(int s) const { return ld(s); }
+  __device__ __forceinline__ void set(int s, const fp& v) { st(s, v); }
+  __device__ __forceinline__ fp get_dx(int s) const { return ld(S + s); }
+  __device__ __forceinline__ void set_dx(int s, const fp& v) { st(S + s, v); }
+};
+
+// LDS bytes per lane of a PrefLds store.
+constexpr uint32_t pref_lds_bytes(int S, bool DX) { return (DX ? 2u : 1u) * 32u * (uint32_t)S; }
+
 // Src supplies: fp ax(int s), fp bx(int s) (x-coordinates only), aff a(int s),
 // aff b(int s) (whole points), void put(int s, const aff&). Slots s >= cnt are idle
 // (d = 1, nothing stored). The forward pass reads only the x-coordinates unless an x
 // is 0 or the two x agree (infinity, tangent, cancel), which then loads the whole
 // points.
-template <int S, class Src>
-__device__ __forceinline__ void batch_affine_add(Src& src, int cnt) {
-  fp pref[S];
+template <int S, bool DX, class Store, class Src>
+__device__ __forceinline__ void batch_affine_add(Src& src, int cnt, Store& st) {
   fp acc = fp_one();
 #pragma unroll
   for (int s = 0; s < S; s++) {
@@ -80,21 +130,29 @@ __device__ __forceinline__ void batch_affine_add(Src& src, int cnt) {
         const aff A = src.a(s), B = src.b(s);
         d = add_denominator(A, B, add_case(A, B));
       }
+      if (DX) st.set_dx(s, d);
       acc = (s == 0) ? d : fp_mul(acc, d);
     }
-    pref[s] = acc;
+    st.set(s, acc);
   }
   fp inv = fp_inv(acc);
 #pragma unroll
   for (int s = S - 1; s >= 0; s--) {
     if (s < cnt) {
-      const fp inv_d = (s > 0) ? fp_mul(inv, pref[s - 1]) : inv;
+      const fp inv_d = (s > 0) ? fp_mul(inv, st.get(s - 1)) : inv;
       const aff A = src.a(s), B = src.b(s);
       const int cs = add_case(A, B);
-      inv = fp_mul(inv, add_denominator(A, B, cs));
+      inv = fp_mul(inv, DX ? st.get_dx(s) : add_denominator(A, B, cs));
       src.put(s, add_finish(A, B, cs, inv_d));
     }
   }
+}
+
+// The batch with its slot state in private memory.
+template <int S, class Src>
+__device__ __forceinline__ void batch_affine_add(Src& src, int cnt) {
+  PrefPrivate<S, false> st;
+  batch_affine_add<S, false>(src, cnt, st);
 }
 
 }  // namespace msmk

@@ -166,6 +166,7 @@ struct msm_ctx {
   int device = 0;
   int affine_levels = 1;  // leading pair-tree levels done with batched affine adds
   int walker_device_state = 1;  // stream walker: accumulators on the device (1) or private (0)
+  int prefix_store = 0;  // batched-affine level: prefix products private (0) / LDS (1), +2 dx cache
   void* ws = nullptr;
   size_t ws_bytes = 0;
   msm_stats* host_stats = nullptr;  // pinned: the plan, then the result's verify flag
@@ -335,7 +336,8 @@ int run_pipeline(msm_ctx* ctx, const g1a* d_points, const uint32_t* d_scalars, s
       // batched affine adds, S per lane sharing one inversion
       const g1a* in = (l == 0) ? pts : aff[(l - 1) & 1];
       PhaseMark ph_lvl(ctx, st, PH_LEVEL, tl);
-      HIP_TRY(launch_level(S, in, idx, aff[l & 1], bsum, counts, offsets, lvl_poff, L.K, np, l, st));
+      HIP_TRY(launch_level(S, ctx->prefix_store, in, idx, aff[l & 1], bsum, counts, offsets,
+                           lvl_poff, L.K, np, l, st));
       ph_lvl.end();
       if (tl) {
         ctx->level_launches++;
@@ -502,6 +504,13 @@ int msm_ctx_set_walker_state(msm_ctx* ctx, int device_state) {
   if (!ctx) return fail(MSM_ERR_ARG, "ctx is NULL%s");
   if (device_state != 0 && device_state != 1) return fail(MSM_ERR_ARG, "device_state must be 0 or 1%s");
   ctx->walker_device_state = device_state;
+  return MSM_OK;
+}
+
+int msm_ctx_set_prefix_store(msm_ctx* ctx, int store) {
+  if (!ctx) return fail(MSM_ERR_ARG, "ctx is NULL%s");
+  if (store < 0 || store > 3) return fail(MSM_ERR_ARG, "store must be in 0..3%s");
+  ctx->prefix_store = store;
   return MSM_OK;
 }
 

@@ -13,7 +13,6 @@ constexpr uint32_t SCAN_TILE = 256 * SCAN_ITEMS;     // counts per scan block
 constexpr int SCAN_TOP_ITEMS = 16;                   // block sums per thread in the top scan
 constexpr uint32_t SCAN_MAX_BLOCKS = 256 * SCAN_TOP_ITEMS;
 constexpr int MAX_LEVELS = 32;                       // pair-tree levels tracked
-constexpr unsigned LEVEL_BLOCK = 128;                // lanes per block in k_level
 constexpr uint32_t XYZZ_QUAD_MAX_PAIRS = 65536;      // XYZZ levels this small use 4 lanes per add
 
 constexpr int MAX_PLANES = 160;                      // reduction planes (at most 128 occur)
@@ -79,9 +78,16 @@ hipError_t launch_scan(const uint32_t* counts, uint32_t n, int level0, int nlev,
 hipError_t launch_bucket_init(const uint32_t* counts, const uint32_t* offsets, uint32_t K,
                               const uint32_t* sorted_idx, const g1a* points, xyzz_st* bsum,
                               hipStream_t s);
-hipError_t launch_level(int S, const g1a* in, const uint32_t* idx, g1a* out, xyzz_st* bsum,
-                        const uint32_t* counts, const uint32_t* offsets, const uint32_t* poff,
-                        uint32_t K, uint32_t npairs, int level, hipStream_t s);
+// Batched-affine pair-tree level; place selects the slot-state placement (0 private
+// memory, bit 0 LDS, bit 1 cached denominators).
+hipError_t launch_level(int S, int place, const g1a* in, const uint32_t* idx, g1a* out,
+                        xyzz_st* bsum, const uint32_t* counts, const uint32_t* offsets,
+                        const uint32_t* poff, uint32_t K, uint32_t npairs, int level,
+                        hipStream_t s);
+hipError_t launch_level_placed(int S, int place, const g1a* in, const uint32_t* idx, g1a* out,
+                               xyzz_st* bsum, const uint32_t* counts, const uint32_t* offsets,
+                               const uint32_t* poff, uint32_t K, uint32_t npairs, int level,
+                               hipStream_t s);
 hipError_t launch_level_xyzz(bool in_aff, const void* in, const uint32_t* idx, xyzz_st* out,
                              xyzz_st* bsum, const uint32_t* counts, const uint32_t* offsets,
                              const uint32_t* poff, uint32_t K, uint32_t npairs, int level,

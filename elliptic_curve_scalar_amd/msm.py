@@ -36,6 +36,7 @@ SYMBOLS = {
     "msm_g1_from_scalars": (_I, [_P, _S, _P, _P]),
     "msm_ctx_set_affine_levels": (_I, [_P, _I]),
     "msm_ctx_set_walker_state": (_I, [_P, _I]),
+    "msm_ctx_set_prefix_store": (_I, [_P, _I]),
     "msm_ctx_set_timing": (_I, [_P, _I]),
     "msm_ctx_timing_read": (_I, [_P, _P]),
     "msm_test_fp": (_I, [_I, _P, _P, _P, _S, _P]),
@@ -145,6 +146,10 @@ class Context:
     def set_walker_state(self, device_state: int):
         """Stream walker's accumulators: 1 in a device buffer, 0 in private memory."""
         _check(lib().msm_ctx_set_walker_state(self._h, int(device_state)))
+
+    def set_prefix_store(self, store: int):
+        """Pair-tree level slot state: 0 private, 1 LDS; +2 caches the denominators."""
+        _check(lib().msm_ctx_set_prefix_store(self._h, int(store)))
 
     def set_timing(self, level: int = 2):
         """0 off, 1 the batched-affine level kernels only, 2 every phase (True = 2)."""

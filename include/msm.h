@@ -193,6 +193,17 @@ int msm_ctx_set_affine_levels(msm_ctx* ctx, int levels);
 int msm_ctx_set_walker_state(msm_ctx* ctx, int device_state);
 
 /*
+ * Where the batched-affine pair-tree level kernel keeps each lane's slot state:
+ * store 0 (default) puts the S prefix products in per-lane arrays that the compiler
+ * places in private memory; 1 puts them in the block's LDS (S * 32 bytes per lane, one
+ * wavefront per block); adding 2 also caches each slot's denominator next to its prefix
+ * (the dx cache of PR #23520 "Summary"), so the backward pass does not form it again.
+ * The result does not depend on it. Returns MSM_ERR_ARG for a NULL ctx or store
+ * outside 0 .. 3.
+ */
+int msm_ctx_set_prefix_store(msm_ctx* ctx, int store);
+
+/*
  * Phase timing. msm_ctx_set_timing(ctx, level) makes msm_run record HIP events on its
  * stream: level 1 brackets only the batched-affine level-kernel launches (what a
  * roofline of that kernel needs, at the least cost to the rest of the pipeline); level

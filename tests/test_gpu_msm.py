@@ -83,6 +83,28 @@ def test_knob_invariance():
                 assert np.array_equal(_gpu_msm(pts, w["scalars"], c, S, sched), want), (sched, c, S)
 
 
+def test_prefix_store_placements():
+    """The level kernel's slot state in private memory or LDS, with or without cached
+    denominators, every S: the same bits, including the edge-case mix."""
+    M = _msm()
+    ctx = M.Context(0)
+    try:
+        for name, n in (("n65536_c13", 4000), ("n262144_c13_edge", 5000)):
+            w = wl.generate(name, n=n)
+            pts = oracle.g1_from_scalars(w["dlogs"])
+            want = oracle.msm_pippenger(pts, w["scalars"], 13)
+            for store in (0, 1, 2, 3):
+                ctx.set_prefix_store(store)
+                for S in (4, 8, 16, 32):
+                    say("prefix store", store, name, "S", S)
+                    got = to_host(ctx.run(to_dev(pts), to_dev(w["scalars"]), 13, S))
+                    assert np.array_equal(got, want), (name, store, S)
+        with pytest.raises(M.MsmError):
+            ctx.set_prefix_store(4)
+    finally:
+        ctx.close()
+
+
 @pytest.mark.parametrize("device_state", [1, 0])
 def test_walker_schedules(device_state):
     """The stream walker, slot state on the device or private, against the oracle: every
