@@ -148,6 +148,62 @@ __device__ __forceinline__ void batch_affine_add(Src& src, int cnt, Store& st) {
   }
 }
 
+// The same batch with checkpointed slot state: only the last prefix of every group of G
+// slots is stored (S / G of them, in a store of that many rows), and the backward pass
+// rebuilds a group's other prefixes, and its denominators, in registers from the
+// previous group's checkpoint before peeling the group's inverses: G - 1 more products
+// and G more denominators per group, for G times less stored state. The group's
+// operands are re-read in the backward pass as in the plain batch.
+template <int S, int G, class Store, class Src>
+__device__ __forceinline__ void batch_affine_add_ckpt(Src& src, int cnt, Store& st) {
+  static_assert(S % G == 0, "groups must tile the slots");
+  auto denom = [&](int s) -> fp {
+    const fp xa = src.ax(s), xb = src.bx(s);
+    if (!fp_eq(xa, xb) && !fp_is_zero(xa) && !fp_is_zero(xb)) return fp_sub(xb, xa);
+    const aff A = src.a(s), B = src.b(s);
+    return add_denominator(A, B, add_case(A, B));
+  };
+  fp acc = fp_one();
+#pragma unroll
+  for (int s = 0; s < S; s++) {
+    if (s < cnt) {
+      const fp d = denom(s);
+      acc = (s == 0) ? d : fp_mul(acc, d);
+    }
+    if (s % G == G - 1) st.set(s / G, acc);
+  }
+  fp inv = fp_inv(acc);
+  static_assert(G == 4, "the group's registers are written out for four slots");
+  for (int g = S / G - 1; g >= 0; g--) {
+    if (G * g >= cnt) continue;
+    const int s0 = G * g;
+    // the group's denominators d0..d3 and prefixes p0..p2 (pref of slots s0 .. s0 + 2),
+    // named registers: the compiler will not unroll a loop this large, and an indexed
+    // array would go to private memory
+    const fp base = (g > 0) ? st.get(g - 1) : fp_one();
+    const fp d0 = denom(s0);
+    const fp d1 = (s0 + 1 < cnt) ? denom(s0 + 1) : fp_one();
+    const fp d2 = (s0 + 2 < cnt) ? denom(s0 + 2) : fp_one();
+    const fp d3 = (s0 + 3 < cnt) ? denom(s0 + 3) : fp_one();
+    const fp p0 = (g > 0) ? fp_mul(base, d0) : d0;
+    const fp p1 = fp_mul(p0, d1);
+    const fp p2 = fp_mul(p1, d2);
+    auto peel = [&](int s, const fp& prev, const fp& d, bool first) {
+      if (s < cnt) {
+        const fp inv_d = first ? inv : fp_mul(inv, prev);
+        const aff A = src.a(s), B = src.b(s);
+        const int cs = add_case(A, B);
+        inv = fp_mul(inv, d);
+        src.put(s, add_finish(A, B, cs, inv_d));
+      }
+    };
+    peel(s0 + 3, p2, d3, false);
+    peel(s0 + 2, p1, d2, false);
+    peel(s0 + 1, p0, d1, false);
+    peel(s0, base, d0, g == 0);
+  }
+}
+
 // The batch with its slot state in private memory.
 template <int S, class Src>
 __device__ __forceinline__ void batch_affine_add(Src& src, int cnt) {

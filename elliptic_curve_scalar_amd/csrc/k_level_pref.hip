@@ -51,6 +51,8 @@ hipError_t launch_level_placed(int S, int place, const g1a* in, const uint32_t* 
     case PLACE_LDS | PLACE_DX:
       return placed_S<PLACE_LDS | PLACE_DX>(S, in, idx, out, bsum, counts, offsets, poff, K, npairs,
                                             level, s);
+    case PLACE_CKPT:
+      return placed_S<PLACE_CKPT>(S, in, idx, out, bsum, counts, offsets, poff, K, npairs, level, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -58,8 +58,10 @@ struct LevelSrc {
 
 // Slot-state placements of the batched-affine level kernel (msm_ctx_set_prefix_store):
 // bit 0 puts the prefix products in LDS instead of private memory, bit 1 adds the cached
-// denominators (PR #23520 "Summary").
-enum : int { PLACE_PRIVATE = 0, PLACE_LDS = 1, PLACE_DX = 2 };
+// denominators (PR #23520 "Summary"); PLACE_CKPT keeps one prefix in CKPT_GROUP in
+// private memory and rebuilds the others (batch_affine_add_ckpt).
+enum : int { PLACE_PRIVATE = 0, PLACE_LDS = 1, PLACE_DX = 2, PLACE_CKPT = 4 };
+constexpr int CKPT_GROUP = 4;  // slots per checkpoint of PLACE_CKPT
 
 // Lanes per block of the level kernel: two wavefronts with private state; one with LDS
 // state, whose size grows with S (S * 32 bytes per lane, twice that with the
@@ -100,7 +102,10 @@ __global__ void __launch_bounds__(128) k_level(const g1a* __restrict__ in,
     }
   }
   constexpr bool DX = (PLACE & PLACE_DX) != 0;
-  if constexpr ((PLACE & PLACE_LDS) != 0) {
+  if constexpr (PLACE == PLACE_CKPT) {
+    PrefPrivate<S / CKPT_GROUP, false> st;
+    batch_affine_add_ckpt<S, CKPT_GROUP>(src, cnt, st);
+  } else if constexpr ((PLACE & PLACE_LDS) != 0) {
     extern __shared__ uint32_t lds_pref[];
     PrefLds<S, DX> st{lds_pref, blockDim.x, threadIdx.x};
     batch_affine_add<S, DX>(src, cnt, st);

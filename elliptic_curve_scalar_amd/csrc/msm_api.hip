@@ -509,7 +509,7 @@ int msm_ctx_set_walker_state(msm_ctx* ctx, int device_state) {
 
 int msm_ctx_set_prefix_store(msm_ctx* ctx, int store) {
   if (!ctx) return fail(MSM_ERR_ARG, "ctx is NULL%s");
-  if (store < 0 || store > 3) return fail(MSM_ERR_ARG, "store must be in 0..3%s");
+  if (store < 0 || store > 4) return fail(MSM_ERR_ARG, "store must be in 0..4%s");
   ctx->prefix_store = store;
   return MSM_OK;
 }

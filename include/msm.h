@@ -197,9 +197,11 @@ int msm_ctx_set_walker_state(msm_ctx* ctx, int device_state);
  * store 0 (default) puts the S prefix products in per-lane arrays that the compiler
  * places in private memory; 1 puts them in the block's LDS (S * 32 bytes per lane, one
  * wavefront per block); adding 2 also caches each slot's denominator next to its prefix
- * (the dx cache of PR #23520 "Summary"), so the backward pass does not form it again.
- * The result does not depend on it. Returns MSM_ERR_ARG for a NULL ctx or store
- * outside 0 .. 3.
+ * (the dx cache of PR #23520 "Summary"), so the backward pass does not form it again;
+ * 4 keeps only every fourth prefix (in private memory) and rebuilds the other three and
+ * the denominators in registers in the backward pass (3 more products per 4 slots for
+ * a quarter of the state). The result does not depend on it. Returns MSM_ERR_ARG for a
+ * NULL ctx or store outside 0 .. 4.
  */
 int msm_ctx_set_prefix_store(msm_ctx* ctx, int store);
 

@@ -93,14 +93,14 @@ def test_prefix_store_placements():
             w = wl.generate(name, n=n)
             pts = oracle.g1_from_scalars(w["dlogs"])
             want = oracle.msm_pippenger(pts, w["scalars"], 13)
-            for store in (0, 1, 2, 3):
+            for store in (0, 1, 2, 3, 4):
                 ctx.set_prefix_store(store)
                 for S in (4, 8, 16, 32):
                     say("prefix store", store, name, "S", S)
                     got = to_host(ctx.run(to_dev(pts), to_dev(w["scalars"]), 13, S))
                     assert np.array_equal(got, want), (name, store, S)
         with pytest.raises(M.MsmError):
-            ctx.set_prefix_store(4)
+            ctx.set_prefix_store(5)
     finally:
         ctx.close()
 
