@@ -183,22 +183,24 @@ __device__ __forceinline__ void bg_lin_mod(const uint32_t (&u)[8], const uint32_
   for (int i = 0; i < 8; i++) out[i] = neg ? rp[i] : ge ? rm[i] : r[i];
 }
 
-// R^3 mod p: mont(v, R^3) = v R^2 turns the integer inverse of x R into (x^-1) R.
-__device__ __forceinline__ fp bg_r3() {
-  fp c;
-  c.v[0] = 0xda1530dfu; c.v[1] = 0xb1cd6dafu; c.v[2] = 0xa7283db6u; c.v[3] = 0x62f210e6u;
-  c.v[4] = 0x0ada0afbu; c.v[5] = 0xef7f0b0cu; c.v[6] = 0x2d592544u; c.v[7] = 0x20fd6e90u;
-  return c;
-}
-
 // x^-1 for x in Montgomery form (the Montgomery form of the inverse); 0 maps to 0.
+//
+// The steps keep a C = u y and b C = v y (mod p) for whatever constant C the run starts
+// from with (a, b, u, v) = (y, p, C, 0), since every step is the same linear map on
+// (a, b) and on (u, v). Here y = x R is the Montgomery representation, and starting
+// from C = R^2 mod p the run ends (b = 1) with v = R^2 / (x R) = x^-1 R, the Montgomery
+// form of the inverse itself: no Montgomery product converts the result afterwards.
+// This is the "trim Montgomery form in the batched-inversion path" lever of the pages
+// (PR #23738 "What would actually win", PR #23736 "Honest status") in the form it takes
+// here: one product per inversion less.
 __device__ __forceinline__ fp fp_inv_bingcd(const fp& x) {
   uint32_t a[8], b[8], u[8], v[8];
+  const fp r2 = fp_r2();  // 2^512 mod p, as a plain integer below p
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     a[i] = x.v[i];
     b[i] = bg_p(i);
-    u[i] = i == 0 ? 1u : 0u;
+    u[i] = r2.v[i];
     v[i] = 0u;
   }
   for (int it = 0; it < BG_BATCHES; it++) {
@@ -236,10 +238,8 @@ __device__ __forceinline__ fp fp_inv_bingcd(const fp& x) {
   for (int i = 1; i < 8; i++) one |= b[i];
   fp r;
   if (one == 0) {
-    fp w;
 #pragma unroll
-    for (int i = 0; i < 8; i++) w.v[i] = v[i];
-    r = fp_mul(w, bg_r3());
+    for (int i = 0; i < 8; i++) r.v[i] = v[i];
   } else {
     r = fp_inv_fermat(x);  // x = 0, or b did not reach 1
   }

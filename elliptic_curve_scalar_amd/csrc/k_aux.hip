@@ -96,6 +96,53 @@ __global__ void __launch_bounds__(256) k_test_pair_add(const g1a* a, const g1a* 
   batch_affine_add<S>(src, cnt);
 }
 
+// Instruction-rate probe: each lane runs `iters` rounds of 16 independent chains of one
+// instruction class, then folds the chains into out[lane] so that nothing is dead.
+//   op 0: 32 x 32 -> 64-bit multiply-add, the product's unit (v_mad_u64_u32)
+//   op 1: 32-bit add (v_add_u32)
+//   op 2: 32-bit add with carry in and out, the carry chains of field add/sub
+//         (v_add_co_u32 / v_addc_co_u32)
+// Timed over many waves per SIMD it gives the sustained issue rate of the class.
+__global__ void __launch_bounds__(256) k_test_rate(int op, uint32_t iters, uint32_t seed,
+                                                   uint32_t* __restrict__ out) {
+  const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t x[16];
+#pragma unroll
+  for (int k = 0; k < 16; k++) x[k] = gid * 2654435761u + (uint32_t)k * 40503u + seed;
+  uint32_t fold = 0;
+  if (op == 0) {
+    uint64_t acc[16];
+#pragma unroll
+    for (int k = 0; k < 16; k++) acc[k] = x[k];
+    for (uint32_t it = 0; it < iters; it++) {
+#pragma unroll
+      for (int k = 0; k < 16; k++) acc[k] = (uint64_t)(uint32_t)acc[k] * seed + acc[k];
+    }
+#pragma unroll
+    for (int k = 0; k < 16; k++) fold ^= (uint32_t)acc[k] ^ (uint32_t)(acc[k] >> 32);
+  } else if (op == 1) {
+    for (uint32_t it = 0; it < iters; it++) {
+#pragma unroll
+      for (int k = 0; k < 16; k += 2) {  // eight Fibonacci pairs: no closed form to fold
+        x[k] = x[k] + x[k + 1];
+        x[k + 1] = x[k + 1] + x[k];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 16; k++) fold ^= x[k];
+  } else {
+    uint32_t c = 0;
+    for (uint32_t it = 0; it < iters; it++) {
+#pragma unroll
+      for (int k = 0; k < 16; k++) x[k] = __builtin_addc(x[k], seed, c, &c);
+    }
+#pragma unroll
+    for (int k = 0; k < 16; k++) fold ^= x[k];
+    fold ^= c;
+  }
+  out[gid] = fold;
+}
+
 // ------------------------------------------------------------------ launchers
 hipError_t launch_from_scalars(const uint32_t* ks, uint32_t n, g1a* out, hipStream_t s) {
   if (n == 0) return hipSuccess;
@@ -126,6 +173,12 @@ hipError_t launch_test_pair_add(int S, const g1a* a, const g1a* b, g1a* out, uin
     case 32: threads = (n + 31) / 32; k_test_pair_add<32><<<grid_for(threads, 256), 256, 0, s>>>(a, b, out, n); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_test_rate(int op, uint32_t blocks, uint32_t iters, uint32_t seed, uint32_t* out,
+                            hipStream_t s) {
+  k_test_rate<<<blocks, 256, 0, s>>>(op, iters, seed, out);
   return hipGetLastError();
 }
 

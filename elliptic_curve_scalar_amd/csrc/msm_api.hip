@@ -204,8 +204,9 @@ struct PhaseMark {
   int phase;
   int level;  // the context's timing level, or 0 where no event may be created
   size_t e0 = SIZE_MAX;
-  // level 1 brackets only the batched-affine level kernels, level 2 every phase
-  bool on() const { return level >= 2 || (level == 1 && phase == PH_LEVEL); }
+  // level 1 brackets the batched-affine accumulate kernels and the combine, level 2
+  // every phase
+  bool on() const { return level >= 2 || (level == 1 && (phase == PH_LEVEL || phase == PH_FINAL)); }
   PhaseMark(msm_ctx* c, hipStream_t s, int ph, int lvl) : ctx(c), st(s), phase(ph), level(lvl) {
     if (on()) e0 = mark(ctx, st);
   }
@@ -608,6 +609,14 @@ int msm_test_fp_sqr(const uint32_t* d_a, uint32_t* d_out, size_t n, void* stream
 
 int msm_test_fp_inv(const uint32_t* d_a, uint32_t* d_out, size_t n, void* stream) {
   return msm_test_fp(4, d_a, nullptr, d_out, n, stream);
+}
+
+int msm_test_issue_rate(int op, uint32_t blocks, uint32_t iters, uint32_t* d_out, void* stream) {
+  if (op < 0 || op > 2) return fail(MSM_ERR_ARG, "op must be 0, 1 or 2%s");
+  if (blocks == 0 || blocks > (1u << 20) || iters == 0) return fail(MSM_ERR_ARG, "blocks or iters out of range%s");
+  if (!d_out || !aligned(d_out, 4)) return fail(MSM_ERR_ARG, "d_out is NULL or misaligned%s");
+  HIP_TRY(launch_test_rate(op, blocks, iters, 0x9e3779b9u, d_out, (hipStream_t)stream));
+  return MSM_OK;
 }
 
 int msm_test_glv(const uint32_t* d_scalars, size_t n, uint32_t* d_halfs, void* stream) {

@@ -47,6 +47,7 @@ SYMBOLS = {
     "msm_test_fp_inv": (_I, [_P, _P, _S, _P]),
     "msm_test_batched_add": (_I, [_P, _P, _P, _S, _I, _P]),
     "msm_test_glv": (_I, [_P, _S, _P, _P]),
+    "msm_test_issue_rate": (_I, [_I, ctypes.c_uint32, ctypes.c_uint32, _P, _P]),
 }
 
 _lib = None
@@ -265,3 +266,12 @@ def test_batched_add(a: torch.Tensor, b: torch.Tensor, S: int = 8) -> torch.Tens
                                       _dev_ptr(out, 16, "out"), a.shape[0], S,
                                       _stream_handle(a.device)))
     return out
+
+
+def test_issue_rate(op: int, blocks: int, iters: int, out: torch.Tensor, stream=None):
+    """Enqueue the instruction-rate probe (msm_test_issue_rate) writing into out
+    (blocks * 256 uint32 words on the device)."""
+    if out.numel() < blocks * 256:
+        raise ValueError("out holds fewer than blocks * 256 words")
+    _check(lib().msm_test_issue_rate(op, blocks, iters, _dev_ptr(out, None, "out"),
+                                     _stream_handle(out.device, stream)))

@@ -207,9 +207,9 @@ int msm_ctx_set_prefix_store(msm_ctx* ctx, int store);
 
 /*
  * Phase timing. msm_ctx_set_timing(ctx, level) makes msm_run record HIP events on its
- * stream: level 1 brackets only the batched-affine level-kernel launches (what a
- * roofline of that kernel needs, at the least cost to the rest of the pipeline); level
- * 2 also brackets each phase: sort (count, scan, scatter), accumulate (bucket init and
+ * stream: level 1 brackets only the batched-affine accumulate kernel launches and the
+ * window-combine kernel (what the rooflines of those kernels need, at the least cost to
+ * the rest of the pipeline); level 2 also brackets each phase: sort (count, scan, scatter), accumulate (bucket init and
  * all pair-tree levels, each XYZZ level kernel on its own), reduce (running sums) and
  * final (window combine); level 0 turns timing off. Each event pair costs the stream
  * a few microseconds. msm_ctx_timing_read waits for the events recorded since the
@@ -256,8 +256,17 @@ int msm_ctx_timing_read(msm_ctx* ctx, msm_timing* out);
  * words each with the sign in bit 127, where s = k1 + k2 lambda (mod r).
  * d_halfs holds 2 n * 4 words.
  *
+ * msm_test_issue_rate: an instruction-rate probe of the device (not a field
+ * operation): `blocks` blocks of 256 lanes each run `iters` rounds of 16 independent
+ * chains of one instruction class, op 0 the 32x32->64-bit multiply-add that the
+ * Montgomery product is made of (v_mad_u64_u32), op 1 a 32-bit add, op 2 a 32-bit add
+ * with carry in and out (the field add/sub chains); lane i writes a fold of its chains
+ * to d_out[i] (blocks * 256 words). Timing it with events gives the sustained issue rate
+ * of the class, which sets the peak of the integer roofline.
+ *
  * Errors: MSM_ERR_ARG for an unknown op or S, n > MSM_MAX_N, NULL or misaligned
- * pointers with n > 0; MSM_ERR_HIP if the launch fails.
+ * pointers with n > 0 (for the probe: blocks outside 1 .. 2^20, iters = 0 or a NULL
+ * d_out); MSM_ERR_HIP if the launch fails.
  */
 int msm_test_fp(int op, const uint32_t* d_a, const uint32_t* d_b, uint32_t* d_out, size_t n,
                 void* stream);
@@ -267,6 +276,7 @@ int msm_test_fp_add(const uint32_t* d_a, const uint32_t* d_b, uint32_t* d_out, s
 int msm_test_fp_sub(const uint32_t* d_a, const uint32_t* d_b, uint32_t* d_out, size_t n, void* stream);
 int msm_test_fp_inv(const uint32_t* d_a, uint32_t* d_out, size_t n, void* stream);
 int msm_test_glv(const uint32_t* d_scalars, size_t n, uint32_t* d_halfs, void* stream);
+int msm_test_issue_rate(int op, uint32_t blocks, uint32_t iters, uint32_t* d_out, void* stream);
 int msm_test_batched_add(const msm_g1_affine* d_a, const msm_g1_affine* d_b,
                          msm_g1_affine* d_out, size_t n, int S, void* stream);
 

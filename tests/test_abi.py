@@ -87,6 +87,10 @@ def test_argument_errors_without_gpu():
     assert L.msm_test_batched_add(p, p, p, 4, 5, None) == M.MSM_ERR_ARG
     assert L.msm_test_batched_add(p, ctypes.c_void_p(8), p, 4, 8, None) == M.MSM_ERR_ARG
     assert L.msm_test_glv(None, 4, p, None) == M.MSM_ERR_ARG
+    assert L.msm_test_issue_rate(3, 1, 1, p, None) == M.MSM_ERR_ARG
+    assert L.msm_test_issue_rate(0, 0, 1, p, None) == M.MSM_ERR_ARG
+    assert L.msm_test_issue_rate(0, 1, 0, p, None) == M.MSM_ERR_ARG
+    assert L.msm_test_issue_rate(0, 1, 1, None, None) == M.MSM_ERR_ARG
     assert L.msm_test_glv(p, 4, ctypes.c_void_p(4), None) == M.MSM_ERR_ARG
     # context creation with a NULL out pointer
     assert L.msm_ctx_create(0, None) == M.MSM_ERR_ARG

@@ -2,8 +2,9 @@
 (csrc/bingcd.hpp), checked against what p fixes:
 
 * -p^-1 mod 2^30, which makes the exact division by 2^30 mod p clear the low bits;
-* R^3 mod p (R = 2^256), which turns the integer inverse of the Montgomery form x R
-  into the Montgomery form x^-1 R of the inverse;
+* the start value u = R^2 mod p (R = 2^256, fp_r2 in fp.hpp): started from (y, p, C, 0)
+  the steps end with v = C / y, so with y = x R the result is x^-1 R, the Montgomery
+  form of the inverse, with no product afterwards;
 * the batch shape: 30 steps a batch keep |f| + |g| <= 2^30 inside int32;
 * a big-integer model of the batches (64-bit stand-ins, factors applied to the full
   values) reaches b = 1 with u, v giving the inverse, within the shipped batch count
@@ -29,16 +30,32 @@ def test_npinv30():
     assert (ref.P * k + 1) % (1 << 30) == 0
 
 
-def test_r_cubed():
-    words = dict((int(i), int(v, 16)) for i, v in re.findall(r"c\.v\[(\d)\] = 0x([0-9a-f]+)u", SRC))
+def test_start_constant_is_r_squared():
+    fp_src = open(os.path.join(ROOT, "elliptic_curve_scalar_amd", "csrc", "fp.hpp")).read()
+    body = fp_src[fp_src.index("fp fp_r2()"):]
+    body = body[:body.index("}")]
+    words = dict((int(i), int(v, 16)) for i, v in re.findall(r"r\.v\[(\d)\] = 0x([0-9a-f]+)u", body))
     assert sorted(words) == list(range(8))
-    val = sum(words[i] << (32 * i) for i in range(8))
     R = 1 << 256
-    assert val == R ** 3 % ref.P
-    # mont(X^-1, R^3) = X^-1 R^2 = x^-1 R for X = x R
-    x = 123456789
-    X = x * R % ref.P
-    assert pow(X, -1, ref.P) * val * pow(R, -1, ref.P) % ref.P == pow(x, -1, ref.P) * R % ref.P
+    assert sum(words[i] << (32 * i) for i in range(8)) == R * R % ref.P
+    assert "u[i] = r2.v[i]" in SRC  # the inverse starts from it
+
+
+def test_start_constant_scales_the_result():
+    """Started from (y, p, C, 0) the batches end with v = C / y: with C = R^2 and
+    y = x R that is x^-1 R; a wrong start (C = 1, the plain inverse) is caught."""
+    R = 1 << 256
+    rng = random.Random(79)
+    batches = _define("BG_BATCHES")
+    for _ in range(40):
+        x = rng.randrange(1, ref.P)
+        y = x * R % ref.P
+        ok, v = _bingcd(y, batches, start=R * R % ref.P)
+        assert ok and v == pow(x, -1, ref.P) * R % ref.P
+        C = rng.randrange(1, ref.P)
+        assert _bingcd(y, batches, start=C)[1] == C * pow(y, -1, ref.P) % ref.P
+    x = 987654321
+    assert _bingcd(x * R % ref.P, batches, start=1)[1] != pow(x, -1, ref.P) * R % ref.P
 
 
 def test_batch_shape():
@@ -71,10 +88,11 @@ def _batch(xa, xb, steps):
     return f0, g0, f1, g1
 
 
-def _bingcd(y, batches, steps=30):
-    """The batches of the device inverse on Python integers; returns (converged, v)."""
+def _bingcd(y, batches, steps=30, start=1):
+    """The batches of the device inverse on Python integers, from (a, b, u, v) =
+    (y, p, start, 0); returns (converged, v)."""
     P = ref.P
-    a, b, u, v = y, P, 1, 0
+    a, b, u, v = y, P, start, 0
     inv2k = pow(2, -steps, P)
     for _ in range(batches):
         f0, g0, f1, g1 = _batch(*_approx(a, b), steps)

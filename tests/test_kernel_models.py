@@ -137,6 +137,15 @@ def test_plane_reduction_equals_weighted_window_sum():
         assert [e for e, _, _ in planes] == sorted((e for e, _, _ in planes), reverse=True)
 
 
+def test_bench_plane_exponents_follow_the_table():
+    """bench.py prices the combine kernel from the planes' exponents; they must be the
+    reduction's own."""
+    import bench
+    for c in range(1, 17):
+        planes, _, _ = _planes(c, _num_windows(c))
+        assert sorted(bench.plane_exponents(c)) == sorted(e for e, _, _ in planes), c
+
+
 def test_plane_reduction_catches_planted_mistakes():
     rng = random.Random(13)
     c, nwin = 13, _num_windows(13)
