@@ -149,7 +149,8 @@ class Context:
         _check(lib().msm_ctx_set_walker_state(self._h, int(device_state)))
 
     def set_prefix_store(self, store: int):
-        """Pair-tree level slot state: 0 private, 1 LDS; +2 caches the denominators."""
+        """Pair-tree level-0 slot state: 0 private, 1 LDS, 2 private and 3 LDS with the
+        denominators cached, 4 one prefix in four stored (checkpoints)."""
         _check(lib().msm_ctx_set_prefix_store(self._h, int(store)))
 
     def set_timing(self, level: int = 2):
