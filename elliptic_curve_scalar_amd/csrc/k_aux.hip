@@ -5,6 +5,7 @@
 #include "batch_add.hpp"
 #include "glv.hpp"
 #include "kern_util.hpp"
+#include "rowchain.hpp"
 
 namespace msmk {
 
@@ -96,6 +97,65 @@ __global__ void __launch_bounds__(256) k_test_pair_add(const g1a* a, const g1a* 
   batch_affine_add<S>(src, cnt);
 }
 
+// Row-form field operations (rowfp.hpp): wavefront w computes elements 4 w .. 4 w + 3, one
+// per row; rows past n compute on zeros and store nothing. op 0 a b, 1 a + b, 2 a - b.
+// One wavefront per 64-lane block.
+__global__ void __launch_bounds__(64) k_test_row(int op, const uint32_t* __restrict__ a,
+                                                 const uint32_t* __restrict__ b,
+                                                 uint32_t* __restrict__ out, uint32_t n) {
+  const uint32_t l = threadIdx.x & 15u, e = 4u * blockIdx.x + (threadIdx.x >> 4);
+  const bool live = e < n && l < 8u;
+  const uint32_t x = live ? a[8 * (size_t)e + l] : 0u, y = live ? b[8 * (size_t)e + l] : 0u;
+  const row_consts k = row_consts_load();
+  uint32_t r;
+  if (op == 0) r = row_mul(x, y, k);
+  else if (op == 1) r = row_add(x, y, k);
+  else r = row_sub(x, y, k);
+  if (live) out[8 * (size_t)e + l] = r;
+}
+
+// 2^d P for n XYZZ points (32 words each: X, Y, ZZ, ZZZ), one wavefront per point: op 3 by
+// runs in row form, op 4 by the quad runs. Every lane computes; lane 0 stores.
+__global__ void __launch_bounds__(64) k_test_row_dbl(int op, const uint32_t* __restrict__ pts,
+                                                     uint32_t d, uint32_t* __restrict__ out) {
+  const xyzz_st* src = reinterpret_cast<const xyzz_st*>(pts) + blockIdx.x;
+  const xyzz p = xyzz_load(src);
+  const int q = (int)(threadIdx.x & 3u);
+  xyzz r;
+  if (op == 3) {
+    const row_consts k = row_consts_load();
+    r = row_dbl_n(p, d, k, q);
+  } else {
+    r = quad_dbl_n(p, d, q);
+  }
+  if (threadIdx.x == 0) xyzz_store(reinterpret_cast<xyzz_st*>(out) + blockIdx.x, r);
+}
+
+// Latency probe, one wavefront: x <- x b, d times, for the four elements of a and b (8 words
+// each): op 5 in row form (element r on row r), op 6 with the per-lane product (element
+// i mod 4 on lane i). out gets the four results.
+__global__ void __launch_bounds__(64) k_test_row_chain(int op, const uint32_t* __restrict__ a,
+                                                       const uint32_t* __restrict__ b, uint32_t d,
+                                                       uint32_t* __restrict__ out) {
+  if (op == 5) {
+    const uint32_t l = threadIdx.x & 15u, e = threadIdx.x >> 4;
+    uint32_t x = l < 8u ? a[8 * e + l] : 0u;
+    const uint32_t y = l < 8u ? b[8 * e + l] : 0u;
+    const row_consts k = row_consts_load();
+    for (uint32_t i = 0; i < d; i++) x = row_mul(x, y, k);
+    if (l < 8u) out[8 * e + l] = x;
+  } else {
+    const uint32_t e = threadIdx.x & 3u;
+    fp x = fp_load_words(a + 8 * e);
+    const fp y = fp_load_words(b + 8 * e);
+    for (uint32_t i = 0; i < d; i++) x = fp_mul(x, y);
+    if (threadIdx.x < 4u) {
+#pragma unroll
+      for (int w = 0; w < 8; w++) out[8 * e + w] = x.v[w];
+    }
+  }
+}
+
 // Instruction-rate probe: each lane runs `iters` rounds of 16 independent chains of one
 // instruction class, then folds the chains into out[lane] so that nothing is dead.
 //   op 0: 32 x 32 -> 64-bit multiply-add, the product's unit (v_mad_u64_u32)
@@ -172,6 +232,20 @@ hipError_t launch_test_pair_add(int S, const g1a* a, const g1a* b, g1a* out, uin
     case 16: threads = (n + 15) / 16; k_test_pair_add<16><<<grid_for(threads, 256), 256, 0, s>>>(a, b, out, n); break;
     case 32: threads = (n + 31) / 32; k_test_pair_add<32><<<grid_for(threads, 256), 256, 0, s>>>(a, b, out, n); break;
     default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_test_row(int op, const uint32_t* a, const uint32_t* b, uint32_t* out, uint32_t n,
+                           uint32_t d, hipStream_t s) {
+  if (op <= 2) {
+    if (n == 0) return hipSuccess;
+    k_test_row<<<(n + 3) / 4, 64, 0, s>>>(op, a, b, out, n);
+  } else if (op <= 4) {
+    if (n == 0) return hipSuccess;
+    k_test_row_dbl<<<n, 64, 0, s>>>(op, a, d, out);
+  } else {
+    k_test_row_chain<<<1, 64, 0, s>>>(op, a, b, d, out);
   }
   return hipGetLastError();
 }

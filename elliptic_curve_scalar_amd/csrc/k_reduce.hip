@@ -23,7 +23,8 @@
 //   k_seg_sums     one quad per (window, segment): T_s and P_s = R_s + T_s
 //   k_plane_sums   one block per 256 elements of a plane: their sum (LDS tree)
 //   k_plane_chain  one wavefront per plane: the plane's partial sums (butterfly),
-//                  2^e S by a run of doublings; the last wavefront of each group of 16
+//                  2^e S by a run of doublings in row form (rowchain.hpp: each of a
+//                  round's four products spread over 16 lanes); the last wavefront of each group of 16
 //                  planes adds the group, the last group adds the groups and converts
 //                  the result to affine
 #include <hip/hip_runtime.h>
@@ -31,6 +32,7 @@
 
 #include "glv.hpp"
 #include "kern_util.hpp"
+#include "rowchain.hpp"
 
 namespace msmk {
 
@@ -54,6 +56,19 @@ __device__ __forceinline__ xyzz xyzz_load_coherent(const xyzz_st* p) {
     a.ZZZ.v[i] = __hip_atomic_load(&p->w[24 + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   return a;
+}
+
+// Lane 0's point on every lane of the wavefront.
+__device__ __forceinline__ xyzz xyzz_from_lane0(const xyzz& a) {
+  xyzz r;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    r.X.v[i] = __builtin_amdgcn_readfirstlane(a.X.v[i]);
+    r.Y.v[i] = __builtin_amdgcn_readfirstlane(a.Y.v[i]);
+    r.ZZ.v[i] = __builtin_amdgcn_readfirstlane(a.ZZ.v[i]);
+    r.ZZZ.v[i] = __builtin_amdgcn_readfirstlane(a.ZZZ.v[i]);
+  }
+  return r;
 }
 
 // Sum over the first `used` quads of a wavefront (1 <= used <= 16; the others hold the
@@ -140,7 +155,7 @@ __global__ void __launch_bounds__(256) k_plane_sums(const xyzz_st* __restrict__ 
 }
 
 // One wavefront per plane p: S = sum of the plane's nb partials, then 2^e S (e = the
-// plane's exponent) by a run of doublings (quad.hpp). Planes are in order of decreasing
+// plane's exponent) by a run of doublings in row form. Planes are in order of decreasing
 // e, so the long runs start first. The last wavefront to finish in each group of 16
 // planes (counted by join[group]) adds the group's results; the last group to finish
 // (join[MAX_PLANE_GROUPS]) adds the group sums and writes the affine result. The counters
@@ -152,10 +167,13 @@ __global__ void __launch_bounds__(64) k_plane_chain(const xyzz_st* __restrict__ 
   const int q = (int)(threadIdx.x & 3u);
   const uint32_t e = pt.e[p] & 0xffu;
   const uint32_t nblk = (plane_count(pt, pt.e[p] >> 16) + PLANE_PER_BLOCK - 1) / PLANE_PER_BLOCK;
+  const row_consts k = row_consts_load();
   xyzz acc = xyzz_inf();
   for (uint32_t i = quad; i < nblk; i += 16) acc = quad_add(acc, xyzz_load(part + (size_t)p * pt.nb + i), q);
   acc = wave_quad_sum(acc, min(nblk, 16u), q);
-  acc = quad_dbl_n(acc, e, q);
+  // the run of doublings in row form needs the plane's sum (quad 0's) on every lane
+  acc = xyzz_from_lane0(acc);
+  acc = row_dbl_n(acc, e, k, q);
   if (threadIdx.x == 0) xyzz_store(res + p, acc);
   __threadfence();
   const uint32_t grp = p >> 4, ngroups = (pt.n + 15u) >> 4;

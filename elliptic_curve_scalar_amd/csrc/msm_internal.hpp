@@ -140,6 +140,9 @@ hipError_t launch_test_fp(int op, const uint32_t* a, const uint32_t* b, uint32_t
                           hipStream_t s);
 hipError_t launch_test_rate(int op, uint32_t blocks, uint32_t iters, uint32_t seed, uint32_t* out,
                             hipStream_t s);
+// Row-form field and doubling-run hooks (ops 0..6 of msm_test_row).
+hipError_t launch_test_row(int op, const uint32_t* a, const uint32_t* b, uint32_t* out, uint32_t n,
+                           uint32_t d, hipStream_t s);
 hipError_t launch_test_glv(const uint32_t* scalars, uint32_t n, uint32_t* halfs, hipStream_t s);
 hipError_t launch_test_pair_add(int S, const g1a* a, const g1a* b, g1a* out, uint32_t n,
                                 hipStream_t s);

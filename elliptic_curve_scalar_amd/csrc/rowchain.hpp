@@ -1,0 +1,72 @@
+// Runs of doublings on one wavefront in row form (rowfp.hpp): the same recurrence as the
+// quad runs of quad.hpp, with each round's (at most) four products on the four rows of the
+// wavefront instead of the four lanes of a quad, and every field value one word per lane.
+//
+// A run keeps (X, U = 2Y, M = 3X^2) and a factor z; the XYZZ point it stands for is
+// (X, U / 2, ZZ0 z^2, ZZZ0 z^3). Two doublings take five rounds (dbl-2008-s-1 with a = 0
+// written in U, with M X and M^2 started a round early; quad.hpp states the algebra).
+#pragma once
+#include "quad.hpp"
+#include "rowfp.hpp"
+
+namespace msmk {
+
+struct rchain {
+  uint32_t X, U, M, z;
+};
+
+__device__ __forceinline__ void row_chain_dbl2(rchain& c, const row_consts& k) {
+  // round A: V = U^2, M X, M^2, z U
+  row4 r = row_gather(row_mul(row_pick(k, c.U, c.M, c.M, c.z), row_pick(k, c.U, c.X, c.M, c.U), k));
+  const uint32_t V = r.r0, MX = r.r1, MM = r.r2, z1 = r.r3;
+  // round B: X V, (M X) V, M M^2, V^2
+  r = row_gather(row_mul(row_pick(k, c.X, MX, c.M, V), row_pick(k, V, V, MM, V), k));
+  const uint32_t XV = r.r0, MXV = r.r1, M3 = r.r2, VV = r.r3;
+  const uint32_t X1 = row_sub(MM, row_dbl(XV, k), k);
+  const uint32_t U1 = row_sub(row_dbl(row_sub(row_triple(MXV, k), M3, k), k), VV, k);
+  // round C: X1^2, V1 = U1^2, z1 U1 (row 3 repeats row 0)
+  r = row_gather(row_mul(row_pick(k, X1, U1, z1, X1), row_pick(k, X1, U1, U1, X1), k));
+  const uint32_t M1 = row_triple(r.r0, k), V1 = r.r1;
+  c.z = r.r2;
+  // round D: M1 X1, M1^2, X1 V1, V1^2
+  r = row_gather(row_mul(row_pick(k, M1, M1, X1, V1), row_pick(k, X1, M1, V1, V1), k));
+  const uint32_t M1X1 = r.r0, MM1 = r.r1, X1V1 = r.r2, VV1 = r.r3;
+  c.X = row_sub(MM1, row_dbl(X1V1, k), k);
+  // round E: (M1 X1) V1, M1 M1^2, X2^2 (row 3 repeats row 2)
+  r = row_gather(row_mul(row_pick(k, M1X1, M1, c.X, c.X), row_pick(k, V1, MM1, c.X, c.X), k));
+  c.U = row_sub(row_dbl(row_sub(row_triple(r.r0, k), r.r1, k), k), VV1, k);
+  c.M = row_triple(r.r2, k);
+}
+
+__device__ __forceinline__ void row_chain_dbl1(rchain& c, const row_consts& k) {
+  row4 r = row_gather(row_mul(row_pick(k, c.U, c.M, c.M, c.z), row_pick(k, c.U, c.X, c.M, c.U), k));
+  const uint32_t V = r.r0, MX = r.r1, MM = r.r2;
+  c.z = r.r3;
+  r = row_gather(row_mul(row_pick(k, c.X, MX, c.M, V), row_pick(k, V, V, MM, V), k));
+  const uint32_t XV = r.r0, MXV = r.r1, M3 = r.r2, VV = r.r3;
+  c.X = row_sub(MM, row_dbl(XV, k), k);
+  c.U = row_sub(row_dbl(row_sub(row_triple(MXV, k), M3, k), k), VV, k);
+  c.M = row_triple(row_mul(c.X, c.X, k), k);  // every row computes X'^2
+}
+
+// 2^n p for a point p that every lane of the wavefront holds (per-lane form); the result
+// is again on every lane. The whole wavefront must be active.
+__device__ __forceinline__ xyzz row_dbl_n(const xyzz& p, uint32_t n, const row_consts& k, int q) {
+  if (n == 0) return p;
+  const dchain c0 = quad_chain_begin(p);
+  rchain c;
+  c.X = row_from_fp(c0.X);
+  c.U = row_from_fp(c0.U);
+  c.M = row_from_fp(c0.M);
+  c.z = row_from_fp(c0.z);
+  for (uint32_t i = 0; i < n / 2; i++) row_chain_dbl2(c, k);
+  if (n & 1u) row_chain_dbl1(c, k);
+  dchain e;
+  e.X = row_to_fp(c.X);
+  e.U = row_to_fp(c.U);
+  e.M = row_to_fp(c.M);
+  e.z = row_to_fp(c.z);
+  return quad_chain_end(e, p.ZZ, p.ZZZ, q);
+}
+
+}  // namespace msmk

@@ -48,6 +48,7 @@ SYMBOLS = {
     "msm_test_batched_add": (_I, [_P, _P, _P, _S, _I, _P]),
     "msm_test_glv": (_I, [_P, _S, _P, _P]),
     "msm_test_issue_rate": (_I, [_I, ctypes.c_uint32, ctypes.c_uint32, _P, _P]),
+    "msm_test_row": (_I, [_I, _P, _P, _P, _S, ctypes.c_uint32, _P]),
 }
 
 _lib = None
@@ -266,6 +267,19 @@ def test_batched_add(a: torch.Tensor, b: torch.Tensor, S: int = 8) -> torch.Tens
     _check(lib().msm_test_batched_add(_dev_ptr(a, 16, "a"), _dev_ptr(b, 16, "b"),
                                       _dev_ptr(out, 16, "out"), a.shape[0], S,
                                       _stream_handle(a.device)))
+    return out
+
+
+def test_row(op: int, a: torch.Tensor, b: torch.Tensor | None = None, d: int = 0,
+             stream=None) -> torch.Tensor:
+    """Row-form hooks of msm_test_row: ops 0..2 field ops on [n, 8] tensors, ops 3 and 4
+    2^d P on [n, 32] XYZZ points (row runs, quad runs), ops 5 and 6 the latency probe on
+    four elements."""
+    words = 32 if op in (3, 4) else 8
+    out = torch.empty_like(a)
+    _check(lib().msm_test_row(op, _dev_ptr(a, words, "a"), _dev_ptr(b, 8, "b"),
+                              _dev_ptr(out, words, "out"), a.shape[0], d,
+                              _stream_handle(a.device, stream)))
     return out
 
 

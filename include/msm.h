@@ -256,6 +256,15 @@ int msm_ctx_timing_read(msm_ctx* ctx, msm_timing* out);
  * words each with the sign in bit 127, where s = k1 + k2 lambda (mod r).
  * d_halfs holds 2 n * 4 words.
  *
+ * msm_test_row: the row form of the field arithmetic that the window combine's runs of
+ * doublings use (one product spread over the 16 lanes of a DPP row, four products per
+ * wavefront). op 0 a*b, 1 a+b, 2 a-b on n elements (8 words each, fully reduced
+ * Montgomery form, like msm_test_fp); op 3 d_out[i] = 2^d * d_a[i] for n XYZZ points (32
+ * words each: X, Y, ZZ, ZZZ; d <= 4096) by runs of doublings in row form, op 4 the same
+ * by the quad runs; ops 5 and 6 are a latency probe on one wavefront (n = 4): x <- x * b,
+ * d times, for the four elements of d_a and d_b, in row form (5) or with the per-lane
+ * product (6), the four results to d_out. d_b unused for ops 3 and 4.
+ *
  * msm_test_issue_rate: an instruction-rate probe of the device (not a field
  * operation): `blocks` blocks of 256 lanes each run `iters` rounds of 16 independent
  * chains of one instruction class, op 0 the 32x32->64-bit multiply-add that the
@@ -276,6 +285,8 @@ int msm_test_fp_add(const uint32_t* d_a, const uint32_t* d_b, uint32_t* d_out, s
 int msm_test_fp_sub(const uint32_t* d_a, const uint32_t* d_b, uint32_t* d_out, size_t n, void* stream);
 int msm_test_fp_inv(const uint32_t* d_a, uint32_t* d_out, size_t n, void* stream);
 int msm_test_glv(const uint32_t* d_scalars, size_t n, uint32_t* d_halfs, void* stream);
+int msm_test_row(int op, const uint32_t* d_a, const uint32_t* d_b, uint32_t* d_out, size_t n,
+                 uint32_t d, void* stream);
 int msm_test_issue_rate(int op, uint32_t blocks, uint32_t iters, uint32_t* d_out, void* stream);
 int msm_test_batched_add(const msm_g1_affine* d_a, const msm_g1_affine* d_b,
                          msm_g1_affine* d_out, size_t n, int S, void* stream);

@@ -91,6 +91,12 @@ def test_argument_errors_without_gpu():
     assert L.msm_test_issue_rate(0, 0, 1, p, None) == M.MSM_ERR_ARG
     assert L.msm_test_issue_rate(0, 1, 0, p, None) == M.MSM_ERR_ARG
     assert L.msm_test_issue_rate(0, 1, 1, None, None) == M.MSM_ERR_ARG
+    assert L.msm_test_row(7, p, p, p, 4, 0, None) == M.MSM_ERR_ARG      # unknown op
+    assert L.msm_test_row(-1, p, p, p, 4, 0, None) == M.MSM_ERR_ARG
+    assert L.msm_test_row(0, p, None, p, 4, 0, None) == M.MSM_ERR_ARG    # binary op, no b
+    assert L.msm_test_row(3, p, None, p, 4, 5000, None) == M.MSM_ERR_ARG  # d > 4096
+    assert L.msm_test_row(5, p, p, p, 8, 10, None) == M.MSM_ERR_ARG      # probe takes n = 4
+    assert L.msm_test_row(1, ctypes.c_void_p(6), p, p, 4, 0, None) == M.MSM_ERR_ARG
     assert L.msm_test_glv(p, 4, ctypes.c_void_p(4), None) == M.MSM_ERR_ARG
     # context creation with a NULL out pointer
     assert L.msm_ctx_create(0, None) == M.MSM_ERR_ARG
