@@ -15,38 +15,48 @@ struct rchain {
   uint32_t X, U, M, z;
 };
 
+// One round: row r computes a_r b_r (lazy product); every row gets all four results.
+__device__ __forceinline__ row4 row_round(const row_consts& k, uint32_t a0, uint32_t a1, uint32_t a2,
+                                          uint32_t a3, uint32_t b0, uint32_t b1, uint32_t b2,
+                                          uint32_t b3) {
+  return row_gather(row_mul_lazy(row_pick(k, a0, a1, a2, a3), row_pick(k, b0, b1, b2, b3), k));
+}
+
+// Two doublings in five rounds. Values stay in the lazy form [0, 3p); the field
+// combinations between rounds are one linear combination each (rowfp.hpp):
+//   X' = M^2 - 2 X V,  U' = 6 (M X) V - 2 M M^2 - V^2,  M' = 3 X'^2.
 __device__ __forceinline__ void row_chain_dbl2(rchain& c, const row_consts& k) {
   // round A: V = U^2, M X, M^2, z U
-  row4 r = row_gather(row_mul(row_pick(k, c.U, c.M, c.M, c.z), row_pick(k, c.U, c.X, c.M, c.U), k));
+  row4 r = row_round(k, c.U, c.M, c.M, c.z, c.U, c.X, c.M, c.U);
   const uint32_t V = r.r0, MX = r.r1, MM = r.r2, z1 = r.r3;
   // round B: X V, (M X) V, M M^2, V^2
-  r = row_gather(row_mul(row_pick(k, c.X, MX, c.M, V), row_pick(k, V, V, MM, V), k));
+  r = row_round(k, c.X, MX, c.M, V, V, V, MM, V);
   const uint32_t XV = r.r0, MXV = r.r1, M3 = r.r2, VV = r.r3;
-  const uint32_t X1 = row_sub(MM, row_dbl(XV, k), k);
-  const uint32_t U1 = row_sub(row_dbl(row_sub(row_triple(MXV, k), M3, k), k), VV, k);
+  const uint32_t X1 = row_lin_a_2b(MM, XV, k);
+  const uint32_t U1 = row_lin_6a_2b_c(MXV, M3, VV, k);
   // round C: X1^2, V1 = U1^2, z1 U1 (row 3 repeats row 0)
-  r = row_gather(row_mul(row_pick(k, X1, U1, z1, X1), row_pick(k, X1, U1, U1, X1), k));
-  const uint32_t M1 = row_triple(r.r0, k), V1 = r.r1;
+  r = row_round(k, X1, U1, z1, X1, X1, U1, U1, X1);
+  const uint32_t M1 = row_lin_3a(r.r0, k), V1 = r.r1;
   c.z = r.r2;
   // round D: M1 X1, M1^2, X1 V1, V1^2
-  r = row_gather(row_mul(row_pick(k, M1, M1, X1, V1), row_pick(k, X1, M1, V1, V1), k));
+  r = row_round(k, M1, M1, X1, V1, X1, M1, V1, V1);
   const uint32_t M1X1 = r.r0, MM1 = r.r1, X1V1 = r.r2, VV1 = r.r3;
-  c.X = row_sub(MM1, row_dbl(X1V1, k), k);
+  c.X = row_lin_a_2b(MM1, X1V1, k);
   // round E: (M1 X1) V1, M1 M1^2, X2^2 (row 3 repeats row 2)
-  r = row_gather(row_mul(row_pick(k, M1X1, M1, c.X, c.X), row_pick(k, V1, MM1, c.X, c.X), k));
-  c.U = row_sub(row_dbl(row_sub(row_triple(r.r0, k), r.r1, k), k), VV1, k);
-  c.M = row_triple(r.r2, k);
+  r = row_round(k, M1X1, M1, c.X, c.X, V1, MM1, c.X, c.X);
+  c.U = row_lin_6a_2b_c(r.r0, r.r1, VV1, k);
+  c.M = row_lin_3a(r.r2, k);
 }
 
 __device__ __forceinline__ void row_chain_dbl1(rchain& c, const row_consts& k) {
-  row4 r = row_gather(row_mul(row_pick(k, c.U, c.M, c.M, c.z), row_pick(k, c.U, c.X, c.M, c.U), k));
+  row4 r = row_round(k, c.U, c.M, c.M, c.z, c.U, c.X, c.M, c.U);
   const uint32_t V = r.r0, MX = r.r1, MM = r.r2;
   c.z = r.r3;
-  r = row_gather(row_mul(row_pick(k, c.X, MX, c.M, V), row_pick(k, V, V, MM, V), k));
+  r = row_round(k, c.X, MX, c.M, V, V, V, MM, V);
   const uint32_t XV = r.r0, MXV = r.r1, M3 = r.r2, VV = r.r3;
-  c.X = row_sub(MM, row_dbl(XV, k), k);
-  c.U = row_sub(row_dbl(row_sub(row_triple(MXV, k), M3, k), k), VV, k);
-  c.M = row_triple(row_mul(c.X, c.X, k), k);  // every row computes X'^2
+  c.X = row_lin_a_2b(MM, XV, k);
+  c.U = row_lin_6a_2b_c(MXV, M3, VV, k);
+  c.M = row_lin_3a(row_mul_lazy(c.X, c.X, k), k);  // every row computes X'^2
 }
 
 // 2^n p for a point p that every lane of the wavefront holds (per-lane form); the result
@@ -62,10 +72,10 @@ __device__ __forceinline__ xyzz row_dbl_n(const xyzz& p, uint32_t n, const row_c
   for (uint32_t i = 0; i < n / 2; i++) row_chain_dbl2(c, k);
   if (n & 1u) row_chain_dbl1(c, k);
   dchain e;
-  e.X = row_to_fp(c.X);
-  e.U = row_to_fp(c.U);
-  e.M = row_to_fp(c.M);
-  e.z = row_to_fp(c.z);
+  e.X = row_to_fp(row_canon(c.X, k));
+  e.U = row_to_fp(row_canon(c.U, k));
+  e.M = fp_zero();  // not used by quad_chain_end
+  e.z = row_to_fp(row_canon(c.z, k));
   return quad_chain_end(e, p.ZZ, p.ZZZ, q);
 }
 

@@ -92,6 +92,9 @@ struct row_consts {
   uint32_t pl[8], ph[8], nl[8], nh[8];
   uint32_t plo;
   uint32_t m0, m1;  // all ones where bit 0 / bit 1 of the row index is set
+  // lanes 0..7 (0 above): words of 11 p - 2 (2^256 - 1), 16 p - 3 (2^256 - 1) and 2^256 - p,
+  // and a mask of all ones
+  uint32_t c2, c3, negp, lo8;
 };
 
 // p and n' = -p^-1 mod 2^256, each between eight zero words on either side so that word
@@ -105,6 +108,18 @@ __device__ const uint32_t kRowNp[24] = {
     0xe4866389u, 0x87d20782u, 0x1eca6ac9u, 0x9ede7d65u,
     0x1833da80u, 0xd8afcbd0u, 0x91888c6bu, 0xf57a22b7u,
     0, 0, 0, 0, 0, 0, 0, 0};
+
+// Offsets of the linear combinations (row_lin2, row_lin3 below) and 2^256 - p, then eight
+// zero words, so that lane l reads entry l.
+__device__ const uint32_t kRowC2[16] = {
+    0x4d5ee20fu, 0x956604fbu, 0x7ce3b411u, 0x828f943fu,
+    0x908ecc05u, 0xeb72fed7u, 0xad21e1cau, 0x144f5eefu, 0, 0, 0, 0, 0, 0, 0, 0};
+__device__ const uint32_t kRowC3[16] = {
+    0x87cfd473u, 0xc208c16du, 0x871ca8d3u, 0x7816a916u,
+    0x181585d9u, 0x85045b68u, 0x131a029bu, 0x0644e72eu, 0, 0, 0, 0, 0, 0, 0, 0};
+__device__ const uint32_t kRowNegP[16] = {
+    0x278302b9u, 0xc3df73e9u, 0x978e3572u, 0x687e956eu,
+    0x7e7ea7a2u, 0x47afba49u, 0x1ece5fd6u, 0xcf9bb18du, 0, 0, 0, 0, 0, 0, 0, 0};
 
 __device__ __forceinline__ row_consts row_consts_load() {
   const uint32_t lane = __lane_id(), l = lane & 15u;
@@ -120,6 +135,10 @@ __device__ __forceinline__ row_consts row_consts_load() {
   k.plo = kRowP[8 + l] * (l < 8 ? 1u : 0u);
   k.m0 = ((lane >> 4) & 1u) ? 0xffffffffu : 0u;
   k.m1 = ((lane >> 5) & 1u) ? 0xffffffffu : 0u;
+  k.c2 = kRowC2[l];
+  k.c3 = kRowC3[l];
+  k.negp = kRowNegP[l];
+  k.lo8 = l < 8 ? 0xffffffffu : 0u;
   return k;
 }
 
@@ -191,8 +210,17 @@ __device__ __forceinline__ uint32_t row_sub(uint32_t a, uint32_t b, const row_co
   return e + (row_lane_bit(C2) ? 1u : 0u);
 }
 
+// Montgomery product without the final subtraction: U / 2^256 for a, b < 3p, which is
+// below 9 p^2 / 2^256 + p < 2.71 p (p < 0.19 * 2^256), so the lazy form [0, 3p) is closed
+// under it. With a, b < p it is below 2p.
+__device__ __forceinline__ uint32_t row_mul_lazy(uint32_t a, uint32_t b, const row_consts& k);
+
 // Montgomery product a b 2^-256 mod p of two row-form elements.
 __device__ __forceinline__ uint32_t row_mul(uint32_t a, uint32_t b, const row_consts& k) {
+  return row_sub_p_if_ge(row_mul_lazy(a, b, k), k);
+}
+
+__device__ __forceinline__ uint32_t row_mul_lazy(uint32_t a, uint32_t b, const row_consts& k) {
   const uint32_t bl = b & 0xffffu, bh = b >> 16;
   uint64_t SL = 0, SH = 0;
   row_for<0, 8>([&](auto ic) {
@@ -219,8 +247,57 @@ __device__ __forceinline__ uint32_t row_mul(uint32_t a, uint32_t b, const row_co
     SL += (uint64_t)mi * k.pl[i];
     SH += (uint64_t)mi * k.ph[i];
   });
-  const uint32_t U = row_columns(SL, SH);  // lanes 0..7: 0; lanes 8..15: U / 2^256 < 2p
-  return row_sub_p_if_ge(row_shl<8>(U), k);
+  const uint32_t U = row_columns(SL, SH);  // lanes 0..7: 0; lanes 8..15: U / 2^256
+  return row_shl<8>(U);
+}
+
+// ---- linear combinations in the lazy form [0, 3p) ---------------------------------------
+// A small combination of lazy elements, ka a - kb b - kc c, is formed per lane as the column
+// ka a_l + kb ~b_l + kc ~c_l + C_l, where ~ is the word-wise complement (2^32 - 1 - w) and
+// C = K p - (kb + kc)(2^256 - 1) >= 0 makes the whole value V = ka a - kb b - kc c + K p
+// non-negative and below 2^259 (lanes 0..8). Then q ~ V / p is estimated from V's top 64 bits
+// and V - q p (formed as V + q (2^256 - p) mod 2^256) is the result. The estimate is never
+// above floor(V / p) and at most 2 below it, so the result lies in [0, 3p).
+
+// Words (lanes 0..8) of sum_l x_l 2^(32 l), x_l < 2^38 given in lanes 0..7.
+__device__ __forceinline__ uint32_t row_resolve(uint64_t x) {
+  const uint32_t c1s = row_shr<1>((uint32_t)(x >> 32));
+  const uint32_t w = (uint32_t)x + c1s;
+  return row_carry16(w, row_lt(w, c1s));
+}
+
+// V - q p in [0, 3p) for V < 2^259 in lanes 0..8 with V = r (mod p). q = floor of
+// (V >> 224) times a float just below 1 / (p_7 + 1) (p_7 = p >> 224): the float error
+// (below 2^-21 relative) is smaller than the factor's margin (2^-18), so q <= V / p, and
+// q is at least floor(V / p) - 2 because V / p < 35.
+__device__ __forceinline__ uint32_t row_reduce_q(uint32_t V, const row_consts& k) {
+  const float top = (float)row_bcast<8>(V) * 0x1.52917cp+2f + (float)row_bcast<7>(V) * 0x1.52917cp-30f;
+  const uint32_t q = (uint32_t)top;
+  const uint64_t y = (uint64_t)q * k.negp + (V & k.lo8);
+  return row_resolve(y) & k.lo8;  // mod 2^256: what reaches lane 8 is dropped
+}
+
+// a - 2b, b < 3p, via 11 p - 2 (2^256 - 1).
+__device__ __forceinline__ uint32_t row_lin_a_2b(uint32_t a, uint32_t b, const row_consts& k) {
+  const uint64_t x = (uint64_t)(~b & k.lo8) * 2u + a + k.c2;
+  return row_reduce_q(row_resolve(x), k);
+}
+
+// 6a - 2b - c, via 16 p - 3 (2^256 - 1).
+__device__ __forceinline__ uint32_t row_lin_6a_2b_c(uint32_t a, uint32_t b, uint32_t c,
+                                                    const row_consts& k) {
+  const uint64_t x = (uint64_t)a * 6u + (uint64_t)(~b & k.lo8) * 2u + (~c & k.lo8) + k.c3;
+  return row_reduce_q(row_resolve(x), k);
+}
+
+// 3a.
+__device__ __forceinline__ uint32_t row_lin_3a(uint32_t a, const row_consts& k) {
+  return row_reduce_q(row_resolve((uint64_t)a * 3u), k);
+}
+
+// The fully reduced element of a lazy one (< 3p).
+__device__ __forceinline__ uint32_t row_canon(uint32_t a, const row_consts& k) {
+  return row_sub_p_if_ge(row_sub_p_if_ge(a, k), k);
 }
 
 // Operand of this row: a0 on row 0, a1 on row 1, ...

@@ -123,6 +123,78 @@ def row_mul(a, b):
     return sub_p_if_ge(shl(U, 8), plo)
 
 
+# ---- lazy form [0, 3p) and linear combinations -----------------------------------------
+C2 = 11 * P - 2 * (R - 1)
+C3 = 16 * P - 3 * (R - 1)
+NEGP = R - P
+P7 = P >> 224
+
+
+def lane_words(x):
+    return [word(x, i & 15) if (i & 15) < 8 else 0 for i in range(64)]
+
+
+def row_mul_lazy(a, b):
+    pl, ph, nl, nh, plo = K
+    bl, bh = [x & 0xFFFF for x in b], [x >> 16 for x in b]
+    SL, SH = [0] * 64, [0] * 64
+    for i in range(8):
+        ai = bcast(a, i)
+        SL = [s + x * y for s, x, y in zip(SL, ai, shr(bl, i))]
+        SH = [s + x * y for s, x, y in zip(SH, ai, shr(bh, i))]
+    T = columns(SL, SH)
+    SL, SH = [0] * 64, [0] * 64
+    for i in range(8):
+        ti = bcast(T, i)
+        SL = [s + x * y for s, x, y in zip(SL, ti, nl[i])]
+        SH = [s + x * y for s, x, y in zip(SH, ti, nh[i])]
+    m = columns(SL, SH)
+    SL, SH = list(T), [0] * 64
+    for i in range(8):
+        mi = bcast(m, i)
+        SL = [s + x * y for s, x, y in zip(SL, mi, pl[i])]
+        SH = [s + x * y for s, x, y in zip(SH, mi, ph[i])]
+    return shl(columns(SL, SH), 8)
+
+
+def resolve(x):
+    assert all(v < 1 << 38 for v in x)  # c0 + c1 of the lane below carries at most 1
+    c1s = shr([v >> 32 for v in x], 1)
+    w = [((v & M32) + c) & M32 for v, c in zip(x, c1s)]
+    return carry16(w, [u < c for u, c in zip(w, c1s)])
+
+
+def reduce_q(V, q_shift=0):
+    """V - q p with q estimated from V's top 64 bits (the kernel's float estimate is never
+    above floor((V >> 224) / (p_7 + 1)) and at most one below it; q_shift = 1 takes that
+    lower end)."""
+    lo8 = lane_words(R - 1)
+    out = []
+    for r in range(4):
+        top = (V[16 * r + 8] << 32) | V[16 * r + 7]
+        q = max(0, top // (P7 + 1) - q_shift)
+        out += [q] * 16
+    y = [q * n + (v & m) for q, n, v, m in zip(out, lane_words(NEGP), V, lo8)]
+    return [w & m for w, m in zip(resolve(y), lo8)]
+
+
+def lin_a_2b(a, b, q_shift=0):
+    lo8 = lane_words(R - 1)
+    x = [2 * ((~v & M32) & m) + u + c for u, v, m, c in zip(a, b, lo8, lane_words(C2))]
+    return reduce_q(resolve(x), q_shift)
+
+
+def lin_6a_2b_c(a, b, c, q_shift=0):
+    lo8 = lane_words(R - 1)
+    x = [6 * u + 2 * ((~v & M32) & m) + ((~w & M32) & m) + k
+         for u, v, w, m, k in zip(a, b, c, lo8, lane_words(C3))]
+    return reduce_q(resolve(x), q_shift)
+
+
+def lin_3a(a, q_shift=0):
+    return reduce_q(resolve([3 * u for u in a]), q_shift)
+
+
 def row_add(a, b):
     s = [(x + y) & M32 for x, y in zip(a, b)]
     return sub_p_if_ge(carry16(s, [x < y for x, y in zip(s, b)]), K[4])
@@ -207,3 +279,42 @@ def test_carry_resolution_ripples_a_whole_row():
     out = carry16(w, h)
     assert out[0] == 5 and out[1:16] == [0] * 15
     assert out[16:] == [M32] * 48
+
+
+def test_lazy_form_closed_under_products_and_combinations():
+    rng = random.Random(8)
+    rinv = pow(R, -1, P)
+    lazy = [0, 1, P - 1, P, P + 1, 2 * P - 1, 2 * P, 3 * P - 1, 3 * P - 2, 2 * P + (1 << 200)]
+    lazy += [rng.randrange(3 * P) for _ in range(60)]
+    for k in range(0, 64, 4):
+        xs, ys, zs = lazy[k:k + 4], lazy[k + 4:k + 8], lazy[k + 8:k + 12]
+        if len(zs) < 4:
+            break
+        A, B, Cv = pack(xs), pack(ys), pack(zs)
+        got = unpack(row_mul_lazy(A, B))
+        for g, x, y in zip(got, xs, ys):
+            assert g < 3 * P and g % P == x * y * rinv % P
+        for sh in (0, 1):
+            for g, x, y in zip(unpack(lin_a_2b(A, B, sh)), xs, ys):
+                assert g < 3 * P and g % P == (x - 2 * y) % P
+            for g, x, y, z in zip(unpack(lin_6a_2b_c(A, B, Cv, sh)), xs, ys, zs):
+                assert g < 3 * P and g % P == (6 * x - 2 * y - z) % P
+            for g, x in zip(unpack(lin_3a(A, sh)), xs):
+                assert g < 3 * P and g % P == 3 * x % P
+
+
+def test_lazy_offsets_and_estimate_bounds():
+    assert C2 >= 0 and C3 >= 0 and C2 == 11 * P - 2 * (R - 1) and C3 == 16 * P - 3 * (R - 1)
+    # the largest combination stays below 2^259 (lanes 0..8) and below 35 p
+    assert 6 * 3 * P + 2 * (R - 1) + (R - 1) + C3 < min(1 << 259, 35 * P)
+    # the kernel's float factor is below 1 / (p_7 + 1) by more than the float error (2^-21)
+    f = float.fromhex("0x1.52917cp-30")
+    assert f * (P7 + 1) < 1 - 2 ** -19
+    assert f * (P7 + 1) > 1 - 2 ** -17
+    assert float.fromhex("0x1.52917cp+2") == f * 2 ** 32
+    src = open(ROWFP).read()
+    for name, val in (("kRowC2", C2), ("kRowC3", C3), ("kRowNegP", NEGP)):
+        body = src[src.index(name + "[16]"):]
+        body = body[:body.index("};")]
+        ws = [int(w, 16) for w in re.findall(r"0x([0-9a-f]+)u", body)]
+        assert sum(w << (32 * i) for i, w in enumerate(ws)) == val, name
