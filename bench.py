@@ -92,7 +92,7 @@ def counter_record(kind: str, workload: str, S: int, affine_levels: int, src: st
 
 def plane_exponents(c: int) -> list[int]:
     """Exponents of the reduction's planes (the doubling-run lengths of the window
-    combine), by the rule of make_planes in the reduction source."""
+    combine), by the rule of make_planes in the library's host plan."""
     nwin = (128 + c - 1) // c
     lam = 3 if c >= 15 else 2
     slots = 1 << (c - 1)

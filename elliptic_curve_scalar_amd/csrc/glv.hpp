@@ -93,6 +93,41 @@ __device__ __forceinline__ void sign_magnitude(const uint32_t (&k)[8], uint32_t 
   o[3] = m[3] | (neg << 31);
 }
 
+// s 2^-256 mod r for any 256-bit s: the scalar of a Montgomery-form F_r element (s = x 2^256
+// mod r, how a prover's field code keeps scalars). Word-serial Montgomery reduction: eight
+// steps of t = (t + m r) / 2^32 with m = t_0 (-r^-1) mod 2^32, then one subtraction of r
+// ((s + M r) / 2^256 < 1 + r).
+__device__ __forceinline__ void fr_from_mont(uint32_t (&s)[8]) {
+  const uint32_t r[8] = {0xf0000001u, 0x43e1f593u, 0x79b97091u, 0x2833e848u,
+                         0x8181585du, 0xb85045b6u, 0xe131a029u, 0x30644e72u};
+  const uint32_t rinv = 0xefffffffu;  // -r^-1 mod 2^32
+  uint32_t t[9];
+#pragma unroll
+  for (int i = 0; i < 8; i++) t[i] = s[i];
+  t[8] = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const uint32_t m = t[0] * rinv;
+    uint64_t acc = (uint64_t)m * r[0] + t[0];  // low word becomes 0
+    uint32_t cy = (uint32_t)(acc >> 32);
+#pragma unroll
+    for (int j = 1; j < 8; j++) {
+      acc = (uint64_t)m * r[j] + t[j] + cy;
+      t[j - 1] = (uint32_t)acc;
+      cy = (uint32_t)(acc >> 32);
+    }
+    acc = (uint64_t)t[8] + cy;
+    t[7] = (uint32_t)acc;
+    t[8] = (uint32_t)(acc >> 32);
+  }
+  uint32_t d[8], borrow = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) d[i] = __builtin_subc(t[i], r[i], borrow, &borrow);
+  // t <= r: keep t when it is below r (borrow), else t - r (= 0)
+#pragma unroll
+  for (int i = 0; i < 8; i++) s[i] = borrow ? t[i] : d[i];
+}
+
 // s (any 256-bit integer) -> (k1, k2) with s = k1 + k2 lambda (mod r), each as four
 // words of magnitude with its sign in bit 127.
 __device__ __forceinline__ void glv_split(const uint32_t (&s_in)[8], uint32_t (&k1)[4],

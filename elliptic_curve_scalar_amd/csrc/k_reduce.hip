@@ -123,9 +123,7 @@ __device__ __forceinline__ void block_quad_sum(xyzz acc, xyzz_st* lds, xyzz_st* 
   if (threadIdx.x == 0) xyzz_store(out, acc);
 }
 
-// Elements of a plane, and its blocks of partial sums (PLANE_PER_BLOCK elements each).
-constexpr uint32_t PLANE_PER_QUAD = 4;
-constexpr uint32_t PLANE_PER_BLOCK = 64 * PLANE_PER_QUAD;
+// Elements of a plane (its blocks of partial sums hold PLANE_PER_BLOCK elements each).
 
 __device__ __forceinline__ uint32_t plane_count(const plane_table& pt, uint32_t sel) {
   return sel ? pt.nseg >> 1 : pt.nseg;
@@ -198,46 +196,6 @@ __global__ void __launch_bounds__(64) k_plane_chain(const xyzz_st* __restrict__ 
 }
 
 // ------------------------------------------------------------------ host side
-// log2 of the segment length: segments of 4 slots up to c = 14, 8 at c = 15 and 16, so a
-// window has at most 4096 segments and a plane at most 16 blocks of partial sums.
-static uint32_t seg_log2(uint32_t c) { return c >= 15 ? 3u : 2u; }
-
-plane_table make_planes(uint32_t c, uint32_t nwin) {
-  plane_table pt;
-  memset(&pt, 0, sizeof pt);
-  const uint32_t lambda = seg_log2(c);
-  const uint32_t slots = 1u << (c - 1);
-  const uint32_t nseg = slots > (1u << lambda) ? slots >> lambda : 1u;
-  uint32_t lgseg = 0;
-  while ((1u << lgseg) < nseg) lgseg++;
-  pt.nseg = nseg;
-  pt.lambda = lambda;
-  pt.nb = (nseg + PLANE_PER_BLOCK - 1) / PLANE_PER_BLOCK;
-  // (exponent, window, selector) of every plane
-  uint32_t tmp[MAX_PLANES];
-  uint32_t n = 0;
-  for (uint32_t j = 0; j < nwin; j++) {
-    const uint32_t phi = (j + 1 == nwin) ? c * nwin - 128 : 0;  // log2 of window_spread
-    tmp[n++] = (c * j) | (j << 8);                               // the (R + T) plane
-    for (uint32_t beta = 0; beta < lgseg; beta++) {
-      // bit kappa of w_lo(s) - 1 = (s << lambda) >> phi is bit kappa + phi - lambda of s
-      if (beta + lambda < phi) continue;
-      const uint32_t kappa = beta + lambda - phi;
-      tmp[n++] = (c * j + kappa) | (j << 8) | ((beta + 1) << 16);
-    }
-  }
-  // decreasing exponent: the longest runs of doublings are dispatched first
-  for (uint32_t a = 1; a < n; a++)
-    for (uint32_t b = a; b > 0 && (tmp[b] & 0xffu) > (tmp[b - 1] & 0xffu); b--) {
-      const uint32_t t = tmp[b];
-      tmp[b] = tmp[b - 1];
-      tmp[b - 1] = t;
-    }
-  pt.n = n;
-  for (uint32_t i = 0; i < n; i++) pt.e[i] = tmp[i];
-  return pt;
-}
-
 hipError_t launch_reduce(const xyzz_st* bsum, uint32_t c, uint32_t nwin, const plane_table& pt,
                          xyzz_st* tseg, xyzz_st* pseg, xyzz_st* part, hipStream_t s) {
   const size_t quads = (size_t)nwin * pt.nseg;

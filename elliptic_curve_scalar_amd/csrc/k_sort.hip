@@ -59,13 +59,14 @@ __device__ __forceinline__ void for_each_signed_digit(const sc256& s, uint32_t c
 __global__ void __launch_bounds__(128) k_glv_prep(const g1a* __restrict__ points,
                                                   const uint32_t* __restrict__ scalars, uint32_t n,
                                                   g1a* __restrict__ pts2, uint32_t* __restrict__ halfs,
-                                                  msm_stats* st, int verify) {
+                                                  msm_stats* st, int verify, int scalar_form) {
   uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   const sc256 sc = load_scalar(scalars, i);
   uint32_t s[8], k1[4], k2[4];
 #pragma unroll
   for (int w = 0; w < 8; w++) s[w] = sc.w[w];
+  if (scalar_form) fr_from_mont(s);
   bool bad = false;
   glv_split(s, k1, k2, bad);
   if (bad) atomicOr(&st->range_flag, 1u);
@@ -390,8 +391,9 @@ hipError_t launch_fill(uint32_t* p, size_t n, uint32_t v, hipStream_t st) {
 }
 
 hipError_t launch_glv_prep(const g1a* points, const uint32_t* scalars, uint32_t n, g1a* pts2,
-                           uint32_t* halfs, msm_stats* st, int verify, hipStream_t s) {
-  k_glv_prep<<<grid_for(n, 128), 128, 0, s>>>(points, scalars, n, pts2, halfs, st, verify);
+                           uint32_t* halfs, msm_stats* st, int verify, int scalar_form, hipStream_t s) {
+  k_glv_prep<<<grid_for(n, 128), 128, 0, s>>>(points, scalars, n, pts2, halfs, st, verify,
+                                                scalar_form);
   return hipGetLastError();
 }
 

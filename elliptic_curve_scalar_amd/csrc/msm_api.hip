@@ -11,6 +11,52 @@
 #include "../../include/msm.h"
 #include "msm_internal.hpp"
 
+// ------------------------------------------------------------------ reduction planes
+namespace msmk {
+
+// Plane table of the bucket reduction (k_reduce.hip states the decomposition).
+// log2 of the segment length: segments of 4 slots up to c = 14, 8 at c = 15 and 16, so a
+// window has at most 4096 segments and a plane at most 16 blocks of partial sums.
+static uint32_t seg_log2(uint32_t c) { return c >= 15 ? 3u : 2u; }
+
+plane_table make_planes(uint32_t c, uint32_t nwin) {
+  plane_table pt;
+  memset(&pt, 0, sizeof pt);
+  const uint32_t lambda = seg_log2(c);
+  const uint32_t slots = 1u << (c - 1);
+  const uint32_t nseg = slots > (1u << lambda) ? slots >> lambda : 1u;
+  uint32_t lgseg = 0;
+  while ((1u << lgseg) < nseg) lgseg++;
+  pt.nseg = nseg;
+  pt.lambda = lambda;
+  pt.nb = (nseg + PLANE_PER_BLOCK - 1) / PLANE_PER_BLOCK;
+  // (exponent, window, selector) of every plane
+  uint32_t tmp[MAX_PLANES];
+  uint32_t n = 0;
+  for (uint32_t j = 0; j < nwin; j++) {
+    const uint32_t phi = (j + 1 == nwin) ? c * nwin - 128 : 0;  // log2 of window_spread
+    tmp[n++] = (c * j) | (j << 8);                               // the (R + T) plane
+    for (uint32_t beta = 0; beta < lgseg; beta++) {
+      // bit kappa of w_lo(s) - 1 = (s << lambda) >> phi is bit kappa + phi - lambda of s
+      if (beta + lambda < phi) continue;
+      const uint32_t kappa = beta + lambda - phi;
+      tmp[n++] = (c * j + kappa) | (j << 8) | ((beta + 1) << 16);
+    }
+  }
+  // decreasing exponent: the longest runs of doublings are dispatched first
+  for (uint32_t a = 1; a < n; a++)
+    for (uint32_t b = a; b > 0 && (tmp[b] & 0xffu) > (tmp[b - 1] & 0xffu); b--) {
+      const uint32_t t = tmp[b];
+      tmp[b] = tmp[b - 1];
+      tmp[b - 1] = t;
+    }
+  pt.n = n;
+  for (uint32_t i = 0; i < n; i++) pt.e[i] = tmp[i];
+  return pt;
+}
+
+}  // namespace msmk
+
 using namespace msmk;
 
 namespace {
@@ -167,6 +213,7 @@ struct msm_ctx {
   int affine_levels = 1;  // leading pair-tree levels done with batched affine adds
   int walker_device_state = 1;  // stream walker: accumulators on the device (1) or private (0)
   int prefix_store = 0;  // batched-affine level: prefix products private (0) / LDS (1), +2 dx cache
+  int scalar_form = 0;   // scalars as integers (0) or Montgomery-form F_r elements (1)
   void* ws = nullptr;
   size_t ws_bytes = 0;
   msm_stats* host_stats = nullptr;  // pinned: the plan, then the result's verify flag
@@ -267,7 +314,7 @@ int run_pipeline(msm_ctx* ctx, const g1a* d_points, const uint32_t* d_scalars, s
   // waits for the plan
   PhaseMark ph_sort(ctx, st, PH_SORT, tl);
   HIP_TRY(launch_fill((uint32_t*)stats, sizeof(msm_stats) / 4, 0, st));
-  HIP_TRY(launch_glv_prep(d_points, d_scalars, n32, pts2, halfs, stats, verify, st));
+  HIP_TRY(launch_glv_prep(d_points, d_scalars, n32, pts2, halfs, stats, verify, ctx->scalar_form, st));
   HIP_TRY(launch_hist(halfs, m32, c32, L.nwin, L.chunk, L.nchunk, hist_blk, counts, rank, stats, st));
   HIP_TRY(launch_scan(counts, L.K, -1, 1, block_sums, offsets, L.K + 1, nullptr, st));
   HIP_TRY(hipMemcpyAsync(ctx->host_stats, stats, sizeof(msm_stats), hipMemcpyDeviceToHost, st));
@@ -512,6 +559,14 @@ int msm_ctx_set_prefix_store(msm_ctx* ctx, int store) {
   if (!ctx) return fail(MSM_ERR_ARG, "ctx is NULL%s");
   if (store < 0 || store > 4) return fail(MSM_ERR_ARG, "store must be in 0..4%s");
   ctx->prefix_store = store;
+  return MSM_OK;
+}
+
+int msm_ctx_set_scalar_form(msm_ctx* ctx, int form) {
+  if (!ctx) return fail(MSM_ERR_ARG, "ctx is NULL%s");
+  if (form != MSM_SCALARS_INTEGER && form != MSM_SCALARS_MONTGOMERY)
+    return fail(MSM_ERR_ARG, "form must be MSM_SCALARS_INTEGER or MSM_SCALARS_MONTGOMERY%s");
+  ctx->scalar_form = form;
   return MSM_OK;
 }
 

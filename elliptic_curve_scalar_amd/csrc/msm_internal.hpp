@@ -49,7 +49,7 @@ hipError_t launch_fill(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
 // verify != 0 also checks every input point (reduced coordinates, on the curve or
 // (0, 0)) and sets st->bad_point when one fails.
 hipError_t launch_glv_prep(const g1a* points, const uint32_t* scalars, uint32_t n, g1a* pts2,
-                           uint32_t* halfs, msm_stats* st, int verify, hipStream_t s);
+                           uint32_t* halfs, msm_stats* st, int verify, int scalar_form, hipStream_t s);
 // *flag |= 1 when the affine point p is neither (0, 0) nor a reduced point on the curve.
 hipError_t launch_verify_point(const g1a* p, uint32_t* flag, hipStream_t s);
 // Counting pass: per (chunk of half-scalars, window) LDS histograms into hist_blk
@@ -125,8 +125,11 @@ hipError_t launch_walk(int S, bool dev_state, const walk_args& a, hipStream_t s)
 // merge_passes pair passes over the partial sums, then the split buckets' sums.
 hipError_t launch_walk_merge(int S, const walk_args& a, uint32_t merge_passes, hipStream_t s);
 
-// Planes of the reduction for window width c and nwin windows.
+// Planes of the reduction for window width c and nwin windows (host side of the plan).
 plane_table make_planes(uint32_t c, uint32_t nwin);
+// Plane elements per quad and per block of partial sums (k_plane_sums).
+constexpr uint32_t PLANE_PER_QUAD = 4;
+constexpr uint32_t PLANE_PER_BLOCK = 64 * PLANE_PER_QUAD;
 // Segment sums (tseg, pseg: nwin nseg points each) and per-plane partial sums (part:
 // n nb points).
 hipError_t launch_reduce(const xyzz_st* bsum, uint32_t c, uint32_t nwin, const plane_table& pt,

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmsm.so")
 
 MSM_OK, MSM_ERR_ARG, MSM_ERR_HIP, MSM_ERR_OOM, MSM_ERR_RANGE, MSM_ERR_OFF_CURVE = 0, -1, -2, -3, -4, -5
 MSM_SCHED_PAIR_TREE, MSM_SCHED_WALKER = 0, 1
+MSM_SCALARS_INTEGER, MSM_SCALARS_MONTGOMERY = 0, 1
 MSM_MAX_N = 1 << 26
 MSM_NOALLOC_MAX_BYTES = 64 << 20
 VALID_S = (4, 8, 16, 32)
@@ -37,6 +38,7 @@ SYMBOLS = {
     "msm_ctx_set_affine_levels": (_I, [_P, _I]),
     "msm_ctx_set_walker_state": (_I, [_P, _I]),
     "msm_ctx_set_prefix_store": (_I, [_P, _I]),
+    "msm_ctx_set_scalar_form": (_I, [_P, _I]),
     "msm_ctx_set_timing": (_I, [_P, _I]),
     "msm_ctx_timing_read": (_I, [_P, _P]),
     "msm_test_fp": (_I, [_I, _P, _P, _P, _S, _P]),
@@ -153,6 +155,10 @@ class Context:
         """Pair-tree level-0 slot state: 0 private, 1 LDS, 2 private and 3 LDS with the
         denominators cached, 4 one prefix in four stored (checkpoints)."""
         _check(lib().msm_ctx_set_prefix_store(self._h, int(store)))
+
+    def set_scalar_form(self, form: int):
+        """MSM_SCALARS_INTEGER (default) or MSM_SCALARS_MONTGOMERY (x * 2^256 mod r)."""
+        _check(lib().msm_ctx_set_scalar_form(self._h, int(form)))
 
     def set_timing(self, level: int = 2):
         """0 off, 1 the batched-affine level kernels only, 2 every phase (True = 2)."""

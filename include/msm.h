@@ -60,6 +60,12 @@ enum {
   MSM_SCHED_WALKER = 1     /* stream walker: S slots per lane walk equal chunks of the lists */
 };
 
+/* Scalar forms (msm_ctx_set_scalar_form). */
+enum {
+  MSM_SCALARS_INTEGER = 0,   /* s_i as 256-bit little-endian integers (any value; used mod r) */
+  MSM_SCALARS_MONTGOMERY = 1 /* s_i as Montgomery-form F_r elements, x * 2^256 mod r */
+};
+
 /* Largest n accepted. Bucket lists are indexed with 32-bit offsets, so in addition
  * 2 n ceil(128 / c) must stay below 2^32 (every c >= 5 allows MSM_MAX_N). */
 #define MSM_MAX_N ((size_t)1 << 26)
@@ -204,6 +210,17 @@ int msm_ctx_set_walker_state(msm_ctx* ctx, int device_state);
  * NULL ctx or store outside 0 .. 4.
  */
 int msm_ctx_set_prefix_store(msm_ctx* ctx, int store);
+
+/*
+ * How the context's runs read the scalars: MSM_SCALARS_INTEGER (default) takes each
+ * s_i as a 256-bit integer, reduced mod r; MSM_SCALARS_MONTGOMERY takes s_i as the
+ * Montgomery form x * 2^256 mod r of the scalar x (how a prover's F_r code keeps
+ * scalars; the pages' scalars enter as field elements of barretenberg's "bb/msm") and
+ * converts it on the device (x = s_i * 2^-256 mod r, for any 256-bit s_i) before the
+ * GLV split. The layout is the same: eight little-endian 32-bit words per scalar.
+ * Returns MSM_ERR_ARG for a NULL ctx or another value.
+ */
+int msm_ctx_set_scalar_form(msm_ctx* ctx, int form);
 
 /*
  * Phase timing. msm_ctx_set_timing(ctx, level) makes msm_run record HIP events on its

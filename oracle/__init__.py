@@ -52,9 +52,10 @@ def lib():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
+    path = os.environ.get("ORACLE_LIB") or LIB_PATH  # another build (the sanitizer test's)
+    if path == LIB_PATH and not os.path.exists(LIB_PATH):
         build()
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     P, S = ctypes.c_void_p, ctypes.c_size_t
     I = ctypes.c_int
     sig = {

@@ -132,6 +132,11 @@ def test_run_argument_errors_without_gpu():
     assert L.msm_run_noalloc(None, p, p, 16, 13, 8, 0, 0, None, out) == M.MSM_ERR_ARG
     assert L.msm_run_noalloc(ctx, p, p, 16, 13, 8, 3, 0, None, out) == M.MSM_ERR_ARG
     assert L.msm_run_noalloc(ctx, p, p, 16, 17, 8, 0, 0, None, out) == M.MSM_ERR_ARG
+    # context knobs: NULL context and out-of-range values are refused before any use
+    assert L.msm_ctx_set_scalar_form(None, 0) == M.MSM_ERR_ARG
+    for form in (-1, 2):
+        assert L.msm_ctx_set_scalar_form(ctx, form) == M.MSM_ERR_ARG
+    assert (M.MSM_SCALARS_INTEGER, M.MSM_SCALARS_MONTGOMERY) == (0, 1)
 
 
 def test_binding_refuses_host_tensors():

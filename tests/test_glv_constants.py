@@ -139,3 +139,28 @@ def test_split_identity_and_bound():
         assert s_red == s % R
         assert (k1 + k2 * lam - s) % R == 0, s
         assert abs(k1) < (1 << 127) and abs(k2) < (1 << 127), s
+
+
+def test_montgomery_scalar_reduction_constants():
+    """fr_from_mont (glv.hpp): -r^-1 mod 2^32 and r as stored, and the word-serial
+    reduction (modelled on integers) gives s 2^-256 mod r for edge and random s."""
+    src = open(SRC).read()
+    body = src[src.index("fr_from_mont"):]
+    body = body[:body.index("uint32_t t[9]")]
+    words = [int(w, 16) for w in re.findall(r"0x([0-9a-f]+)u", body)]
+    r_words, rinv = words[:8], words[8]
+    assert _words(r_words) == ref.R
+    assert (rinv * ref.R) % (1 << 32) == (1 << 32) - 1
+
+    def model(s):
+        t = s
+        for _ in range(8):
+            m = (t * rinv) % (1 << 32)
+            t = (t + m * ref.R) >> 32
+        assert t <= ref.R  # one subtraction of r is enough
+        return t - ref.R if t >= ref.R else t
+
+    rng = random.Random(21)
+    rinv256 = pow(1 << 256, -1, ref.R)
+    for s in [0, 1, ref.R - 1, ref.R, (1 << 256) - 1] + [rng.getrandbits(256) for _ in range(500)]:
+        assert model(s) == s * rinv256 % ref.R

@@ -268,6 +268,34 @@ def test_full_range_scalars():
         assert np.array_equal(_gpu_msm(pts, sc, c, S), want), (c, S)
 
 
+def test_montgomery_form_scalars():
+    """With MSM_SCALARS_MONTGOMERY each scalar word vector s is read as x 2^256 mod r and
+    the result is sum x_i P_i, x_i = s_i 2^-256 mod r, for any 256-bit s_i (reduced or
+    not). Expected values: the oracle's Pippenger on the integers x_i and the closed form."""
+    M = _msm()
+    rng = random.Random(17)
+    dl = [rng.randrange(1, ref.R) for _ in range(300)]
+    pts = _pts(dl)
+    mont = [0, 1, ref.R - 1, ref.R, (1 << 256) - 1, (1 << 256) % ref.R] + \
+        [rng.getrandbits(256) for _ in range(294)]
+    rinv = pow(1 << 256, -1, ref.R)
+    xs = [m * rinv % ref.R for m in mont]
+    want = oracle.msm_pippenger(pts, wl.from_ints(xs), 13)
+    assert ref.decode_point(want) == ref.msm_linear(dl, xs)
+    ctx = M.Context(DEV)
+    try:
+        ctx.set_scalar_form(M.MSM_SCALARS_MONTGOMERY)
+        for c, S in ((8, 8), (13, 8), (16, 16)):
+            say("montgomery-form scalars c", c, "S", S)
+            got = to_host(ctx.run(to_dev(pts), to_dev(wl.from_ints(mont)), c, S))
+            assert np.array_equal(got, want), (c, S)
+        ctx.set_scalar_form(M.MSM_SCALARS_INTEGER)  # back to integers: the same words mean s_i
+        got = to_host(ctx.run(to_dev(pts), to_dev(wl.from_ints(xs)), 13, 8))
+        assert np.array_equal(got, want)
+    finally:
+        ctx.close()
+
+
 def test_timing_levels():
     """Level 1 times only the batched-affine kernels, level 2 every phase, 0 nothing;
     the result does not depend on the level."""

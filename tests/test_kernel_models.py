@@ -4,7 +4,8 @@ each checked against the plain definition it replaces:
 * the top-window spread (kern_util.hpp, window_spread; k_sort.hip, digit_slot): with 127-bit
   half-scalar magnitudes the top window's digit never exceeds 2^(127 - c (W - 1)), so
   spreading each digit over 2^(c W - 128) slots stays inside the window's 2^(c-1) slots;
-* the bucket reduction by planes (k_reduce.hip: make_planes, k_seg_sums, plane_segment):
+* the bucket reduction by planes (msm_api.hip: make_planes; k_reduce.hip: k_seg_sums,
+  plane_segment):
   segment running sums plus bit planes of the segment weights, each plane doubled by its
   exponent, must add up to sum_j 2^(c j) sum_b (floor(b / f_j) + 1) B_{j,b} for every c;
 * the runs of doublings with lookahead (quad.hpp, quad_dbl_n): the (X, U = 2Y, M = 3X^2, z)
@@ -60,7 +61,7 @@ def _seg_log2(c):
 
 
 def _planes(c, nwin):
-    """make_planes (k_reduce.hip): (exponent, window, selector) of every plane, in order
+    """make_planes (msm_api.hip): (exponent, window, selector) of every plane, in order
     of decreasing exponent, plus the segment count and log2 segment length."""
     lam = _seg_log2(c)
     slots = 1 << (c - 1)
