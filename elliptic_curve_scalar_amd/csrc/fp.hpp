@@ -209,9 +209,67 @@ __device__ __forceinline__ fp fp_mul_cios(const fp& a, const fp& b) {
   return fp_reduce_once(r);
 }
 
+// Montgomery square a^2 * 2^-256 mod p by separated operand scanning: the 28 products
+// a_i a_j (i < j) once, the 512-bit sum doubled by a one-bit shift, the 8 squares a_i^2
+// added, then the word-serial Montgomery reduction (8 rounds of t += m p 2^(32 i),
+// m = t_i (-p^-1) mod 2^32): 108 multiply-adds against 136 for the product.
+__device__ __forceinline__ fp fp_sqr_sos(const fp& a) {
+  uint32_t t[16];
+#pragma unroll
+  for (int k = 0; k < 16; k++) t[k] = 0;
+  // off-diagonal products: row i adds a_i a_j (j > i) at t[i + j]
+#pragma unroll
+  for (int i = 0; i < 7; i++) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = i + 1; j < 8; j++) {
+      const uint64_t s = (uint64_t)a.v[i] * a.v[j] + fp_add33(t[i + j], c);
+      t[i + j] = (uint32_t)s;
+      c = (uint32_t)(s >> 32);
+    }
+    t[i + 8] = c;
+  }
+  // double (the top bit of t[14] moves into t[15], which is still 0)
+#pragma unroll
+  for (int k = 15; k > 0; k--) t[k] = __builtin_amdgcn_alignbit(t[k], t[k - 1], 31);
+  t[0] = 0;
+  // the squares a_i^2 at t[2i], t[2i + 1]
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const uint64_t s = (uint64_t)a.v[i] * a.v[i] + fp_add33(t[2 * i], c);
+    t[2 * i] = (uint32_t)s;
+    const uint64_t u = (uint64_t)t[2 * i + 1] + (uint32_t)(s >> 32);
+    t[2 * i + 1] = (uint32_t)u;
+    c = (uint32_t)(u >> 32);
+  }
+  // reduction: after round i, t[0..i] are 0 and the value is unchanged mod p; the carry
+  // out of t[i + 8] is deferred to round i + 1, whose last add lands on t[i + 9]
+  uint32_t cc = 0;
+#pragma unroll
+  for (int i = 0; i < 8; i++) {
+    const uint32_t m = t[i] * MSM_PINV;
+    uint32_t c2 = 0;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const uint64_t s = (uint64_t)m * p_limb(j) + fp_add33(t[i + j], c2);
+      t[i + j] = (uint32_t)s;
+      c2 = (uint32_t)(s >> 32);
+    }
+    const uint64_t u = (uint64_t)t[i + 8] + c2 + cc;
+    t[i + 8] = (uint32_t)u;
+    cc = (uint32_t)(u >> 32);
+  }
+  // (a^2 + M p) / 2^256 < (p^2 + 2^256 p) / 2^256 < 2p < 2^255: no carry is left in cc
+  fp r;
+#pragma unroll
+  for (int j = 0; j < 8; j++) r.v[j] = t[8 + j];
+  return fp_reduce_once(r);
+}
+
 // Montgomery product a * b * 2^-256 mod p; inputs and output fully reduced.
 __device__ __forceinline__ fp fp_mul(const fp& a, const fp& b) { return fp_mul_cios(a, b); }
-__device__ __forceinline__ fp fp_sqr(const fp& a) { return fp_mul_cios(a, a); }
+__device__ __forceinline__ fp fp_sqr(const fp& a) { return fp_sqr_sos(a); }
 
 // Small constant c (< 2^32) in Montgomery form.
 __device__ __forceinline__ fp fp_from_u32(uint32_t c) {
