@@ -20,9 +20,16 @@
 // longest chain is one plane's doublings instead of a running sum per window followed
 // by c (W - 1) doublings of the top window.
 //
+// The planes of segment totals share their sub-sums: with s = hi 2^lb + lo, the sums
+// A_hi = sum_lo T_s and B_lo = sum_hi T_s are formed once per window, and the plane of
+// bit beta is the sum of the B_lo whose lo has bit beta (beta < lb), or of the A_hi whose
+// hi has bit beta - lb: about 2 nseg additions per window for all such planes, against
+// nseg / 2 for each.
+//
 //   k_seg_sums     one quad per (window, segment): T_s and P_s = R_s + T_s
-//   k_plane_sums   one block per 256 elements of a plane: their sum (LDS tree)
-//   k_plane_chain  one wavefront per plane: the plane's partial sums (butterfly),
+//   k_plane_sums   one wavefront per group: the A_hi and B_lo of every window, and the
+//                  (R + T) planes in groups of 64 segments (butterfly over the quads)
+//   k_plane_chain  one wavefront per plane: the plane's terms (butterfly),
 //                  2^e S by a run of doublings in row form (rowchain.hpp: each of a
 //                  round's four products spread over 16 lanes); the last wavefront of each group of 16
 //                  planes adds the group, the last group adds the groups and converts
@@ -35,14 +42,6 @@
 #include "rowchain.hpp"
 
 namespace msmk {
-
-// Element i of a plane: its segment index. sel 0 (the (R + T) plane) takes every
-// segment; sel = beta + 1 takes the segments with bit beta set, in increasing order.
-__device__ __forceinline__ uint32_t plane_segment(uint32_t sel, uint32_t i) {
-  if (sel == 0) return i;
-  const uint32_t beta = sel - 1;
-  return ((i >> beta) << (beta + 1)) | (1u << beta) | (i & ((1u << beta) - 1u));
-}
 
 // Coherent 128-byte load of a point another block has just written (after the fence
 // that followed its counter's atomic): device-scope atomic loads bypass this CU's cache.
@@ -107,52 +106,54 @@ __global__ void __launch_bounds__(256) k_seg_sums(const xyzz_st* __restrict__ bs
   }
 }
 
-// The 64 quads of a block add their points through an LDS tree; thread 0 stores the sum.
-__device__ __forceinline__ void block_quad_sum(xyzz acc, xyzz_st* lds, xyzz_st* out) {
-  const uint32_t quad = threadIdx.x >> 2;
-  const int q = (int)(threadIdx.x & 3u);
-  if (q == 0) xyzz_store(&lds[quad], acc);
-  __syncthreads();
-  for (uint32_t stride = 32; stride > 0; stride >>= 1) {
-    if (quad < stride) {
-      acc = quad_add(acc, xyzz_load(&lds[quad + stride]), q);
-      if (q == 0) xyzz_store(&lds[quad], acc);
-    }
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) xyzz_store(out, acc);
+// Spread t over the bits other than beta and set bit beta: the t-th index with bit beta set.
+__device__ __forceinline__ uint32_t with_bit(uint32_t t, uint32_t beta) {
+  return ((t >> beta) << (beta + 1)) | (1u << beta) | (t & ((1u << beta) - 1u));
 }
 
-// Elements of a plane (its blocks of partial sums hold PLANE_PER_BLOCK elements each).
-
-__device__ __forceinline__ uint32_t plane_count(const plane_table& pt, uint32_t sel) {
-  return sel ? pt.nseg >> 1 : pt.nseg;
-}
-
-// Block (p, k) of plane p adds the plane's elements [256 k, 256 k + 256): four per quad,
-// then the block's LDS tree; the sum goes to part[p nb + k]. A plane of segment totals has
-// half as many elements as one of R + T values, so its upper blocks have nothing to do
-// and leave at once (before any barrier, all threads together).
+// Group r of window j (r < pt.wstride), at part[j wstride + r]:
+//   r < np:            P_s for the segments s in [r 2^pg, (r + 1) 2^pg) (fewer in the last)
+//   r - np = hi < nA:  A_hi = sum of T_s, s = hi 2^lb + lo over lo  (2^lb terms)
+//   else lo:           B_lo = sum of T_s, s = hi 2^lb + lo over hi  (2^hb terms)
+// One wavefront per group (at most 64 terms), four groups per block: the 16 quads share
+// the terms evenly (quad q adds its run of ceil(terms / 16)), then a butterfly over the
+// quads (no barriers; whole wavefronts leave together).
 __global__ void __launch_bounds__(256) k_plane_sums(const xyzz_st* __restrict__ tseg,
                                                     const xyzz_st* __restrict__ pseg,
-                                                    plane_table pt, xyzz_st* __restrict__ part) {
-  __shared__ xyzz_st lds[64];
-  const uint32_t p = blockIdx.x / pt.nb, k = blockIdx.x % pt.nb;
-  const uint32_t ent = pt.e[p];
-  const uint32_t j = (ent >> 8) & 0xffu, sel = ent >> 16;
-  const uint32_t cnt = plane_count(pt, sel);
-  if (k * PLANE_PER_BLOCK >= cnt) return;
-  const xyzz_st* src = (sel ? tseg : pseg) + (size_t)j * pt.nseg;
-  const uint32_t quad = threadIdx.x >> 2;
+                                                    plane_table pt, uint32_t nwin,
+                                                    xyzz_st* __restrict__ part) {
+  const uint32_t g = blockIdx.x * 4u + (threadIdx.x >> 6);
+  if (g >= nwin * pt.wstride) return;
+  const uint32_t j = g / pt.wstride, r = g % pt.wstride;
+  const uint32_t quad = (threadIdx.x & 63u) >> 2;
   const int q = (int)(threadIdx.x & 3u);
-  const uint32_t i0 = k * PLANE_PER_BLOCK + PLANE_PER_QUAD * quad;
+  const uint32_t nA = 1u << pt.hb;
+  uint32_t cnt, base, stride;
+  const xyzz_st* src = tseg + (size_t)j * pt.nseg;
+  if (r < pt.np) {
+    src = pseg + (size_t)j * pt.nseg;
+    base = r << pt.pg;
+    cnt = min(1u << pt.pg, pt.nseg - base);
+    stride = 1;
+  } else if (r - pt.np < nA) {
+    base = (r - pt.np) << pt.lb;
+    cnt = 1u << pt.lb;
+    stride = 1;
+  } else {
+    base = r - pt.np - nA;
+    cnt = nA;
+    stride = 1u << pt.lb;
+  }
+  const uint32_t per = (cnt + 15u) / 16u;
   xyzz acc = xyzz_inf();
-  for (uint32_t i = i0; i < i0 + PLANE_PER_QUAD && i < cnt; i++)
-    acc = quad_add(acc, xyzz_load(src + plane_segment(sel, i)), q);
-  block_quad_sum(acc, lds, part + blockIdx.x);
+  for (uint32_t i = per * quad; i < per * quad + per && i < cnt; i++)
+    acc = quad_add(acc, xyzz_load(src + base + i * stride), q);
+  acc = wave_quad_sum(acc, min(16u, (cnt + per - 1u) / per), q);
+  if ((threadIdx.x & 63u) == 0) xyzz_store(part + (size_t)j * pt.wstride + r, acc);
 }
 
-// One wavefront per plane p: S = sum of the plane's nb partials, then 2^e S (e = the
+// One wavefront per plane p: S = the sum of the plane's terms among its window's group
+// sums (the np (R + T) group sums, or the A_hi or B_lo of its bit), then 2^e S (e = the
 // plane's exponent) by a run of doublings in row form. Planes are in order of decreasing
 // e, so the long runs start first. The last wavefront to finish in each group of 16
 // planes (counted by join[group]) adds the group's results; the last group to finish
@@ -163,12 +164,29 @@ __global__ void __launch_bounds__(64) k_plane_chain(const xyzz_st* __restrict__ 
                                                     uint32_t* join, g1a* out) {
   const uint32_t p = blockIdx.x, quad = threadIdx.x >> 2;
   const int q = (int)(threadIdx.x & 3u);
-  const uint32_t e = pt.e[p] & 0xffu;
-  const uint32_t nblk = (plane_count(pt, pt.e[p] >> 16) + PLANE_PER_BLOCK - 1) / PLANE_PER_BLOCK;
+  const uint32_t e = pt.e[p] & 0xffu, j = (pt.e[p] >> 8) & 0xffu, sel = pt.e[p] >> 16;
+  // the plane's terms: term t is part[first + term_index(t)]
+  const xyzz_st* grp_sums = part + (size_t)j * pt.wstride;
+  uint32_t nterm, first, beta = 0;
+  if (sel == 0) {
+    nterm = pt.np;
+    first = 0;
+  } else if (sel - 1 < pt.lb) {  // B_lo with bit beta of lo
+    beta = sel - 1;
+    nterm = 1u << (pt.lb - 1);
+    first = pt.np + (1u << pt.hb);
+  } else {  // A_hi with bit beta - lb of hi
+    beta = sel - 1 - pt.lb;
+    nterm = 1u << (pt.hb - 1);
+    first = pt.np;
+  }
   const row_consts k = row_consts_load();
   xyzz acc = xyzz_inf();
-  for (uint32_t i = quad; i < nblk; i += 16) acc = quad_add(acc, xyzz_load(part + (size_t)p * pt.nb + i), q);
-  acc = wave_quad_sum(acc, min(nblk, 16u), q);
+  for (uint32_t t = quad; t < nterm; t += 16) {
+    const uint32_t idx = sel ? with_bit(t, beta) : t;
+    acc = quad_add(acc, xyzz_load(grp_sums + first + idx), q);
+  }
+  acc = wave_quad_sum(acc, min(nterm, 16u), q);
   // the run of doublings in row form needs the plane's sum (quad 0's) on every lane
   acc = xyzz_from_lane0(acc);
   acc = row_dbl_n(acc, e, k, q);
@@ -200,7 +218,8 @@ hipError_t launch_reduce(const xyzz_st* bsum, uint32_t c, uint32_t nwin, const p
                          xyzz_st* tseg, xyzz_st* pseg, xyzz_st* part, hipStream_t s) {
   const size_t quads = (size_t)nwin * pt.nseg;
   k_seg_sums<<<grid_for(quads * 4, 256), 256, 0, s>>>(bsum, c, nwin, pt.lambda, pt.nseg, tseg, pseg);
-  k_plane_sums<<<pt.n * pt.nb, 256, 0, s>>>(tseg, pseg, pt, part);
+  const uint32_t groups = nwin * pt.wstride;
+  k_plane_sums<<<(groups + 3u) / 4u, 256, 0, s>>>(tseg, pseg, pt, nwin, part);
   return hipGetLastError();
 }
 

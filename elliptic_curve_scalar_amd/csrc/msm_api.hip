@@ -16,7 +16,7 @@ namespace msmk {
 
 // Plane table of the bucket reduction (k_reduce.hip states the decomposition).
 // log2 of the segment length: segments of 4 slots up to c = 14, 8 at c = 15 and 16, so a
-// window has at most 4096 segments and a plane at most 16 blocks of partial sums.
+// window has at most 4096 segments (group sums of at most 64 terms).
 static uint32_t seg_log2(uint32_t c) { return c >= 15 ? 3u : 2u; }
 
 plane_table make_planes(uint32_t c, uint32_t nwin) {
@@ -29,7 +29,11 @@ plane_table make_planes(uint32_t c, uint32_t nwin) {
   while ((1u << lgseg) < nseg) lgseg++;
   pt.nseg = nseg;
   pt.lambda = lambda;
-  pt.nb = (nseg + PLANE_PER_BLOCK - 1) / PLANE_PER_BLOCK;
+  pt.hb = lgseg / 2;
+  pt.lb = lgseg - pt.hb;
+  pt.pg = nseg >= 2048 ? 6u : 5u;  // groups of at most 64 terms, at most 64 groups per plane
+  pt.np = (nseg + (1u << pt.pg) - 1) >> pt.pg;
+  pt.wstride = pt.np + (1u << pt.hb) + (1u << pt.lb);
   // (exponent, window, selector) of every plane
   uint32_t tmp[MAX_PLANES];
   uint32_t n = 0;
@@ -142,7 +146,7 @@ Layout plan(size_t n, int c, int S) {
   L.bsum = take((size_t)L.K * sizeof(xyzz_st));
   L.tseg = take((size_t)L.nwin * L.planes.nseg * sizeof(xyzz_st));
   L.pseg = take((size_t)L.nwin * L.planes.nseg * sizeof(xyzz_st));
-  L.part = take((size_t)L.planes.n * L.planes.nb * sizeof(xyzz_st));
+  L.part = take((size_t)L.nwin * L.planes.wstride * sizeof(xyzz_st));
   L.res = take((size_t)L.planes.n * sizeof(xyzz_st));
   L.gres = take((size_t)MAX_PLANE_GROUPS * sizeof(xyzz_st));
   L.total = off;

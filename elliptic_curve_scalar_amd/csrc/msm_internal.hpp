@@ -33,10 +33,13 @@ struct msm_stats {
 // window (e[i] >> 8) & 0xff and selector e[i] >> 16 (0: every segment's R + T; beta + 1:
 // the segment totals T of segments with bit beta set). Passed to kernels by value.
 struct plane_table {
-  uint32_t n;       // planes, in order of decreasing exponent
-  uint32_t nseg;    // segments per window
-  uint32_t lambda;  // log2 of the slots per segment
-  uint32_t nb;      // blocks of partial sums per plane: ceil(nseg / 256)
+  uint32_t n;        // planes, in order of decreasing exponent
+  uint32_t nseg;     // segments per window (2^(hb + lb))
+  uint32_t lambda;   // log2 of the slots per segment
+  uint32_t hb, lb;   // segment index s = hi 2^lb + lo, hi < 2^hb, lo < 2^lb (lb >= hb)
+  uint32_t pg;       // log2 of the segments per (R + T) group: 5, or 6 for 2048 or more
+  uint32_t np;       // (R + T) group sums per window: ceil(nseg / 2^pg)
+  uint32_t wstride;  // group sums per window: np, then 2^hb sums A_hi, then 2^lb sums B_lo
   uint32_t e[MAX_PLANES];
 };
 
@@ -127,11 +130,9 @@ hipError_t launch_walk_merge(int S, const walk_args& a, uint32_t merge_passes, h
 
 // Planes of the reduction for window width c and nwin windows (host side of the plan).
 plane_table make_planes(uint32_t c, uint32_t nwin);
-// Plane elements per quad and per block of partial sums (k_plane_sums).
-constexpr uint32_t PLANE_PER_QUAD = 4;
-constexpr uint32_t PLANE_PER_BLOCK = 64 * PLANE_PER_QUAD;
-// Segment sums (tseg, pseg: nwin nseg points each) and per-plane partial sums (part:
-// n nb points).
+
+// Segment sums (tseg, pseg: nwin nseg points each) and the group sums the planes are
+// made of (part: nwin wstride points).
 hipError_t launch_reduce(const xyzz_st* bsum, uint32_t c, uint32_t nwin, const plane_table& pt,
                          xyzz_st* tseg, xyzz_st* pseg, xyzz_st* part, hipStream_t s);
 // Doubling runs of every plane and their sum, in affine form, to out (res: n points,

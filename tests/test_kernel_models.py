@@ -5,9 +5,10 @@ each checked against the plain definition it replaces:
   half-scalar magnitudes the top window's digit never exceeds 2^(127 - c (W - 1)), so
   spreading each digit over 2^(c W - 128) slots stays inside the window's 2^(c-1) slots;
 * the bucket reduction by planes (msm_api.hip: make_planes; k_reduce.hip: k_seg_sums,
-  plane_segment):
+  k_plane_sums, with_bit):
   segment running sums plus bit planes of the segment weights, each plane doubled by its
-  exponent, must add up to sum_j 2^(c j) sum_b (floor(b / f_j) + 1) B_{j,b} for every c;
+  exponent and formed from shared group sums (A_hi, B_lo), must add up to
+  sum_j 2^(c j) sum_b (floor(b / f_j) + 1) B_{j,b} for every c;
 * the runs of doublings with lookahead (quad.hpp, quad_dbl_n): the (X, U = 2Y, M = 3X^2, z)
   recurrence against repeated XYZZ doubling (dbl-2008-s-1) on curve points, odd and even
   run lengths, and the point at infinity;
@@ -79,11 +80,9 @@ def _planes(c, nwin):
     return out, nseg, lam
 
 
-def _plane_segment(sel, i):
-    if sel == 0:
-        return i
-    beta = sel - 1
-    return ((i >> beta) << (beta + 1)) | (1 << beta) | (i & ((1 << beta) - 1))
+def _with_bit(t, beta):
+    """with_bit (k_reduce.hip): the t-th index whose bit beta is set."""
+    return ((t >> beta) << (beta + 1)) | (1 << beta) | (t & ((1 << beta) - 1))
 
 
 def _seg_sums(B, lo, hi, f):
@@ -105,13 +104,35 @@ def _reduce_by_planes(buckets, c, nwin, mistake=None):
         for s in range(nseg):
             lo, hi = s << lam, min(slots, (s + 1) << lam)
             T[j, s], Pv[j, s] = _seg_sums(buckets[j], lo, hi, f)
+    # k_plane_sums: per window the (R + T) group sums of 2^pg segments, A_hi = sum over lo of
+    # T_s and B_lo = sum over hi of T_s, s = hi 2^lb + lo
+    lgseg = (nseg - 1).bit_length()
+    hb = lgseg // 2
+    lb = lgseg - hb
+    pg = 6 if nseg >= 2048 else 5
+    np_ = (nseg + (1 << pg) - 1) >> pg
+    assert max(np_, 1 << (lb - 1) if lb else 1, 1 << (hb - 1) if hb else 1) <= 64  # chain terms
+    assert max(1 << pg, 1 << lb, 1 << hb) <= 64  # group sizes of k_plane_sums
+    G = {}
+    for j in range(nwin):
+        for r in range(np_):
+            G[j, r] = sum(Pv[j, s] for s in range((r << pg), min((r + 1) << pg, nseg)))
+        for hi in range(1 << hb):
+            G[j, np_ + hi] = sum(T[j, (hi << lb) + lo] for lo in range(1 << lb))
+        for lo in range(1 << lb):
+            G[j, np_ + (1 << hb) + lo] = sum(T[j, (hi << lb) + lo] for hi in range(1 << hb))
+    # k_plane_chain: each plane's terms among its window's group sums
     total = 0
     for e, j, sel in planes:
-        cnt = nseg >> 1 if sel else nseg
-        segs = [_plane_segment(sel, i) for i in range(cnt)]
-        if mistake == "selector":
-            segs = [_plane_segment(sel + 1 if sel else 0, i) % nseg for i in range(cnt)]
-        v = sum((T if sel else Pv)[j, s] for s in segs)
+        if sel == 0:
+            terms = list(range(np_))
+        elif sel - 1 < lb:
+            beta = sel - 1 + (1 if mistake == "selector" else 0)
+            terms = [np_ + (1 << hb) + _with_bit(t, beta) % (1 << lb) for t in range(1 << (lb - 1))]
+        else:
+            beta = sel - 1 - lb
+            terms = [np_ + _with_bit(t, beta) for t in range(1 << (hb - 1))]
+        v = sum(G[j, r] for r in terms)
         total += v << (e + (1 if mistake == "exponent" and sel == 1 else 0))
     return total, planes
 
