@@ -31,9 +31,9 @@
 //                  (R + T) planes in groups of 64 segments (butterfly over the quads)
 //   k_plane_chain  one wavefront per plane: the plane's terms (butterfly),
 //                  2^e S by a run of doublings in row form (rowchain.hpp: each of a
-//                  round's four products spread over 16 lanes); the last wavefront of each group of 16
-//                  planes adds the group, the last group adds the groups and converts
-//                  the result to affine
+//                  round's four products spread over 16 lanes); the last wavefront of each
+//                  join group of planes adds the group, the last group adds the groups and
+//                  converts the result to affine
 #include <hip/hip_runtime.h>
 #include <string.h>
 
@@ -106,6 +106,9 @@ __global__ void __launch_bounds__(256) k_seg_sums(const xyzz_st* __restrict__ bs
   }
 }
 
+// Join group of plane p: 0 for p < 2, else floor(log2 p) (group k >= 1 is [2^k, 2^(k+1))).
+__device__ __forceinline__ uint32_t plane_group(uint32_t p) { return p < 2u ? 0u : 31u - __clz(p); }
+
 // Spread t over the bits other than beta and set bit beta: the t-th index with bit beta set.
 __device__ __forceinline__ uint32_t with_bit(uint32_t t, uint32_t beta) {
   return ((t >> beta) << (beta + 1)) | (1u << beta) | (t & ((1u << beta) - 1u));
@@ -155,8 +158,8 @@ __global__ void __launch_bounds__(256) k_plane_sums(const xyzz_st* __restrict__ 
 // One wavefront per plane p: S = the sum of the plane's terms among its window's group
 // sums (the np (R + T) group sums, or the A_hi or B_lo of its bit), then 2^e S (e = the
 // plane's exponent) by a run of doublings in row form. Planes are in order of decreasing
-// e, so the long runs start first. The last wavefront to finish in each group of 16
-// planes (counted by join[group]) adds the group's results; the last group to finish
+// e, so the long runs start first. The last wavefront to finish in each join group
+// (counted by join[group]) adds the group's results; the last group to finish
 // (join[MAX_PLANE_GROUPS]) adds the group sums and writes the affine result. The counters
 // start at zero (cleared with the plan statistics before the MSM).
 __global__ void __launch_bounds__(64) k_plane_chain(const xyzz_st* __restrict__ part,
@@ -192,15 +195,20 @@ __global__ void __launch_bounds__(64) k_plane_chain(const xyzz_st* __restrict__ 
   acc = row_dbl_n(acc, e, k, q);
   if (threadIdx.x == 0) xyzz_store(res + p, acc);
   __threadfence();
-  const uint32_t grp = p >> 4, ngroups = (pt.n + 15u) >> 4;
-  const uint32_t gsize = min(16u, pt.n - 16u * grp);
+  // join groups by finishing order: planes [0, 2), [2, 4), [4, 8), [8, 16), ... (group k >= 1
+  // holds planes [2^k, 2^(k+1))). The long runs end last and sit in the small groups, so the
+  // last plane to finish adds at most one other point before the groups' sum.
+  const uint32_t grp = plane_group(p), ngroups = plane_group(pt.n - 1u) + 1u;
+  const uint32_t g0 = grp ? (1u << grp) : 0u;
+  const uint32_t gsize = min(grp ? (1u << grp) : 2u, pt.n - g0);
   uint32_t old = 0;
   if (threadIdx.x == 0) old = atomicAdd(&join[grp], 1u);
   old = (uint32_t)__shfl((int)old, 0, 64);
   if (old + 1u != gsize) return;
   __threadfence();
-  acc = (quad < gsize) ? xyzz_load_coherent(res + 16u * grp + quad) : xyzz_inf();
-  acc = wave_quad_sum(acc, gsize, q);
+  acc = xyzz_inf();
+  for (uint32_t i = quad; i < gsize; i += 16) acc = quad_add(acc, xyzz_load_coherent(res + g0 + i), q);
+  acc = wave_quad_sum(acc, min(gsize, 16u), q);
   if (threadIdx.x == 0) xyzz_store(gres + grp, acc);
   __threadfence();
   if (threadIdx.x == 0) old = atomicAdd(&join[MAX_PLANE_GROUPS], 1u);

@@ -16,7 +16,7 @@ constexpr int MAX_LEVELS = 32;                       // pair-tree levels tracked
 constexpr uint32_t XYZZ_QUAD_MAX_PAIRS = 65536;      // XYZZ levels this small use 4 lanes per add
 
 constexpr int MAX_PLANES = 160;                      // reduction planes (at most 128 occur)
-constexpr int MAX_PLANE_GROUPS = (MAX_PLANES + 15) / 16;
+constexpr int MAX_PLANE_GROUPS = 10;                 // join groups (8 occur: 2, 2, 4, ..., 32 planes)
 
 // Plan read back to the host after the sort (one small copy).
 struct msm_stats {
