@@ -5,7 +5,7 @@
 #include "batch_add.hpp"
 #include "glv.hpp"
 #include "kern_util.hpp"
-#include "rowchain.hpp"
+#include "rowpoint.hpp"
 
 namespace msmk {
 
@@ -106,7 +106,7 @@ __global__ void __launch_bounds__(64) k_test_row(int op, const uint32_t* __restr
   const uint32_t l = threadIdx.x & 15u, e = 4u * blockIdx.x + (threadIdx.x >> 4);
   const bool live = e < n && l < 8u;
   const uint32_t x = live ? a[8 * (size_t)e + l] : 0u, y = live ? b[8 * (size_t)e + l] : 0u;
-  const row_consts k = row_consts_load();
+  row_consts k = row_consts_load();
   uint32_t r;
   if (op == 0) r = row_mul(x, y, k);
   else if (op == 1) r = row_add(x, y, k);
@@ -114,21 +114,35 @@ __global__ void __launch_bounds__(64) k_test_row(int op, const uint32_t* __restr
   if (live) out[8 * (size_t)e + l] = r;
 }
 
-// 2^d P for n XYZZ points (32 words each: X, Y, ZZ, ZZZ), one wavefront per point: op 3 by
-// runs in row form, op 4 by the quad runs. Every lane computes; lane 0 stores.
-__global__ void __launch_bounds__(64) k_test_row_dbl(int op, const uint32_t* __restrict__ pts,
-                                                     uint32_t d, uint32_t* __restrict__ out) {
+// XYZZ points (32 words each: X, Y, ZZ, ZZZ), one wavefront per point:
+//   op 3  2^d P by a run of doublings in row form (rowpoint.hpp)
+//   op 4  2^d P by the quad runs (quad.hpp)
+//   op 7  P + Q in row form (every special case)
+//   op 8  2P in row form
+//   op 9  P in affine coordinates (16 words) by the uniform path of the window combine's
+//         end (the inverse on scalar registers)
+__global__ void __launch_bounds__(64) k_test_row_pts(int op, const uint32_t* __restrict__ pts,
+                                                     const uint32_t* __restrict__ pts2, uint32_t d,
+                                                     uint32_t* __restrict__ out) {
   const xyzz_st* src = reinterpret_cast<const xyzz_st*>(pts) + blockIdx.x;
-  const xyzz p = xyzz_load(src);
-  const int q = (int)(threadIdx.x & 3u);
-  xyzz r;
-  if (op == 3) {
-    const row_consts k = row_consts_load();
-    r = row_dbl_n(p, d, k, q);
-  } else {
-    r = quad_dbl_n(p, d, q);
+  xyzz_st* dst = reinterpret_cast<xyzz_st*>(out) + blockIdx.x;
+  if (op == 4) {
+    const xyzz r = quad_dbl_n(xyzz_load(src), d, (int)(threadIdx.x & 3u));
+    if (threadIdx.x == 0) xyzz_store(dst, r);
+    return;
   }
-  if (threadIdx.x == 0) xyzz_store(reinterpret_cast<xyzz_st*>(out) + blockIdx.x, r);
+  row_consts k = row_consts_load();
+  const rxyzz a = rxyzz_load(src);
+  if (op == 9) {
+    const aff r = xyzz_to_aff(rxyzz_to_uniform(a, k));
+    if (threadIdx.x == 0) aff_store(reinterpret_cast<g1a*>(out) + blockIdx.x, r);
+    return;
+  }
+  rxyzz r;
+  if (op == 3) r = rxyzz_dbl_n(a, d, k);
+  else if (op == 7) r = rxyzz_add(a, rxyzz_load(reinterpret_cast<const xyzz_st*>(pts2) + blockIdx.x), k);
+  else r = rxyzz_dbl(a, k);
+  rxyzz_store(dst, r, k);
 }
 
 // Latency probe, one wavefront: x <- x b, d times, for the four elements of a and b (8 words
@@ -141,7 +155,7 @@ __global__ void __launch_bounds__(64) k_test_row_chain(int op, const uint32_t* _
     const uint32_t l = threadIdx.x & 15u, e = threadIdx.x >> 4;
     uint32_t x = l < 8u ? a[8 * e + l] : 0u;
     const uint32_t y = l < 8u ? b[8 * e + l] : 0u;
-    const row_consts k = row_consts_load();
+    row_consts k = row_consts_load();
     for (uint32_t i = 0; i < d; i++) x = row_mul(x, y, k);
     if (l < 8u) out[8 * e + l] = x;
   } else {
@@ -241,11 +255,11 @@ hipError_t launch_test_row(int op, const uint32_t* a, const uint32_t* b, uint32_
   if (op <= 2) {
     if (n == 0) return hipSuccess;
     k_test_row<<<(n + 3) / 4, 64, 0, s>>>(op, a, b, out, n);
-  } else if (op <= 4) {
-    if (n == 0) return hipSuccess;
-    k_test_row_dbl<<<n, 64, 0, s>>>(op, a, d, out);
-  } else {
+  } else if (op == 5 || op == 6) {
     k_test_row_chain<<<1, 64, 0, s>>>(op, a, b, d, out);
+  } else {
+    if (n == 0) return hipSuccess;
+    k_test_row_pts<<<n, 64, 0, s>>>(op, a, b, d, out);
   }
   return hipGetLastError();
 }

@@ -29,46 +29,19 @@
 //   k_seg_sums     one quad per (window, segment): T_s and P_s = R_s + T_s
 //   k_plane_sums   one wavefront per group: the A_hi and B_lo of every window, and the
 //                  (R + T) planes in groups of 64 segments (butterfly over the quads)
-//   k_plane_chain  one wavefront per plane: the plane's terms (butterfly),
-//                  2^e S by a run of doublings in row form (rowchain.hpp: each of a
-//                  round's four products spread over 16 lanes); the last wavefront of each
-//                  join group of planes adds the group, the last group adds the groups and
-//                  converts the result to affine
+//   k_plane_chain  one block of eight wavefronts per plane, in row form (rowpoint.hpp: each
+//                  of a round's four products spread over the 16 lanes of a row): the
+//                  plane's terms, then 2^e S by a run of doublings on one wavefront; the
+//                  last block of each join group of planes adds the group, the last group
+//                  adds the groups and converts the result to affine
 #include <hip/hip_runtime.h>
 #include <string.h>
 
 #include "glv.hpp"
 #include "kern_util.hpp"
-#include "rowchain.hpp"
+#include "rowpoint.hpp"
 
 namespace msmk {
-
-// Coherent 128-byte load of a point another block has just written (after the fence
-// that followed its counter's atomic): device-scope atomic loads bypass this CU's cache.
-__device__ __forceinline__ xyzz xyzz_load_coherent(const xyzz_st* p) {
-  xyzz a;
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    a.X.v[i] = __hip_atomic_load(&p->w[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    a.Y.v[i] = __hip_atomic_load(&p->w[8 + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    a.ZZ.v[i] = __hip_atomic_load(&p->w[16 + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    a.ZZZ.v[i] = __hip_atomic_load(&p->w[24 + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  return a;
-}
-
-// Lane 0's point on every lane of the wavefront.
-__device__ __forceinline__ xyzz xyzz_from_lane0(const xyzz& a) {
-  xyzz r;
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    r.X.v[i] = __builtin_amdgcn_readfirstlane(a.X.v[i]);
-    r.Y.v[i] = __builtin_amdgcn_readfirstlane(a.Y.v[i]);
-    r.ZZ.v[i] = __builtin_amdgcn_readfirstlane(a.ZZ.v[i]);
-    r.ZZZ.v[i] = __builtin_amdgcn_readfirstlane(a.ZZZ.v[i]);
-  }
-  return r;
-}
 
 // Sum over the first `used` quads of a wavefront (1 <= used <= 16; the others hold the
 // point at infinity): a ds_bpermute butterfly over the smallest power-of-two group of quads
@@ -155,18 +128,43 @@ __global__ void __launch_bounds__(256) k_plane_sums(const xyzz_st* __restrict__ 
   if ((threadIdx.x & 63u) == 0) xyzz_store(part + (size_t)j * pt.wstride + r, acc);
 }
 
-// One wavefront per plane p: S = the sum of the plane's terms among its window's group
-// sums (the np (R + T) group sums, or the A_hi or B_lo of its bit), then 2^e S (e = the
-// plane's exponent) by a run of doublings in row form. Planes are in order of decreasing
-// e, so the long runs start first. The last wavefront to finish in each join group
-// (counted by join[group]) adds the group's results; the last group to finish
-// (join[MAX_PLANE_GROUPS]) adds the group sums and writes the affine result. The counters
-// start at zero (cleared with the plan statistics before the MSM).
-__global__ void __launch_bounds__(64) k_plane_chain(const xyzz_st* __restrict__ part,
-                                                    plane_table pt, xyzz_st* res, xyzz_st* gres,
-                                                    uint32_t* join, g1a* out) {
-  const uint32_t p = blockIdx.x, quad = threadIdx.x >> 2;
-  const int q = (int)(threadIdx.x & 3u);
+// Waves per block of k_plane_chain: at least the number of join groups (plane_group of the
+// last plane, plus one).
+constexpr uint32_t CHAIN_WAVES = 8;
+static_assert(MAX_PLANES <= (1 << CHAIN_WAVES), "join groups must fit the block's waves");
+
+// Sum of the points of the block's CHAIN_WAVES wavefronts (row form; LDS holds one point per
+// wavefront), a butterfly three additions deep: wave 0 ends with the total. Every
+// wavefront of the block calls it (barriers).
+__device__ __forceinline__ rxyzz block_row_sum(rxyzz acc, uint32_t w, uint32_t (*sh)[32],
+                                               row_consts& k) {
+#pragma unroll 1
+  for (uint32_t s = 1; s < CHAIN_WAVES; s <<= 1) {
+    if ((w & (2u * s - 1u)) == s) rxyzz_to_lds(sh[w], acc);
+    __syncthreads();
+    if ((w & (2u * s - 1u)) == 0) acc = rxyzz_add(acc, rxyzz_from_lds(sh[w + s]), k);
+  }
+  return acc;
+}
+
+// One block of CHAIN_WAVES wavefronts per plane p, in row form throughout (rowpoint.hpp):
+// S = the sum of the plane's terms among its window's group sums (the np (R + T) group
+// sums, or the A_hi or B_lo of its bit; wavefront w adds terms w, w + CHAIN_WAVES, ...,
+// then the block adds the wavefronts' sums), then 2^e S (e = the plane's exponent) by a
+// run of doublings on wavefront 0 while the others wait at the barrier. Planes are in
+// order of decreasing e, so the long runs start first. The last block to finish in each
+// join group (counted by join[group]) adds the group's results, the block's wavefronts
+// sharing them; the last group to finish (join[MAX_PLANE_GROUPS]) adds the group sums
+// (one per wavefront) and writes the affine result (its one inversion on wavefront 0).
+// The counters start at zero (cleared with the plan statistics before the MSM).
+__global__ void __launch_bounds__(64 * CHAIN_WAVES) __attribute__((amdgpu_waves_per_eu(1, 2)))
+k_plane_chain(const xyzz_st* __restrict__ part,
+                                                                 plane_table pt, xyzz_st* res,
+                                                                 xyzz_st* gres, uint32_t* join,
+                                                                 g1a* out) {
+  __shared__ uint32_t sh[CHAIN_WAVES][32];
+  __shared__ uint32_t last_in_group, last_group;
+  const uint32_t p = blockIdx.x, w = threadIdx.x >> 6;
   const uint32_t e = pt.e[p] & 0xffu, j = (pt.e[p] >> 8) & 0xffu, sel = pt.e[p] >> 16;
   // the plane's terms: term t is part[first + term_index(t)]
   const xyzz_st* grp_sums = part + (size_t)j * pt.wstride;
@@ -183,42 +181,44 @@ __global__ void __launch_bounds__(64) k_plane_chain(const xyzz_st* __restrict__ 
     nterm = 1u << (pt.hb - 1);
     first = pt.np;
   }
-  const row_consts k = row_consts_load();
-  xyzz acc = xyzz_inf();
-  for (uint32_t t = quad; t < nterm; t += 16) {
+  row_consts k = row_consts_load();
+  rxyzz acc = rxyzz_inf();
+  for (uint32_t t = w; t < nterm; t += CHAIN_WAVES) {
     const uint32_t idx = sel ? with_bit(t, beta) : t;
-    acc = quad_add(acc, xyzz_load(grp_sums + first + idx), q);
+    acc = rxyzz_add(acc, rxyzz_load(grp_sums + first + idx), k);
   }
-  acc = wave_quad_sum(acc, min(nterm, 16u), q);
-  // the run of doublings in row form needs the plane's sum (quad 0's) on every lane
-  acc = xyzz_from_lane0(acc);
-  acc = row_dbl_n(acc, e, k, q);
-  if (threadIdx.x == 0) xyzz_store(res + p, acc);
-  __threadfence();
+  acc = block_row_sum(acc, w, sh, k);
   // join groups by finishing order: planes [0, 2), [2, 4), [4, 8), [8, 16), ... (group k >= 1
-  // holds planes [2^k, 2^(k+1))). The long runs end last and sit in the small groups, so the
-  // last plane to finish adds at most one other point before the groups' sum.
+  // holds planes [2^k, 2^(k+1))). The long runs end last and sit in the small groups.
   const uint32_t grp = plane_group(p), ngroups = plane_group(pt.n - 1u) + 1u;
   const uint32_t g0 = grp ? (1u << grp) : 0u;
   const uint32_t gsize = min(grp ? (1u << grp) : 2u, pt.n - g0);
-  uint32_t old = 0;
-  if (threadIdx.x == 0) old = atomicAdd(&join[grp], 1u);
-  old = (uint32_t)__shfl((int)old, 0, 64);
-  if (old + 1u != gsize) return;
+  if (w == 0) {
+    acc = rxyzz_dbl_n(acc, e, k);
+    rxyzz_store(res + p, acc, k);
+    __threadfence();
+    if (threadIdx.x == 0) last_in_group = (atomicAdd(&join[grp], 1u) + 1u == gsize) ? 1u : 0u;
+  }
+  __syncthreads();
+  if (!last_in_group) return;  // the whole block leaves
   __threadfence();
-  acc = xyzz_inf();
-  for (uint32_t i = quad; i < gsize; i += 16) acc = quad_add(acc, xyzz_load_coherent(res + g0 + i), q);
-  acc = wave_quad_sum(acc, min(gsize, 16u), q);
-  if (threadIdx.x == 0) xyzz_store(gres + grp, acc);
+  acc = rxyzz_inf();
+  for (uint32_t i = w; i < gsize; i += CHAIN_WAVES) acc = rxyzz_add(acc, rxyzz_load_coherent(res + g0 + i), k);
+  acc = block_row_sum(acc, w, sh, k);
+  if (w == 0) {
+    rxyzz_store(gres + grp, acc, k);
+    __threadfence();
+    if (threadIdx.x == 0) last_group = (atomicAdd(&join[MAX_PLANE_GROUPS], 1u) + 1u == ngroups) ? 1u : 0u;
+  }
+  __syncthreads();
+  if (!last_group) return;
   __threadfence();
-  if (threadIdx.x == 0) old = atomicAdd(&join[MAX_PLANE_GROUPS], 1u);
-  old = (uint32_t)__shfl((int)old, 0, 64);
-  if (old + 1u != ngroups) return;
-  __threadfence();
-  acc = (quad < ngroups) ? xyzz_load_coherent(gres + quad) : xyzz_inf();
-  acc = wave_quad_sum(acc, ngroups, q);
-  const aff a = xyzz_to_aff(acc);
-  if (threadIdx.x == 0) aff_store(out, a);
+  acc = (w < ngroups) ? rxyzz_load_coherent(gres + w) : rxyzz_inf();
+  acc = block_row_sum(acc, w, sh, k);
+  if (w == 0) {
+    const aff a = xyzz_to_aff(rxyzz_to_uniform(acc, k));
+    if (threadIdx.x == 0) aff_store(out, a);
+  }
 }
 
 // ------------------------------------------------------------------ host side
@@ -233,7 +233,7 @@ hipError_t launch_reduce(const xyzz_st* bsum, uint32_t c, uint32_t nwin, const p
 
 hipError_t launch_final(const xyzz_st* part, const plane_table& pt, xyzz_st* res, xyzz_st* gres,
                         uint32_t* join, g1a* out, hipStream_t s) {
-  k_plane_chain<<<pt.n, 64, 0, s>>>(part, pt, res, gres, join, out);
+  k_plane_chain<<<pt.n, 64 * CHAIN_WAVES, 0, s>>>(part, pt, res, gres, join, out);
   return hipGetLastError();
 }
 

@@ -672,11 +672,11 @@ int msm_test_fp_inv(const uint32_t* d_a, uint32_t* d_out, size_t n, void* stream
 
 int msm_test_row(int op, const uint32_t* d_a, const uint32_t* d_b, uint32_t* d_out, size_t n,
                  uint32_t d, void* stream) {
-  if (op < 0 || op > 6) return fail(MSM_ERR_ARG, "op must be in 0..6%s");
+  if (op < 0 || op > 9) return fail(MSM_ERR_ARG, "op must be in 0..9%s");
   if (n > MSM_MAX_N) return fail(MSM_ERR_ARG, "n exceeds MSM_MAX_N%s");
-  if (op >= 5 && n != 4) return fail(MSM_ERR_ARG, "the latency probe takes n = 4%s");
-  if (op >= 3 && op <= 4 && d > 4096) return fail(MSM_ERR_ARG, "d must be at most 4096%s");
-  const bool binary = op <= 2 || op >= 5;
+  if ((op == 5 || op == 6) && n != 4) return fail(MSM_ERR_ARG, "the latency probe takes n = 4%s");
+  if ((op == 3 || op == 4) && d > 4096) return fail(MSM_ERR_ARG, "d must be at most 4096%s");
+  const bool binary = op <= 2 || op == 5 || op == 6 || op == 7;
   if (n && (!d_a || !d_out || (binary && !d_b))) return fail(MSM_ERR_ARG, "NULL pointer%s");
   if (!aligned(d_a, 4) || !aligned(d_b, 4) || !aligned(d_out, 4))
     return fail(MSM_ERR_ARG, "pointers must be 4-byte aligned%s");

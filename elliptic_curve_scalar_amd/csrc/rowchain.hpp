@@ -6,7 +6,6 @@
 // (X, U / 2, ZZ0 z^2, ZZZ0 z^3). Two doublings take five rounds (dbl-2008-s-1 with a = 0
 // written in U, with M X and M^2 started a round early; quad.hpp states the algebra).
 #pragma once
-#include "quad.hpp"
 #include "rowfp.hpp"
 
 namespace msmk {
@@ -16,7 +15,7 @@ struct rchain {
 };
 
 // One round: row r computes a_r b_r (lazy product); every row gets all four results.
-__device__ __forceinline__ row4 row_round(const row_consts& k, uint32_t a0, uint32_t a1, uint32_t a2,
+__device__ __forceinline__ row4 row_round(row_consts& k, uint32_t a0, uint32_t a1, uint32_t a2,
                                           uint32_t a3, uint32_t b0, uint32_t b1, uint32_t b2,
                                           uint32_t b3) {
   return row_gather(row_mul_lazy(row_pick(k, a0, a1, a2, a3), row_pick(k, b0, b1, b2, b3), k));
@@ -25,7 +24,7 @@ __device__ __forceinline__ row4 row_round(const row_consts& k, uint32_t a0, uint
 // Two doublings in five rounds. Values stay in the lazy form [0, 3p); the field
 // combinations between rounds are one linear combination each (rowfp.hpp):
 //   X' = M^2 - 2 X V,  U' = 6 (M X) V - 2 M M^2 - V^2,  M' = 3 X'^2.
-__device__ __forceinline__ void row_chain_dbl2(rchain& c, const row_consts& k) {
+__device__ __forceinline__ void row_chain_dbl2(rchain& c, row_consts& k) {
   // round A: V = U^2, M X, M^2, z U
   row4 r = row_round(k, c.U, c.M, c.M, c.z, c.U, c.X, c.M, c.U);
   const uint32_t V = r.r0, MX = r.r1, MM = r.r2, z1 = r.r3;
@@ -48,7 +47,7 @@ __device__ __forceinline__ void row_chain_dbl2(rchain& c, const row_consts& k) {
   c.M = row_lin_3a(r.r2, k);
 }
 
-__device__ __forceinline__ void row_chain_dbl1(rchain& c, const row_consts& k) {
+__device__ __forceinline__ void row_chain_dbl1(rchain& c, row_consts& k) {
   row4 r = row_round(k, c.U, c.M, c.M, c.z, c.U, c.X, c.M, c.U);
   const uint32_t V = r.r0, MX = r.r1, MM = r.r2;
   c.z = r.r3;
@@ -57,26 +56,6 @@ __device__ __forceinline__ void row_chain_dbl1(rchain& c, const row_consts& k) {
   c.X = row_lin_a_2b(MM, XV, k);
   c.U = row_lin_6a_2b_c(MXV, M3, VV, k);
   c.M = row_lin_3a(row_mul_lazy(c.X, c.X, k), k);  // every row computes X'^2
-}
-
-// 2^n p for a point p that every lane of the wavefront holds (per-lane form); the result
-// is again on every lane. The whole wavefront must be active.
-__device__ __forceinline__ xyzz row_dbl_n(const xyzz& p, uint32_t n, const row_consts& k, int q) {
-  if (n == 0) return p;
-  const dchain c0 = quad_chain_begin(p);
-  rchain c;
-  c.X = row_from_fp(c0.X);
-  c.U = row_from_fp(c0.U);
-  c.M = row_from_fp(c0.M);
-  c.z = row_from_fp(c0.z);
-  for (uint32_t i = 0; i < n / 2; i++) row_chain_dbl2(c, k);
-  if (n & 1u) row_chain_dbl1(c, k);
-  dchain e;
-  e.X = row_to_fp(row_canon(c.X, k));
-  e.U = row_to_fp(row_canon(c.U, k));
-  e.M = fp_zero();  // not used by quad_chain_end
-  e.z = row_to_fp(row_canon(c.z, k));
-  return quad_chain_end(e, p.ZZ, p.ZZZ, q);
 }
 
 }  // namespace msmk

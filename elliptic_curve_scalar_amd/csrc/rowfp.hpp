@@ -92,9 +92,9 @@ struct row_consts {
   uint32_t pl[8], ph[8], nl[8], nh[8];
   uint32_t plo;
   uint32_t m0, m1;  // all ones where bit 0 / bit 1 of the row index is set
-  // lanes 0..7 (0 above): words of 11 p - 2 (2^256 - 1), 16 p - 3 (2^256 - 1) and 2^256 - p,
-  // and a mask of all ones
-  uint32_t c2, c3, negp, lo8;
+  // lanes 0..7 (0 above): words of 6 p - (2^256 - 1), 11 p - 2 (2^256 - 1),
+  // 16 p - 3 (2^256 - 1) and 2^256 - p, and a mask of all ones
+  uint32_t c1, c2, c3, negp, lo8;
 };
 
 // p and n' = -p^-1 mod 2^256, each between eight zero words on either side so that word
@@ -109,8 +109,11 @@ __device__ const uint32_t kRowNp[24] = {
     0x1833da80u, 0xd8afcbd0u, 0x91888c6bu, 0xf57a22b7u,
     0, 0, 0, 0, 0, 0, 0, 0};
 
-// Offsets of the linear combinations (row_lin2, row_lin3 below) and 2^256 - p, then eight
-// zero words, so that lane l reads entry l.
+// Offsets of the linear combinations (row_lin_* below) and 2^256 - p, then eight zero
+// words, so that lane l reads entry l.
+__device__ const uint32_t kRowC1[16] = {
+    0x12edefabu, 0x68c34889u, 0x72aabf4fu, 0x8d087f68u,
+    0x09081231u, 0x51e1a247u, 0x4729c0fau, 0x2259d6b1u, 0, 0, 0, 0, 0, 0, 0, 0};
 __device__ const uint32_t kRowC2[16] = {
     0x4d5ee20fu, 0x956604fbu, 0x7ce3b411u, 0x828f943fu,
     0x908ecc05u, 0xeb72fed7u, 0xad21e1cau, 0x144f5eefu, 0, 0, 0, 0, 0, 0, 0, 0};
@@ -135,11 +138,26 @@ __device__ __forceinline__ row_consts row_consts_load() {
   k.plo = kRowP[8 + l] * (l < 8 ? 1u : 0u);
   k.m0 = ((lane >> 4) & 1u) ? 0xffffffffu : 0u;
   k.m1 = ((lane >> 5) & 1u) ? 0xffffffffu : 0u;
+  k.c1 = kRowC1[l];
   k.c2 = kRowC2[l];
   k.c3 = kRowC3[l];
   k.negp = kRowNegP[l];
   k.lo8 = l < 8 ? 0xffffffffu : 0u;
   return k;
+}
+
+// Marks the constants as redefined here (no instruction): the optimizer would otherwise
+// hoist their 64-bit widening out of the loops that use them, and a product by a widened
+// value that arrives from another block takes three multiply-adds instead of one.
+__device__ __forceinline__ void row_consts_here(row_consts& k) {
+  asm volatile("" : "+v"(k.pl[0]), "+v"(k.pl[1]), "+v"(k.pl[2]), "+v"(k.pl[3]), "+v"(k.pl[4]),
+               "+v"(k.pl[5]), "+v"(k.pl[6]), "+v"(k.pl[7]), "+v"(k.ph[0]), "+v"(k.ph[1]),
+               "+v"(k.ph[2]), "+v"(k.ph[3]), "+v"(k.ph[4]), "+v"(k.ph[5]), "+v"(k.ph[6]),
+               "+v"(k.ph[7]), "+v"(k.negp));
+  asm volatile("" : "+v"(k.nl[0]), "+v"(k.nl[1]), "+v"(k.nl[2]), "+v"(k.nl[3]), "+v"(k.nl[4]),
+               "+v"(k.nl[5]), "+v"(k.nl[6]), "+v"(k.nl[7]), "+v"(k.nh[0]), "+v"(k.nh[1]),
+               "+v"(k.nh[2]), "+v"(k.nh[3]), "+v"(k.nh[4]), "+v"(k.nh[5]), "+v"(k.nh[6]),
+               "+v"(k.nh[7]));
 }
 
 // Words w_l plus the carries that reach them: G holds the lanes with a carry out. No
@@ -155,6 +173,9 @@ __device__ __forceinline__ uint32_t row_carry16(uint32_t w, uint64_t G) {
 // c1_(l-1) and c2_(l-2) (carry g <= 2), then g_(l-1) (carry h <= 1), then the rippled
 // carries.
 __device__ __forceinline__ uint32_t row_columns(uint64_t SL, uint64_t SH) {
+  // opaque to the optimizer: otherwise it may fold SL + 2^16 SH back into the sums as one
+  // 64 x 32-bit product per term (three multiply-adds per term instead of two)
+  asm("" : "+v"(SL), "+v"(SH));
   const uint64_t x = SL + (SH << 16);
   const uint32_t c2 = (uint32_t)(SH >> 48) + (x < SL ? 1u : 0u);
   const uint32_t c0 = (uint32_t)x, c1s = row_shr<1>((uint32_t)(x >> 32)), c2s = row_shr<2>(c2);
@@ -167,7 +188,7 @@ __device__ __forceinline__ uint32_t row_columns(uint64_t SL, uint64_t SH) {
 }
 
 // s - p if s >= p, for s < 2p in lanes 0..7 (0 in lanes 8..15).
-__device__ __forceinline__ uint32_t row_sub_p_if_ge(uint32_t s, const row_consts& k) {
+__device__ __forceinline__ uint32_t row_sub_p_if_ge(uint32_t s, row_consts& k) {
   const uint32_t d = s - k.plo;
   const uint64_t G = row_lt(s, k.plo) & ROW_LO8;
   const uint64_t Pf = row_eq(d, 0u) & ROW_LO8;
@@ -180,19 +201,19 @@ __device__ __forceinline__ uint32_t row_sub_p_if_ge(uint32_t s, const row_consts
 }
 
 // a + b mod p.
-__device__ __forceinline__ uint32_t row_add(uint32_t a, uint32_t b, const row_consts& k) {
+__device__ __forceinline__ uint32_t row_add(uint32_t a, uint32_t b, row_consts& k) {
   const uint32_t s = a + b;
   // a + b < 2p < 2^255: no carry leaves lane 7, and lanes 8..15 stay 0
   return row_sub_p_if_ge(row_carry16(s, row_lt(s, b)), k);
 }
 
-__device__ __forceinline__ uint32_t row_dbl(uint32_t a, const row_consts& k) { return row_add(a, a, k); }
-__device__ __forceinline__ uint32_t row_triple(uint32_t a, const row_consts& k) {
+__device__ __forceinline__ uint32_t row_dbl(uint32_t a, row_consts& k) { return row_add(a, a, k); }
+__device__ __forceinline__ uint32_t row_triple(uint32_t a, row_consts& k) {
   return row_add(row_add(a, a, k), a, k);
 }
 
 // a - b mod p.
-__device__ __forceinline__ uint32_t row_sub(uint32_t a, uint32_t b, const row_consts& k) {
+__device__ __forceinline__ uint32_t row_sub(uint32_t a, uint32_t b, row_consts& k) {
   uint32_t d = a - b;
   const uint64_t G = row_lt(a, b) & ROW_LO8;
   const uint64_t Pf = row_eq(d, 0u) & ROW_LO8;
@@ -213,14 +234,15 @@ __device__ __forceinline__ uint32_t row_sub(uint32_t a, uint32_t b, const row_co
 // Montgomery product without the final subtraction: U / 2^256 for a, b < 3p, which is
 // below 9 p^2 / 2^256 + p < 2.71 p (p < 0.19 * 2^256), so the lazy form [0, 3p) is closed
 // under it. With a, b < p it is below 2p.
-__device__ __forceinline__ uint32_t row_mul_lazy(uint32_t a, uint32_t b, const row_consts& k);
+__device__ __forceinline__ uint32_t row_mul_lazy(uint32_t a, uint32_t b, row_consts& k);
 
 // Montgomery product a b 2^-256 mod p of two row-form elements.
-__device__ __forceinline__ uint32_t row_mul(uint32_t a, uint32_t b, const row_consts& k) {
+__device__ __forceinline__ uint32_t row_mul(uint32_t a, uint32_t b, row_consts& k) {
   return row_sub_p_if_ge(row_mul_lazy(a, b, k), k);
 }
 
-__device__ __forceinline__ uint32_t row_mul_lazy(uint32_t a, uint32_t b, const row_consts& k) {
+__device__ __forceinline__ uint32_t row_mul_lazy(uint32_t a, uint32_t b, row_consts& k) {
+  row_consts_here(k);
   const uint32_t bl = b & 0xffffu, bh = b >> 16;
   uint64_t SL = 0, SH = 0;
   row_for<0, 8>([&](auto ic) {
@@ -270,7 +292,7 @@ __device__ __forceinline__ uint32_t row_resolve(uint64_t x) {
 // (V >> 224) times a float just below 1 / (p_7 + 1) (p_7 = p >> 224): the float error
 // (below 2^-21 relative) is smaller than the factor's margin (2^-18), so q <= V / p, and
 // q is at least floor(V / p) - 2 because V / p < 35.
-__device__ __forceinline__ uint32_t row_reduce_q(uint32_t V, const row_consts& k) {
+__device__ __forceinline__ uint32_t row_reduce_q(uint32_t V, row_consts& k) {
   const float top = (float)row_bcast<8>(V) * 0x1.52917cp+2f + (float)row_bcast<7>(V) * 0x1.52917cp-30f;
   const uint32_t q = (uint32_t)top;
   const uint64_t y = (uint64_t)q * k.negp + (V & k.lo8);
@@ -278,30 +300,60 @@ __device__ __forceinline__ uint32_t row_reduce_q(uint32_t V, const row_consts& k
 }
 
 // a - 2b, b < 3p, via 11 p - 2 (2^256 - 1).
-__device__ __forceinline__ uint32_t row_lin_a_2b(uint32_t a, uint32_t b, const row_consts& k) {
+__device__ __forceinline__ uint32_t row_lin_a_2b(uint32_t a, uint32_t b, row_consts& k) {
   const uint64_t x = (uint64_t)(~b & k.lo8) * 2u + a + k.c2;
   return row_reduce_q(row_resolve(x), k);
 }
 
 // 6a - 2b - c, via 16 p - 3 (2^256 - 1).
 __device__ __forceinline__ uint32_t row_lin_6a_2b_c(uint32_t a, uint32_t b, uint32_t c,
-                                                    const row_consts& k) {
+                                                    row_consts& k) {
   const uint64_t x = (uint64_t)a * 6u + (uint64_t)(~b & k.lo8) * 2u + (~c & k.lo8) + k.c3;
   return row_reduce_q(row_resolve(x), k);
 }
 
 // 3a.
-__device__ __forceinline__ uint32_t row_lin_3a(uint32_t a, const row_consts& k) {
+__device__ __forceinline__ uint32_t row_lin_3a(uint32_t a, row_consts& k) {
   return row_reduce_q(row_resolve((uint64_t)a * 3u), k);
 }
 
+// 2a.
+__device__ __forceinline__ uint32_t row_lin_2a(uint32_t a, row_consts& k) {
+  return row_reduce_q(row_resolve((uint64_t)a * 2u), k);
+}
+
+// a - b, via 6 p - (2^256 - 1).
+__device__ __forceinline__ uint32_t row_lin_a_b(uint32_t a, uint32_t b, row_consts& k) {
+  const uint64_t x = (uint64_t)(~b & k.lo8) + a + k.c1;
+  return row_reduce_q(row_resolve(x), k);
+}
+
+// a - b - 2c, via 16 p - 3 (2^256 - 1).
+__device__ __forceinline__ uint32_t row_lin_a_b_2c(uint32_t a, uint32_t b, uint32_t c,
+                                                   row_consts& k) {
+  const uint64_t x = (uint64_t)(~b & k.lo8) + (uint64_t)(~c & k.lo8) * 2u + a + k.c3;
+  return row_reduce_q(row_resolve(x), k);
+}
+
+// a / 2 mod p in [0, 2p) for a < 3p: (a + p) / 2 when a is odd, a / 2 when even.
+__device__ __forceinline__ uint32_t row_half(uint32_t a, row_consts& k) {
+  const uint32_t add = (row_bcast<0>(a) & 1u) ? k.plo : 0u;
+  uint32_t s = a + add;
+  s = row_carry16(s, row_lt(s, add));  // a + p < 4p < 2^256: no carry leaves lane 7
+  return (s >> 1) | (row_shl<1>(s) << 31);
+}
+
+// True when the element is 0 on every row (all four rows hold the same fully reduced
+// element, or the whole wavefront tests one element).
+__device__ __forceinline__ bool row_all_zero(uint32_t a) { return row_eq(a, 0u) == ~0ull; }
+
 // The fully reduced element of a lazy one (< 3p).
-__device__ __forceinline__ uint32_t row_canon(uint32_t a, const row_consts& k) {
+__device__ __forceinline__ uint32_t row_canon(uint32_t a, row_consts& k) {
   return row_sub_p_if_ge(row_sub_p_if_ge(a, k), k);
 }
 
 // Operand of this row: a0 on row 0, a1 on row 1, ...
-__device__ __forceinline__ uint32_t row_pick(const row_consts& k, uint32_t a0, uint32_t a1,
+__device__ __forceinline__ uint32_t row_pick(row_consts& k, uint32_t a0, uint32_t a1,
                                              uint32_t a2, uint32_t a3) {
   const uint32_t lo = (a1 & k.m0) | (a0 & ~k.m0), hi = (a3 & k.m0) | (a2 & ~k.m0);
   return (hi & k.m1) | (lo & ~k.m1);

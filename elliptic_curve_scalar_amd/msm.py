@@ -280,11 +280,17 @@ def test_row(op: int, a: torch.Tensor, b: torch.Tensor | None = None, d: int = 0
              stream=None) -> torch.Tensor:
     """Row-form hooks of msm_test_row: ops 0..2 field ops on [n, 8] tensors, ops 3 and 4
     2^d P on [n, 32] XYZZ points (row runs, quad runs), ops 5 and 6 the latency probe on
-    four elements."""
-    words = 32 if op in (3, 4) else 8
-    out = torch.empty_like(a)
-    _check(lib().msm_test_row(op, _dev_ptr(a, words, "a"), _dev_ptr(b, 8, "b"),
-                              _dev_ptr(out, words, "out"), a.shape[0], d,
+    four elements, op 7 P + Q and op 8 2P on [n, 32] XYZZ points in row form, op 9 the
+    affine form ([n, 16]) of [n, 32] XYZZ points."""
+    words = 32 if op in (3, 4, 7, 8, 9) else 8
+    if b is not None and b.shape[0] < a.shape[0]:
+        raise ValueError("b must have at least as many rows as a")
+    if op == 9:
+        out = torch.empty((a.shape[0], 16), dtype=a.dtype, device=a.device)
+    else:
+        out = torch.empty_like(a)
+    _check(lib().msm_test_row(op, _dev_ptr(a, words, "a"), _dev_ptr(b, words, "b"),
+                              _dev_ptr(out, 16 if op == 9 else words, "out"), a.shape[0], d,
                               _stream_handle(a.device, stream)))
     return out
 

@@ -277,10 +277,14 @@ int msm_ctx_timing_read(msm_ctx* ctx, msm_timing* out);
  * doublings use (one product spread over the 16 lanes of a DPP row, four products per
  * wavefront). op 0 a*b, 1 a+b, 2 a-b on n elements (8 words each, fully reduced
  * Montgomery form, like msm_test_fp); op 3 d_out[i] = 2^d * d_a[i] for n XYZZ points (32
- * words each: X, Y, ZZ, ZZZ; d <= 4096) by runs of doublings in row form, op 4 the same
- * by the quad runs; ops 5 and 6 are a latency probe on one wavefront (n = 4): x <- x * b,
- * d times, for the four elements of d_a and d_b, in row form (5) or with the per-lane
- * product (6), the four results to d_out. d_b unused for ops 3 and 4.
+ * words each: X, Y, ZZ, ZZZ, fully reduced; d <= 4096) by runs of doublings in row form,
+ * op 4 the same by the quad runs; ops 5 and 6 are a latency probe on one wavefront
+ * (n = 4): x <- x * b, d times, for the four elements of d_a and d_b, in row form (5) or
+ * with the per-lane product (6), the four results to d_out; op 7 d_out[i] = d_a[i] +
+ * d_b[i] and op 8 d_out[i] = 2 * d_a[i] for n XYZZ points by the row-form point
+ * arithmetic of the window combine (any inputs: infinity, equal and opposite points);
+ * op 9 d_out[i] (16 words: x, y, infinity as (0, 0)) = d_a[i] in affine coordinates by
+ * the combine's final conversion. d_b is used by ops 0..2 and 5..7 only.
  *
  * msm_test_issue_rate: an instruction-rate probe of the device (not a field
  * operation): `blocks` blocks of 256 lanes each run `iters` rounds of 16 independent

@@ -94,7 +94,8 @@ def check_libmsm(path, ref_path):
                       ("msm_ctx_set_prefix_store", 5), ("msm_ctx_set_scalar_form", 2),
                       ("msm_ctx_set_timing", 3)):
         assert getattr(L, name)(None, 0) == -1 and getattr(L, name)(ctx, bad) == -1, name
-    assert L.msm_test_row(7, p, p, p, 4, 0, None) == -1
+    assert L.msm_test_row(10, p, p, p, 4, 0, None) == -1
+    assert L.msm_test_row(7, p, None, p, 4, 0, None) == -1
     assert L.msm_test_fp(9, p, p, p, 4, None) == -1
     print("ok libmsm")
 

@@ -91,7 +91,8 @@ def test_argument_errors_without_gpu():
     assert L.msm_test_issue_rate(0, 0, 1, p, None) == M.MSM_ERR_ARG
     assert L.msm_test_issue_rate(0, 1, 0, p, None) == M.MSM_ERR_ARG
     assert L.msm_test_issue_rate(0, 1, 1, None, None) == M.MSM_ERR_ARG
-    assert L.msm_test_row(7, p, p, p, 4, 0, None) == M.MSM_ERR_ARG      # unknown op
+    assert L.msm_test_row(10, p, p, p, 4, 0, None) == M.MSM_ERR_ARG     # unknown op
+    assert L.msm_test_row(7, p, None, p, 4, 0, None) == M.MSM_ERR_ARG    # point sum, no b
     assert L.msm_test_row(-1, p, p, p, 4, 0, None) == M.MSM_ERR_ARG
     assert L.msm_test_row(0, p, None, p, 4, 0, None) == M.MSM_ERR_ARG    # binary op, no b
     assert L.msm_test_row(3, p, None, p, 4, 5000, None) == M.MSM_ERR_ARG  # d > 4096

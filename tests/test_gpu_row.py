@@ -1,7 +1,9 @@
-"""GPU row-form arithmetic (rowfp.hpp, rowchain.hpp) against Python integers and the
-chord-and-tangent reference: the product, sum and difference spread over the 16 lanes of a
-DPP row, and 2^d P by runs of doublings in row form (which must also equal the quad runs
-bit for bit: both compute the same recurrence in canonical field elements)."""
+"""GPU row-form arithmetic (rowfp.hpp, rowchain.hpp, rowpoint.hpp) against Python integers
+and the chord-and-tangent reference: the product, sum and difference spread over the 16
+lanes of a DPP row; 2^d P by runs of doublings in row form (which must also equal the quad
+runs bit for bit: both compute the same recurrence in canonical field elements); the
+row-form point addition and doubling with every special case; and the affine conversion
+that ends the window combine."""
 import random
 
 import numpy as np
@@ -97,3 +99,59 @@ def test_row_latency_probe_matches_per_lane_chain():
             x = x * y * rinv % P
         want.append(x)
     assert row == want and lane == want
+
+
+def _point_cases(rng):
+    """Pairs (a, b) of affine points (None = infinity) with every special case of the XYZZ
+    addition: infinity on either or both sides, a = b (the doubling branch), a = -b, and
+    random pairs."""
+    pts = [ref.scalar_mul(rng.randrange(1, ref.R), ref.G) for _ in range(40)]
+    pairs = [(None, None), (None, pts[0]), (pts[1], None), (pts[2], pts[2]), (ref.G, ref.G),
+             (pts[3], ref.neg(pts[3])), (ref.G, ref.neg(ref.G)), (pts[4], ref.dbl(pts[4]))]
+    pairs += [(pts[i], pts[i + 1]) for i in range(5, 39)]
+    return pairs
+
+
+def _check_xyzz_invariant(words):
+    X, Y, ZZ, ZZZ = [ref.from_mont(v) for v in wl.to_ints(words.reshape(4, 8))]
+    assert max(X, Y, ZZ, ZZZ) < P
+    assert ZZ ** 3 % P == ZZZ ** 2 % P  # ZZ = Z^2, ZZZ = Z^3 for some Z
+
+
+def test_row_point_addition_every_case():
+    from elliptic_curve_scalar_amd import msm as M
+    rng = random.Random(500)
+    pairs = _point_cases(rng)
+    # each side gets its own random scaling, so a = b arrives in different coordinates
+    a = to_dev(_xyzz_words([x for x, _ in pairs], rng))
+    b = to_dev(_xyzz_words([y for _, y in pairs], rng))
+    say("row point add, pairs", len(pairs))
+    got = to_host(M.test_row(7, a, b))
+    for i, (x, y) in enumerate(pairs):
+        _check_xyzz_invariant(got[i])
+        assert _affine(got[i]) == ref.add(x, y), i
+
+
+def test_row_point_doubling():
+    from elliptic_curve_scalar_amd import msm as M
+    rng = random.Random(501)
+    pts = [None, ref.G] + [ref.scalar_mul(rng.randrange(1, ref.R), ref.G) for _ in range(30)]
+    a = to_dev(_xyzz_words(pts, rng))
+    say("row point doubling, points", len(pts))
+    got = to_host(M.test_row(8, a))
+    for i, pt in enumerate(pts):
+        _check_xyzz_invariant(got[i])
+        assert _affine(got[i]) == ref.dbl(pt), i
+
+
+def test_uniform_affine_conversion():
+    from elliptic_curve_scalar_amd import msm as M
+    rng = random.Random(502)
+    pts = [None, ref.G, ref.neg(ref.G)] + [ref.scalar_mul(rng.randrange(1, ref.R), ref.G)
+                                           for _ in range(29)]
+    a = to_dev(_xyzz_words(pts, rng))
+    say("uniform affine conversion, points", len(pts))
+    got = to_host(M.test_row(9, a))
+    for i, pt in enumerate(pts):
+        x, y = [ref.from_mont(v) for v in wl.to_ints(got[i].reshape(2, 8))]
+        assert (None if (x, y) == (0, 0) else (x, y)) == pt, i

@@ -124,6 +124,7 @@ def row_mul(a, b):
 
 
 # ---- lazy form [0, 3p) and linear combinations -----------------------------------------
+C1 = 6 * P - (R - 1)
 C2 = 11 * P - 2 * (R - 1)
 C3 = 16 * P - 3 * (R - 1)
 NEGP = R - P
@@ -193,6 +194,37 @@ def lin_6a_2b_c(a, b, c, q_shift=0):
 
 def lin_3a(a, q_shift=0):
     return reduce_q(resolve([3 * u for u in a]), q_shift)
+
+
+def lin_2a(a, q_shift=0):
+    return reduce_q(resolve([2 * u for u in a]), q_shift)
+
+
+def lin_a_b(a, b, q_shift=0):
+    lo8 = lane_words(R - 1)
+    x = [((~v & M32) & m) + u + c for u, v, m, c in zip(a, b, lo8, lane_words(C1))]
+    return reduce_q(resolve(x), q_shift)
+
+
+def lin_a_b_2c(a, b, c, q_shift=0):
+    lo8 = lane_words(R - 1)
+    x = [((~v & M32) & m) + 2 * ((~w & M32) & m) + u + k
+         for u, v, w, m, k in zip(a, b, c, lo8, lane_words(C3))]
+    return reduce_q(resolve(x), q_shift)
+
+
+def row_half(a):
+    """The kernel's a / 2 mod p: add p (lane l word l) when lane 0's word is odd, carry,
+    then shift the row right by one bit (lane l takes bit 0 of lane l + 1 as its bit 31)."""
+    plo = K[4]
+    out = []
+    for r in range(4):
+        row = a[16 * r:16 * r + 16]
+        add = plo[16 * r:16 * r + 16] if row[0] & 1 else [0] * 16
+        s = [(x + y) & M32 for x, y in zip(row, add)]
+        s = carry16(s + [0] * 48, [x < y for x, y in zip(s, add)] + [False] * 48)[:16]
+        out += [(s[l] >> 1) | (((s[l + 1] if l < 15 else 0) << 31) & M32) for l in range(16)]
+    return out
 
 
 def row_add(a, b):
@@ -301,10 +333,20 @@ def test_lazy_form_closed_under_products_and_combinations():
                 assert g < 3 * P and g % P == (6 * x - 2 * y - z) % P
             for g, x in zip(unpack(lin_3a(A, sh)), xs):
                 assert g < 3 * P and g % P == 3 * x % P
+            for g, x in zip(unpack(lin_2a(A, sh)), xs):
+                assert g < 3 * P and g % P == 2 * x % P
+            for g, x, y in zip(unpack(lin_a_b(A, B, sh)), xs, ys):
+                assert g < 3 * P and g % P == (x - y) % P
+            for g, x, y, z in zip(unpack(lin_a_b_2c(A, B, Cv, sh)), xs, ys, zs):
+                assert g < 3 * P and g % P == (x - y - 2 * z) % P
+        half = pow(2, -1, P)
+        for g, x in zip(unpack(row_half(A)), xs):
+            assert g < 2 * P and g % P == x * half % P
 
 
 def test_lazy_offsets_and_estimate_bounds():
-    assert C2 >= 0 and C3 >= 0 and C2 == 11 * P - 2 * (R - 1) and C3 == 16 * P - 3 * (R - 1)
+    assert C1 >= 0 and C2 >= 0 and C3 >= 0
+    assert C1 == 6 * P - (R - 1) and C2 == 11 * P - 2 * (R - 1) and C3 == 16 * P - 3 * (R - 1)
     # the largest combination stays below 2^259 (lanes 0..8) and below 35 p
     assert 6 * 3 * P + 2 * (R - 1) + (R - 1) + C3 < min(1 << 259, 35 * P)
     # the kernel's float factor is below 1 / (p_7 + 1) by more than the float error (2^-21)
@@ -313,7 +355,7 @@ def test_lazy_offsets_and_estimate_bounds():
     assert f * (P7 + 1) > 1 - 2 ** -17
     assert float.fromhex("0x1.52917cp+2") == f * 2 ** 32
     src = open(ROWFP).read()
-    for name, val in (("kRowC2", C2), ("kRowC3", C3), ("kRowNegP", NEGP)):
+    for name, val in (("kRowC1", C1), ("kRowC2", C2), ("kRowC3", C3), ("kRowNegP", NEGP)):
         body = src[src.index(name + "[16]"):]
         body = body[:body.index("};")]
         ws = [int(w, 16) for w in re.findall(r"0x([0-9a-f]+)u", body)]
