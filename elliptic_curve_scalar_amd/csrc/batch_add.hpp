@@ -42,7 +42,20 @@ __device__ __forceinline__ fp add_denominator(const aff& A, const aff& B, int cs
   return fp_one();
 }
 
+// Product and square of a batch: inline, or as calls (OUTLINE, fp_mul_call).
+template <bool OUTLINE>
+__device__ __forceinline__ fp bmul(const fp& a, const fp& b) {
+  if constexpr (OUTLINE) return fp_mul_call(a, b);
+  else return fp_mul(a, b);
+}
+template <bool OUTLINE>
+__device__ __forceinline__ fp bsqr(const fp& a) {
+  if constexpr (OUTLINE) return fp_sqr_call(a);
+  else return fp_sqr(a);
+}
+
 // Finish slot s once 1/d is known.
+template <bool OUTLINE = false>
 __device__ __forceinline__ aff add_finish(const aff& A, const aff& B, int cs, const fp& inv_d) {
   if (cs == ADD_A_INF) return B;
   if (cs == ADD_B_INF) return A;
@@ -51,13 +64,13 @@ __device__ __forceinline__ aff add_finish(const aff& A, const aff& B, int cs, co
   if (cs == ADD_CHORD) {
     num = fp_sub(B.y, A.y);
   } else {
-    fp xx = fp_sqr(A.x);
+    fp xx = bsqr<OUTLINE>(A.x);
     num = fp_add(fp_dbl(xx), xx);
   }
-  fp lam = fp_mul(num, inv_d);
+  fp lam = bmul<OUTLINE>(num, inv_d);
   aff r;
-  r.x = fp_sub(fp_sub(fp_sqr(lam), A.x), B.x);
-  r.y = fp_sub(fp_mul(lam, fp_sub(A.x, r.x)), A.y);
+  r.x = fp_sub(fp_sub(bsqr<OUTLINE>(lam), A.x), B.x);
+  r.y = fp_sub(bmul<OUTLINE>(lam, fp_sub(A.x, r.x)), A.y);
   return r;
 }
 
@@ -116,7 +129,7 @@ constexpr uint32_t pref_lds_bytes(int S, bool DX) { return (DX ? 2u : 1u) * 32u 
 // (d = 1, nothing stored). The forward pass reads only the x-coordinates unless an x
 // is 0 or the two x agree (infinity, tangent, cancel), which then loads the whole
 // points.
-template <int S, bool DX, class Store, class Src>
+template <int S, bool DX, bool OUTLINE = false, class Store, class Src>
 __device__ __forceinline__ void batch_affine_add(Src& src, int cnt, Store& st) {
   fp acc = fp_one();
 #pragma unroll
@@ -131,7 +144,7 @@ __device__ __forceinline__ void batch_affine_add(Src& src, int cnt, Store& st) {
         d = add_denominator(A, B, add_case(A, B));
       }
       if (DX) st.set_dx(s, d);
-      acc = (s == 0) ? d : fp_mul(acc, d);
+      acc = (s == 0) ? d : bmul<OUTLINE>(acc, d);
     }
     st.set(s, acc);
   }
@@ -139,11 +152,11 @@ __device__ __forceinline__ void batch_affine_add(Src& src, int cnt, Store& st) {
 #pragma unroll
   for (int s = S - 1; s >= 0; s--) {
     if (s < cnt) {
-      const fp inv_d = (s > 0) ? fp_mul(inv, st.get(s - 1)) : inv;
+      const fp inv_d = (s > 0) ? bmul<OUTLINE>(inv, st.get(s - 1)) : inv;
       const aff A = src.a(s), B = src.b(s);
       const int cs = add_case(A, B);
-      inv = fp_mul(inv, DX ? st.get_dx(s) : add_denominator(A, B, cs));
-      src.put(s, add_finish(A, B, cs, inv_d));
+      inv = bmul<OUTLINE>(inv, DX ? st.get_dx(s) : add_denominator(A, B, cs));
+      src.put(s, add_finish<OUTLINE>(A, B, cs, inv_d));
     }
   }
 }
@@ -205,10 +218,10 @@ __device__ __forceinline__ void batch_affine_add_ckpt(Src& src, int cnt, Store& 
 }
 
 // The batch with its slot state in private memory.
-template <int S, class Src>
+template <int S, bool OUTLINE = false, class Src>
 __device__ __forceinline__ void batch_affine_add(Src& src, int cnt) {
   PrefPrivate<S, false> st;
-  batch_affine_add<S, false>(src, cnt, st);
+  batch_affine_add<S, false, OUTLINE>(src, cnt, st);
 }
 
 }  // namespace msmk

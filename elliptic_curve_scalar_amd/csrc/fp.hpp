@@ -10,8 +10,9 @@
 //     format, always fully reduced (< p) between operations;
 //   * the product is coarsely integrated operand scanning with 32x32->64
 //     multiply-adds (v_mad_u64_u32 on gfx950, issued at half the rate of plain 32-bit
-//     ALU ops); p < 2^254 keeps every partial sum inside 288 bits and the result
-//     before the final subtraction below 2p;
+//     ALU ops), each row's multiply-adds independent of each other and its carries in
+//     one add-with-carry chain; p < 2^254 keeps every partial sum inside 288 bits and
+//     the result before the final subtraction below 2p;
 //   * Fermat's x^(p-2) (fp_inv_fermat) is here; the inverse the kernels use is the
 //     binary GCD of bingcd.hpp (Fermat remains its fallback).
 //
@@ -153,114 +154,100 @@ __device__ __forceinline__ fp fp_half(const fp& a) {
 }
 
 // Montgomery product a * b * 2^-256 mod p, coarsely integrated operand scanning on
-// 32-bit limbs.
-// 64-bit value kept whole through code generation: the empty asm stops the compiler
-// from re-associating a * b + (t + c) into (a * b + t) + c, which costs two 64-bit
-// adds and the register moves that widen t and c, where the form below costs one
-// 32-bit add and the select of its carry.
-__device__ __forceinline__ uint64_t fp_opaque(uint64_t x) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  asm("" : "+v"(x));
-#endif
-  return x;
-}
-
-// t + c (both 32-bit) as a 64-bit multiply-add addend.
-__device__ __forceinline__ uint64_t fp_add33(uint32_t t, uint32_t c) {
-  const uint32_t lo = t + c;
-  const uint32_t hi = lo < c ? 1u : 0u;
-  return fp_opaque(((uint64_t)hi << 32) | lo);
-}
-
+// 32-bit limbs. Each row (t += a b_i, then t = (t + m p) / 2^32 with m = t_0 (-p^-1) mod
+// 2^32) is eight independent multiply-adds s_j = x_j y + t_j (each below 2^64) and one
+// carry chain t_j = lo(s_j) + hi(s_(j-1)) + carry: the products of a row do not wait for
+// each other, and the chain of the row overlaps the next row's products. The word t_8
+// rides in the high half of the last addend (s_7 = x_7 y + t_7 + 2^32 t_8), which stays
+// below 2^64 because a_7 and p_7 are below 2^30, so the chain needs no ninth step. Bounds:
+// t < 2p before each product row, so t + a b_i < 2^287 (t_8 < 2^31) and after each
+// reduction row t < 2p again (t_8 = 0).
 __device__ __forceinline__ fp fp_mul_cios(const fp& a, const fp& b) {
   uint32_t t[9];
 #pragma unroll
   for (int j = 0; j < 9; j++) t[j] = 0;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
-    // t += a * b_i: each step is (hi, lo) = a_j b_i + (t_j + carry), which fits 64 bits
+    uint64_t s[8];
+#pragma unroll
+    for (int j = 0; j < 7; j++) s[j] = (uint64_t)a.v[j] * b.v[i] + t[j];
+    s[7] = (uint64_t)a.v[7] * b.v[i] + (((uint64_t)t[8] << 32) | t[7]);
     uint32_t c = 0;
+    t[0] = (uint32_t)s[0];
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-      const uint64_t s = (uint64_t)a.v[j] * b.v[i] + (i == 0 ? fp_opaque(c) : fp_add33(t[j], c));
-      t[j] = (uint32_t)s;
-      c = (uint32_t)(s >> 32);
-    }
-    uint64_t top = (uint64_t)t[8] + c;
-    t[8] = (uint32_t)top;
-    // with p < 2^254 the running value stays below 2p * 2^32, so no word above t[8]
+    for (int j = 1; j < 8; j++) t[j] = __builtin_addc((uint32_t)s[j], (uint32_t)(s[j - 1] >> 32), c, &c);
+    t[8] = (uint32_t)(s[7] >> 32) + c;
     const uint32_t m = t[0] * MSM_PINV;
-    const uint64_t s0 = (uint64_t)m * p_limb(0) + fp_opaque(t[0]);
-    c = (uint32_t)(s0 >> 32);
 #pragma unroll
-    for (int j = 1; j < 8; j++) {
-      const uint64_t s = (uint64_t)m * p_limb(j) + fp_add33(t[j], c);
-      t[j - 1] = (uint32_t)s;
-      c = (uint32_t)(s >> 32);
-    }
-    top = (uint64_t)t[8] + c;
-    t[7] = (uint32_t)top;
-    t[8] = (uint32_t)(top >> 32);
+    for (int j = 0; j < 7; j++) s[j] = (uint64_t)m * p_limb(j) + t[j];
+    s[7] = (uint64_t)m * p_limb(7) + (((uint64_t)t[8] << 32) | t[7]);
+    c = 0;  // lo(s_0) = 0 by the choice of m: the row drops it
+#pragma unroll
+    for (int j = 1; j < 8; j++) t[j - 1] = __builtin_addc((uint32_t)s[j], (uint32_t)(s[j - 1] >> 32), c, &c);
+    t[7] = (uint32_t)(s[7] >> 32) + c;
+    t[8] = 0;
   }
   fp r;
 #pragma unroll
   for (int j = 0; j < 8; j++) r.v[j] = t[j];
-  // inputs < p give t < 2p < 2^255, so t[8] == 0
-  return fp_reduce_once(r);
+  return fp_reduce_once(r);  // t < 2p
 }
 
 // Montgomery square a^2 * 2^-256 mod p by separated operand scanning: the 28 products
 // a_i a_j (i < j) once, the 512-bit sum doubled by a one-bit shift, the 8 squares a_i^2
 // added, then the word-serial Montgomery reduction (8 rounds of t += m p 2^(32 i),
-// m = t_i (-p^-1) mod 2^32): 108 multiply-adds against 136 for the product.
+// m = t_i (-p^-1) mod 2^32): 108 multiply-adds against 136 for the product. Every row is
+// independent multiply-adds and one carry chain, as in fp_mul_cios. The carry out of a
+// reduction round's top word (t_(i+8)) belongs to word i + 9, which is the high half of
+// the next round's last addend (m p_7 < 2^62 leaves room for it); after the last round
+// it is 0, since (a^2 + M p) / 2^256 < 2p < 2^255.
 __device__ __forceinline__ fp fp_sqr_sos(const fp& a) {
   uint32_t t[16];
 #pragma unroll
   for (int k = 0; k < 16; k++) t[k] = 0;
-  // off-diagonal products: row i adds a_i a_j (j > i) at t[i + j]
+  // off-diagonal products: row i adds a_i a_j (j > i) at t[i + j]; t[i + 8] is still 0
 #pragma unroll
   for (int i = 0; i < 7; i++) {
-    uint32_t c = 0;
+    uint64_t s[8];
 #pragma unroll
-    for (int j = i + 1; j < 8; j++) {
-      const uint64_t s = (uint64_t)a.v[i] * a.v[j] + fp_add33(t[i + j], c);
-      t[i + j] = (uint32_t)s;
-      c = (uint32_t)(s >> 32);
-    }
-    t[i + 8] = c;
+    for (int j = i + 1; j < 8; j++) s[j] = (uint64_t)a.v[i] * a.v[j] + t[i + j];
+    uint32_t c = 0;
+    t[2 * i + 1] = (uint32_t)s[i + 1];
+#pragma unroll
+    for (int j = i + 2; j < 8; j++) t[i + j] = __builtin_addc((uint32_t)s[j], (uint32_t)(s[j - 1] >> 32), c, &c);
+    t[i + 8] = (uint32_t)(s[7] >> 32) + c;
   }
   // double (the top bit of t[14] moves into t[15], which is still 0)
 #pragma unroll
   for (int k = 15; k > 0; k--) t[k] = __builtin_amdgcn_alignbit(t[k], t[k - 1], 31);
   t[0] = 0;
-  // the squares a_i^2 at t[2i], t[2i + 1]
-  uint32_t c = 0;
+  // the squares a_i^2 at t[2i], t[2i + 1]: one chain over the sixteen words
+  {
+    uint64_t s[8];
 #pragma unroll
-  for (int i = 0; i < 8; i++) {
-    const uint64_t s = (uint64_t)a.v[i] * a.v[i] + fp_add33(t[2 * i], c);
-    t[2 * i] = (uint32_t)s;
-    const uint64_t u = (uint64_t)t[2 * i + 1] + (uint32_t)(s >> 32);
-    t[2 * i + 1] = (uint32_t)u;
-    c = (uint32_t)(u >> 32);
+    for (int i = 0; i < 8; i++) s[i] = (uint64_t)a.v[i] * a.v[i] + t[2 * i];
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      t[2 * i] = __builtin_addc((uint32_t)s[i], 0u, c, &c);
+      t[2 * i + 1] = __builtin_addc(t[2 * i + 1], (uint32_t)(s[i] >> 32), c, &c);
+    }
   }
-  // reduction: after round i, t[0..i] are 0 and the value is unchanged mod p; the carry
-  // out of t[i + 8] is deferred to round i + 1, whose last add lands on t[i + 9]
+  // reduction: after round i, t[0..i] are 0 and the value is unchanged mod p
   uint32_t cc = 0;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     const uint32_t m = t[i] * MSM_PINV;
-    uint32_t c2 = 0;
+    uint64_t s[8];
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-      const uint64_t s = (uint64_t)m * p_limb(j) + fp_add33(t[i + j], c2);
-      t[i + j] = (uint32_t)s;
-      c2 = (uint32_t)(s >> 32);
-    }
-    const uint64_t u = (uint64_t)t[i + 8] + c2 + cc;
-    t[i + 8] = (uint32_t)u;
-    cc = (uint32_t)(u >> 32);
+    for (int j = 0; j < 7; j++) s[j] = (uint64_t)m * p_limb(j) + t[i + j];
+    s[7] = (uint64_t)m * p_limb(7) + (((uint64_t)cc << 32) | t[i + 7]);
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 1; j < 8; j++) t[i + j] = __builtin_addc((uint32_t)s[j], (uint32_t)(s[j - 1] >> 32), c, &c);
+    t[i + 8] = __builtin_addc(t[i + 8], (uint32_t)(s[7] >> 32), c, &c);
+    cc = c;
   }
-  // (a^2 + M p) / 2^256 < (p^2 + 2^256 p) / 2^256 < 2p < 2^255: no carry is left in cc
   fp r;
 #pragma unroll
   for (int j = 0; j < 8; j++) r.v[j] = t[8 + j];
@@ -270,6 +257,12 @@ __device__ __forceinline__ fp fp_sqr_sos(const fp& a) {
 // Montgomery product a * b * 2^-256 mod p; inputs and output fully reduced.
 __device__ __forceinline__ fp fp_mul(const fp& a, const fp& b) { return fp_mul_cios(a, b); }
 __device__ __forceinline__ fp fp_sqr(const fp& a) { return fp_sqr_sos(a); }
+
+// The same as calls, one copy of each in the code object: for kernels that would inline
+// hundreds of them into one body (the stream walker's batches at large S), where the
+// register coalescer's compile time grows without bound on the inlined form.
+__device__ __noinline__ fp fp_mul_call(const fp& a, const fp& b) { return fp_mul_cios(a, b); }
+__device__ __noinline__ fp fp_sqr_call(const fp& a) { return fp_sqr_sos(a); }
 
 // Small constant c (< 2^32) in Montgomery form.
 __device__ __forceinline__ fp fp_from_u32(uint32_t c) {

@@ -134,7 +134,7 @@ __global__ void __launch_bounds__(64) k_test_row_pts(int op, const uint32_t* __r
   row_consts k = row_consts_load();
   const rxyzz a = rxyzz_load(src);
   if (op == 9) {
-    const aff r = xyzz_to_aff(rxyzz_to_uniform(a, k));
+    const aff r = xyzz_to_aff(rxyzz_to_fp(a, k));
     if (threadIdx.x == 0) aff_store(reinterpret_cast<g1a*>(out) + blockIdx.x, r);
     return;
   }

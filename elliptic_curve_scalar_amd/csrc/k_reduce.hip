@@ -216,7 +216,7 @@ k_plane_chain(const xyzz_st* __restrict__ part,
   acc = (w < ngroups) ? rxyzz_load_coherent(gres + w) : rxyzz_inf();
   acc = block_row_sum(acc, w, sh, k);
   if (w == 0) {
-    const aff a = xyzz_to_aff(rxyzz_to_uniform(acc, k));
+    const aff a = xyzz_to_aff(rxyzz_to_fp(acc, k));
     if (threadIdx.x == 0) aff_store(out, a);
   }
 }

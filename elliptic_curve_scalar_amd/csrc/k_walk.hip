@@ -131,7 +131,7 @@ __global__ void __launch_bounds__(128) k_walk(const g1a* __restrict__ pts,
       if ((uint64_t)src.zof(s) * L + step < E) cnt = s + 1;
     if (cnt == 0) break;
     for (int s = 0; s < cnt; s++) src.ent[s] = idx[src.zof(s) * L + step];
-    batch_affine_add<S>(src, cnt);
+    batch_affine_add<S, true>(src, cnt);  // products as calls: see fp_mul_call
     for (int s = 0; s < cnt; s++) {
       const uint32_t z = src.zof(s);
       const uint32_t cstart = z * L;  // below E: slot s had an entry this step

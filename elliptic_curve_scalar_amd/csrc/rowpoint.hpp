@@ -94,18 +94,17 @@ __device__ __forceinline__ rxyzz rxyzz_from_lds(const uint32_t* s) {
   return r;
 }
 
-// The point as per-lane field elements in scalar registers (word i read from lane i), for
-// code that the whole wavefront runs on one value; fully reduced.
-__device__ __forceinline__ xyzz rxyzz_to_uniform(const rxyzz& a, row_consts& k) {
+// The point as per-lane field elements (every lane holds all eight words of each
+// coordinate, read from lanes 0..7 of its row), fully reduced. The values stay in vector
+// registers: in scalar registers the binary-GCD inverse that follows would run its steps
+// on the scalar unit, which issues them no faster and needs more of them.
+__device__ __forceinline__ xyzz rxyzz_to_fp(const rxyzz& a, row_consts& k) {
   const rxyzz c = rxyzz_canon(a, k);
   xyzz r;
-#pragma unroll
-  for (int i = 0; i < 8; i++) {
-    r.X.v[i] = __builtin_amdgcn_readlane(c.X, i);
-    r.Y.v[i] = __builtin_amdgcn_readlane(c.Y, i);
-    r.ZZ.v[i] = __builtin_amdgcn_readlane(c.ZZ, i);
-    r.ZZZ.v[i] = __builtin_amdgcn_readlane(c.ZZZ, i);
-  }
+  r.X = row_to_fp(c.X);
+  r.Y = row_to_fp(c.Y);
+  r.ZZ = row_to_fp(c.ZZ);
+  r.ZZZ = row_to_fp(c.ZZZ);
   return r;
 }
 
