@@ -112,23 +112,26 @@ __device__ __forceinline__ void bg_batch(uint64_t xa, uint64_t xb, int32_t& f0, 
 
 // t = x f + y g (+ k p when KP) as nine words of a two's-complement integer, for x, y
 // below 2^254 and |f| + |g| <= 2^30. The factors are offset to f + 2^30 and g + 2^30
-// (both in [0, 2^31]), so each word is plain chained multiply-adds that stay inside 64
-// bits ((2^32 - 1)(f + g + 2^31 + k) plus a carry is below 2^64 as f + g + 2^31 <= 3 2^30
-// and k < 2^30), and 2^30 (x + y) is subtracted once at the end.
+// (both in [0, 2^31]), so word i's products sum to s_i = x_i fo + y_i go (+ k p_i), below
+// (2^32 - 1)(f + g + 2^31 + k) < 2^64 as f + g + 2^31 <= 3 2^30 and k < 2^30: the words'
+// multiply-adds are independent of each other, and one add-with-carry chain joins them
+// (t_i = lo(s_i) + hi(s_(i-1)) + carry). 2^30 (x + y) is subtracted once at the end.
 template <bool KP>
 __device__ __forceinline__ void bg_comb(const uint32_t (&x)[8], const uint32_t (&y)[8], int32_t f,
                                         int32_t g, uint32_t k, uint32_t (&t)[9]) {
   const uint32_t fo = (uint32_t)f + (1u << 30), go = (uint32_t)g + (1u << 30);
-  uint32_t c = 0;
+  uint64_t s[8];
 #pragma unroll
   for (int i = 0; i < 8; i++) {
-    uint64_t s = (uint64_t)x[i] * fo + c;
-    s = (uint64_t)y[i] * go + s;
-    if (KP) s = (uint64_t)k * bg_p(i) + s;
-    t[i] = (uint32_t)s;
-    c = (uint32_t)(s >> 32);
+    s[i] = (uint64_t)x[i] * fo;
+    s[i] = (uint64_t)y[i] * go + s[i];
+    if (KP) s[i] = (uint64_t)k * bg_p(i) + s[i];
   }
-  t[8] = c;
+  uint32_t c = 0;
+  t[0] = (uint32_t)s[0];
+#pragma unroll
+  for (int i = 1; i < 8; i++) t[i] = __builtin_addc((uint32_t)s[i], (uint32_t)(s[i - 1] >> 32), c, &c);
+  t[8] = (uint32_t)(s[7] >> 32) + c;
   // subtract (x + y) << 30 (x + y < 2^255: nine words after the shift)
   uint32_t sum[8], cs = 0;
 #pragma unroll

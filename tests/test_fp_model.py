@@ -1,8 +1,10 @@
-"""Word-exact model of the per-lane Montgomery product and square of fp.hpp
-(fp_mul_cios, fp_sqr_sos): each row's 32 x 32 -> 64-bit multiply-adds with their addends,
-then one add-with-carry chain, with the top word carried in the high half of the row's last
-addend. The model asserts every bound the kernel relies on (no multiply-add above 2^64, no
-carry lost) and checks the result against a b 2^-256 mod p on edge and random values."""
+"""Word-exact models of the per-lane Montgomery product and square of fp.hpp
+(fp_mul_cios, fp_sqr_sos) and of the binary-GCD inverse's linear combination (bingcd.hpp,
+bg_comb): each row's 32 x 32 -> 64-bit multiply-adds with their addends, then one
+add-with-carry chain, with the top word carried in the high half of the row's last addend.
+The models assert every bound the kernels rely on (no multiply-add above 2^64, no carry
+lost) and check the results against the plain integer definitions on edge and random
+values."""
 import random
 
 from oracle import ref
@@ -151,3 +153,37 @@ def test_models_catch_a_dropped_top_word():
         x, y = rng.randrange(P), rng.randrange(P)
         wrong += mul_dropped(x, y) != x * y * rinv % P
     assert wrong > 40
+
+
+def comb_model(x, y, f, g, k, kp):
+    """bingcd.hpp's bg_comb before its final subtraction: word i's products summed into one
+    64-bit value (f, g offset by 2^30), then one add-with-carry chain over the words."""
+    fo, go = f + (1 << 30), g + (1 << 30)
+    assert 0 <= fo <= 1 << 31 and 0 <= go <= 1 << 31
+    X, Y = words(x), words(y)
+    s = [mad(X[i], fo, 0) + Y[i] * go + (k * PL[i] if kp else 0) for i in range(8)]
+    assert all(v < 1 << 64 for v in s)
+    t, c = [s[0] & M32], 0
+    for i in range(1, 8):
+        w, c = addc(s[i] & M32, s[i - 1] >> 32, c)
+        t.append(w)
+    top = (s[7] >> 32) + c
+    assert top <= M32
+    return sum(w << (32 * i) for i, w in enumerate(t + [top]))
+
+
+def test_inverse_combination_model():
+    rng = random.Random(24)
+    for _ in range(3000):
+        x, y = rng.randrange(1 << 254), rng.randrange(1 << 254)
+        f = rng.randrange(-(1 << 30), (1 << 30) + 1)
+        lim = (1 << 30) - abs(f)
+        g = rng.randrange(-lim, lim + 1)
+        k, kp = rng.randrange(1 << 30), rng.random() < 0.5
+        want = x * (f + (1 << 30)) + y * (g + (1 << 30)) + (k * P if kp else 0)
+        assert comb_model(x, y, f, g, k, kp) == want
+    # extremes of the factors
+    for f, g in ((1 << 30, 0), (0, 1 << 30), (-(1 << 30), 0), (0, -(1 << 30)), (1 << 29, -(1 << 29))):
+        x = y = (1 << 254) - 1
+        assert comb_model(x, y, f, g, (1 << 30) - 1, True) == \
+            x * (f + (1 << 30)) + y * (g + (1 << 30)) + ((1 << 30) - 1) * P
