@@ -13,9 +13,11 @@ step against the same peak (roofline_largest), and the CPU oracle timed on this 
 cores on the same workload (cpu_baseline).
 
 Other modes (one JSON line each, not the benchmark line):
-  --probe-rates  sustained issue rates of the instruction classes the field code is
-                 made of (msm_test_issue_rate), which set the integer roofline's peak;
-  --cpu-table    the oracle on every workload, all host cores and one core.
+  --probe-latency  latency of one wavefront's product and doubling chains, row form
+                   against the per-lane and quad forms (msm_test_row);
+  --probe-rates    sustained issue rates of the instruction classes the field code is
+                   made of (msm_test_issue_rate), which set the integer roofline's peak;
+  --cpu-table      the oracle on every workload, all host cores and one core.
 """
 from __future__ import annotations
 
@@ -143,6 +145,55 @@ def probe_rates(args) -> int:
     return 0
 
 
+def probe_latency(args) -> int:
+    """Latency of one wavefront's dependent chains, from the msm_test_row hooks timed with
+    events: a chain of 2000 Montgomery products in row form (one product per row of 16
+    lanes, op 5) and with the per-lane product (op 6), and a run of 2000 doublings of one
+    point in row form (op 3) and in the quad form (op 4)."""
+    import random
+
+    import torch
+
+    from elliptic_curve_scalar_amd import msm as M
+    from elliptic_curve_scalar_amd import workloads as wl
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    P = 0x30644E72E131A029B85045B68181585D97816A916871CA8D3C208C16D87CFD47
+    rng = random.Random(11)
+    a = torch.from_numpy(wl.from_ints([rng.randrange(P) for _ in range(4)])).to(dev)
+    b = torch.from_numpy(wl.from_ints([rng.randrange(P) for _ in range(4)])).to(dev)
+    # one XYZZ point (X, Y, ZZ, ZZZ) = (x, y, 1, 1) in Montgomery form: the generator (1, 2)
+    R = 1 << 256
+    pt = torch.from_numpy(wl.from_ints([R % P, 2 * R % P, R % P, R % P]).reshape(1, 32)).to(dev)
+    D = 2000
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        best = None
+        for _ in range(5):
+            ev0.record()
+            fn()
+            ev1.record()
+            torch.cuda.synchronize()
+            t = ev0.elapsed_time(ev1) * 1e3 / D  # us per step
+            best = t if best is None else min(best, t)
+        return best
+
+    res = {
+        "row_product_us": timed(lambda: M.test_row(5, a, b, D)),
+        "lane_product_us": timed(lambda: M.test_row(6, a, b, D)),
+        "row_doubling_us": timed(lambda: M.test_row(3, pt, None, D)),
+        "quad_doubling_us": timed(lambda: M.test_row(4, pt, None, D)),
+    }
+    for k, v in res.items():
+        log(f"[latency] {k}: {v:.3f}")
+    print(json.dumps({"probe": "chain latency", "steps": D, **res}), flush=True)
+    return 0
+
+
 def cpu_table(args) -> int:
     """The oracle's Pippenger on every workload at the workload's c, with every host core
     (one thread per window, up to the cores there are) and with one core."""
@@ -192,6 +243,8 @@ def main() -> int:
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB on the device once: "
                          "a kernel of known traffic for scaling hardware byte counters")
+    ap.add_argument("--probe-latency", action="store_true",
+                    help="latency of one wavefront's product and doubling chains (row vs per-lane)")
     ap.add_argument("--probe-rates", action="store_true",
                     help="measure instruction issue rates instead of the MSM")
     ap.add_argument("--cpu-table", action="store_true",
@@ -203,6 +256,8 @@ def main() -> int:
         return 2
     if args.probe_rates:
         return probe_rates(args)
+    if args.probe_latency:
+        return probe_latency(args)
     if args.cpu_table:
         return cpu_table(args)
 
