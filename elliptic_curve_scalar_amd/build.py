@@ -17,7 +17,8 @@ OBJ_DIR = os.path.join(HERE, "_build")
 SOURCES = ["k_sort.hip", "k_levels.hip", "k_level_pref.hip", "k_walk.hip", "k_reduce.hip", "k_aux.hip", "msm_api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-Wall",
-         # no packed FP32 instructions anywhere (none of this code is floating point)
+         # no packed FP32 instructions anywhere (the only floating point is the row form's
+         # quotient estimate, one float multiply-add per lane)
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 

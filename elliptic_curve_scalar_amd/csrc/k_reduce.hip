@@ -157,11 +157,9 @@ __device__ __forceinline__ rxyzz block_row_sum(rxyzz acc, uint32_t w, uint32_t (
 // sharing them; the last group to finish (join[MAX_PLANE_GROUPS]) adds the group sums
 // (one per wavefront) and writes the affine result (its one inversion on wavefront 0).
 // The counters start at zero (cleared with the plan statistics before the MSM).
-__global__ void __launch_bounds__(64 * CHAIN_WAVES) __attribute__((amdgpu_waves_per_eu(1, 2)))
-k_plane_chain(const xyzz_st* __restrict__ part,
-                                                                 plane_table pt, xyzz_st* res,
-                                                                 xyzz_st* gres, uint32_t* join,
-                                                                 g1a* out) {
+__global__ void __launch_bounds__(64 * CHAIN_WAVES)
+k_plane_chain(const xyzz_st* __restrict__ part, plane_table pt, xyzz_st* res, xyzz_st* gres,
+              uint32_t* join, g1a* out) {
   __shared__ uint32_t sh[CHAIN_WAVES][32];
   __shared__ uint32_t last_in_group, last_group;
   const uint32_t p = blockIdx.x, w = threadIdx.x >> 6;
@@ -203,7 +201,8 @@ k_plane_chain(const xyzz_st* __restrict__ part,
   if (!last_in_group) return;  // the whole block leaves
   __threadfence();
   acc = rxyzz_inf();
-  for (uint32_t i = w; i < gsize; i += CHAIN_WAVES) acc = rxyzz_add(acc, rxyzz_load_coherent(res + g0 + i), k);
+  for (uint32_t i = w; i < gsize; i += CHAIN_WAVES)
+    acc = rxyzz_add(acc, rxyzz_load_coherent(res + g0 + i), k);
   acc = block_row_sum(acc, w, sh, k);
   if (w == 0) {
     rxyzz_store(gres + grp, acc, k);
