@@ -113,7 +113,6 @@ Layout plan(size_t n, int c, int S) {
   L.halfs = take(2 * n * 16);
   L.pts2 = take(2 * n * sizeof(g1a));
   L.counts = take((size_t)L.K * 4);
-  L.offsets = take(((size_t)L.K + 1) * 4);
   L.rank = take((size_t)L.nwin * 2 * n * 4);  // rank of each (window, half-scalar) entry
   // counting-sort chunks: about 512 (chunk, window) blocks, chunks a multiple of 1024
   {
@@ -125,8 +124,11 @@ Layout plan(size_t n, int c, int S) {
     if (L.nchunk == 0) L.nchunk = 1;
   }
   L.hist_blk = take((size_t)L.nwin * L.nchunk * ((size_t)1 << (c - 1)) * 4);
-  L.poff = take((size_t)MAX_LEVELS * ((size_t)L.K + 1) * 4);  // pair offsets of every level
-  L.block_sums = take((size_t)MAX_LEVELS * (scan_blocks(L.K) + 1) * 4);
+  // bucket offsets, then the pair offsets of every level, K + 1 words each: one scan
+  // writes them all
+  L.offsets = take((size_t)(MAX_LEVELS + 1) * ((size_t)L.K + 1) * 4);
+  L.poff = L.offsets + ((size_t)L.K + 1) * 4;
+  L.block_sums = take((size_t)(MAX_LEVELS + 1) * (scan_blocks(L.K) + 1) * 4);
   L.sorted_idx = take(L.E_max * 4);
   const size_t region = off;
   L.aff_a = take(L.half * sizeof(g1a));
@@ -320,7 +322,10 @@ int run_pipeline(msm_ctx* ctx, const g1a* d_points, const uint32_t* d_scalars, s
   HIP_TRY(launch_fill((uint32_t*)stats, sizeof(msm_stats) / 4, 0, st));
   HIP_TRY(launch_glv_prep(d_points, d_scalars, n32, pts2, halfs, stats, verify, ctx->scalar_form, st));
   HIP_TRY(launch_hist(halfs, m32, c32, L.nwin, L.chunk, L.nchunk, hist_blk, counts, rank, stats, st));
-  HIP_TRY(launch_scan(counts, L.K, -1, 1, block_sums, offsets, L.K + 1, nullptr, st));
+  // bucket offsets (scan level -1) and, for the pair tree, the pair offsets of every level
+  // it can need (level l at poff + l (K + 1)) in one set of scan launches
+  HIP_TRY(launch_scan(counts, L.K, -1, 1 + (sched == MSM_SCHED_PAIR_TREE ? level_bound : 0),
+                      block_sums, offsets, (size_t)L.K + 1, &stats->max_count, st));
   HIP_TRY(hipMemcpyAsync(ctx->host_stats, stats, sizeof(msm_stats), hipMemcpyDeviceToHost, st));
   HIP_TRY(hipEventRecord(ctx->plan_ready, st));
   HIP_TRY(launch_scatter(halfs, m32, c32, L.nwin, L.chunk, L.nchunk, offsets, hist_blk, rank,
@@ -328,11 +333,7 @@ int run_pipeline(msm_ctx* ctx, const g1a* d_points, const uint32_t* d_scalars, s
   ph_sort.end();
   PhaseMark ph_acc(ctx, st, PH_ACCUM, tl);
   HIP_TRY(launch_bucket_init(counts, offsets, L.K, sorted_idx, pts, bsum, st));
-  // pair offsets of every level at once: level l at poff_all + l (K + 1)
   uint32_t* const poff_all = poff;
-  if (sched == MSM_SCHED_PAIR_TREE)
-    HIP_TRY(launch_scan(counts, L.K, 0, level_bound, block_sums, poff_all, (size_t)L.K + 1,
-                        &stats->max_count, st));
   HIP_TRY(hipEventRecord(ctx->done, st));
   ctx->has_done = true;
   HIP_TRY(hipEventSynchronize(ctx->plan_ready));
