@@ -316,40 +316,36 @@ __global__ void __launch_bounds__(256) k_scan_reduce(const uint32_t* __restrict_
   if (threadIdx.x == 0) block_sums[(size_t)blockIdx.y * (nb + 1) + blockIdx.x] = total;
 }
 
-// One block of 256 threads per level scans up to 256 * SCAN_TOP_ITEMS block sums in
-// place (exclusive) and stores the grand total at block_sums[nb].
-__global__ void __launch_bounds__(256) k_scan_top(uint32_t* block_sums_all, uint32_t nb, int level0,
-                                                  const uint32_t* max_count) {
-  __shared__ uint32_t lds[256];
-  if (!level_needed(level0 + (int)blockIdx.x, max_count)) return;
-  uint32_t* block_sums = block_sums_all + (size_t)blockIdx.x * (nb + 1);
-  uint32_t base = threadIdx.x * SCAN_TOP_ITEMS;
-  uint32_t v[SCAN_TOP_ITEMS];
-  uint32_t sum = 0;
-#pragma unroll
-  for (int e = 0; e < SCAN_TOP_ITEMS; e++) {
-    v[e] = (base + e < nb) ? block_sums[base + e] : 0u;
-    sum += v[e];
-  }
-  uint32_t total;
-  uint32_t run = block_exclusive_scan(sum, lds, &total);
-#pragma unroll
-  for (int e = 0; e < SCAN_TOP_ITEMS; e++) {
-    if (base + e < nb) block_sums[base + e] = run;
-    run += v[e];
-  }
-  if (threadIdx.x == 0) block_sums[nb] = total;
-}
-
+// Writes the exclusive prefixes of every tile: each block adds up the sums of the tiles
+// before it (nb <= SCAN_MAX_BLOCKS), and block 0 adds up all of them for the total.
 __global__ void __launch_bounds__(256) k_scan_down(const uint32_t* __restrict__ counts, uint32_t n,
                                                    int level0, const uint32_t* __restrict__ block_sums_all,
                                                    uint32_t nb, uint32_t* __restrict__ out_all,
                                                    size_t out_stride, const uint32_t* max_count) {
   __shared__ uint32_t lds[256];
+  __shared__ uint32_t wab[4][2];
   const int level = level0 + (int)blockIdx.y;
   if (!level_needed(level, max_count)) return;
   const uint32_t* block_sums = block_sums_all + (size_t)blockIdx.y * (nb + 1);
   uint32_t* out = out_all + (size_t)blockIdx.y * out_stride;
+  // the sums of tiles 0 .. blockIdx.x - 1 and of all nb tiles, over the block's threads
+  uint32_t a = 0, b = 0;
+#pragma unroll
+  for (uint32_t e = 0; e < SCAN_PRE_ITEMS; e++) {
+    const uint32_t i = threadIdx.x + 256u * e;
+    const uint32_t x = i < nb ? block_sums[i] : 0u;
+    a += i < blockIdx.x ? x : 0u;
+    b += x;
+  }
+  a = wave_sum(a);
+  b = wave_sum(b);
+  if ((threadIdx.x & 63u) == 0) {
+    wab[threadIdx.x >> 6][0] = a;
+    wab[threadIdx.x >> 6][1] = b;
+  }
+  __syncthreads();
+  const uint32_t pre = wab[0][0] + wab[1][0] + wab[2][0] + wab[3][0];
+  const uint32_t grand = wab[0][1] + wab[1][1] + wab[2][1] + wab[3][1];
   uint32_t base = blockIdx.x * SCAN_TILE + threadIdx.x * SCAN_ITEMS;
   uint32_t v[SCAN_ITEMS];
   uint32_t sum = 0;
@@ -359,13 +355,13 @@ __global__ void __launch_bounds__(256) k_scan_down(const uint32_t* __restrict__ 
     sum += v[e];
   }
   uint32_t total;
-  uint32_t run = block_exclusive_scan(sum, lds, &total) + block_sums[blockIdx.x];
+  uint32_t run = block_exclusive_scan(sum, lds, &total) + pre;
 #pragma unroll
   for (int e = 0; e < SCAN_ITEMS; e++) {
     if (base + e < n) out[base + e] = run;
     run += v[e];
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) out[n] = block_sums[nb];
+  if (blockIdx.x == 0 && threadIdx.x == 0) out[n] = grand;
 }
 
 __global__ void __launch_bounds__(256) k_bucket_init(const uint32_t* __restrict__ counts,
@@ -435,8 +431,8 @@ hipError_t launch_scan(const uint32_t* counts, uint32_t n, int level0, int nlev,
                        const uint32_t* max_count, hipStream_t s) {
   uint32_t nb = scan_blocks(n);
   if (nlev < 1) return hipSuccess;
+  if (nb > SCAN_MAX_BLOCKS) return hipErrorInvalidValue;  // K <= 2^18 buckets for c <= 16
   k_scan_reduce<<<dim3(nb, nlev), 256, 0, s>>>(counts, n, level0, block_sums, nb, max_count);
-  k_scan_top<<<nlev, 256, 0, s>>>(block_sums, nb, level0, max_count);
   k_scan_down<<<dim3(nb, nlev), 256, 0, s>>>(counts, n, level0, block_sums, nb, out, out_stride,
                                               max_count);
   return hipGetLastError();

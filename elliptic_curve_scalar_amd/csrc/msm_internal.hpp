@@ -10,8 +10,8 @@ namespace msmk {
 
 constexpr int SCAN_ITEMS = 4;                        // counts per thread in a scan tile
 constexpr uint32_t SCAN_TILE = 256 * SCAN_ITEMS;     // counts per scan block
-constexpr int SCAN_TOP_ITEMS = 16;                   // block sums per thread in the top scan
-constexpr uint32_t SCAN_MAX_BLOCKS = 256 * SCAN_TOP_ITEMS;
+constexpr uint32_t SCAN_PRE_ITEMS = 4;               // tile sums per thread of a down block
+constexpr uint32_t SCAN_MAX_BLOCKS = 256 * SCAN_PRE_ITEMS;  // tiles of one scan
 constexpr int MAX_LEVELS = 32;                       // pair-tree levels tracked
 constexpr uint32_t XYZZ_QUAD_MAX_PAIRS = 65536;      // XYZZ levels this small use 4 lanes per add
 
