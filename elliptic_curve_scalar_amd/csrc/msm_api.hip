@@ -227,6 +227,7 @@ struct msm_ctx {
   hipEvent_t plan_ready = nullptr;   // the plan's copy to host_stats has completed
   hipEvent_t done = nullptr;         // the last kernel of the previous call has run
   bool has_done = false;
+  hipStream_t done_stream = nullptr;  // the stream done was last recorded on
   void* noalloc_ws = nullptr;        // this device's fixed workspace of msm_run_noalloc
   // phase timing: 0 off, 1 the batched-affine level kernels only, 2 every phase
   int timing = 0;
@@ -243,7 +244,9 @@ namespace {
 size_t mark(msm_ctx* ctx, hipStream_t st) {
   if (ctx->ev_used == ctx->events.size()) {
     hipEvent_t e;
-    if (hipEventCreate(&e) != hipSuccess) return SIZE_MAX;
+    // timing only: no system-scope cache writeback when it is recorded, which would
+    // otherwise stall the kernel after it
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return SIZE_MAX;
     ctx->events.push_back(e);
   }
   size_t i = ctx->ev_used++;
@@ -281,12 +284,22 @@ int run_pipeline(msm_ctx* ctx, const g1a* d_points, const uint32_t* d_scalars, s
                  int S, int sched, int verify, char* ws, const Layout& L, hipStream_t st,
                  g1a* d_out, bool timed) {
   const int tl = timed ? ctx->timing : 0;
-  // calls on one context are ordered even across streams: wait for the previous one
-  if (ctx->has_done) HIP_TRY(hipStreamWaitEvent(st, ctx->done, 0));
+  // calls on one context are ordered even across streams: wait for the previous one (on
+  // the same stream, stream order already does)
+  if (ctx->has_done && ctx->done_stream != st) HIP_TRY(hipStreamWaitEvent(st, ctx->done, 0));
+  // marks the last kernel queued so far: at the end, and before an error return once
+  // kernels are queued
+  auto record_done = [&]() -> hipError_t {
+    hipError_t e = hipEventRecord(ctx->done, st);
+    if (e == hipSuccess) {
+      ctx->has_done = true;
+      ctx->done_stream = st;
+    }
+    return e;
+  };
   if (n == 0) {
     HIP_TRY(launch_fill((uint32_t*)d_out, sizeof(msm_g1_affine) / 4, 0, st));
-    HIP_TRY(hipEventRecord(ctx->done, st));
-    ctx->has_done = true;
+    HIP_TRY(record_done());
     return MSM_OK;
   }
   msm_stats* stats = (msm_stats*)(ws + L.stats);
@@ -334,10 +347,15 @@ int run_pipeline(msm_ctx* ctx, const g1a* d_points, const uint32_t* d_scalars, s
   PhaseMark ph_acc(ctx, st, PH_ACCUM, tl);
   HIP_TRY(launch_bucket_init(counts, offsets, L.K, sorted_idx, pts, bsum, st));
   uint32_t* const poff_all = poff;
-  HIP_TRY(hipEventRecord(ctx->done, st));
-  ctx->has_done = true;
-  HIP_TRY(hipEventSynchronize(ctx->plan_ready));
+  {
+    const hipError_t e = hipEventSynchronize(ctx->plan_ready);
+    if (e != hipSuccess) {
+      (void)record_done();
+      return fail(MSM_ERR_HIP, "HIP error: %s (waiting for the plan)", hipGetErrorString(e));
+    }
+  }
   const msm_stats hs = *ctx->host_stats;
+  if (hs.range_flag || hs.bad_point) HIP_TRY(record_done());
   if (hs.range_flag) return fail(MSM_ERR_RANGE, "GLV half-scalar out of bound (internal error)%s");
   if (hs.bad_point)
     return fail(MSM_ERR_OFF_CURVE, "an input point is not on the curve or not reduced below p%s");
@@ -418,7 +436,7 @@ int run_pipeline(msm_ctx* ctx, const g1a* d_points, const uint32_t* d_scalars, s
   HIP_TRY(launch_final(part, L.planes, res, gres, stats->join, d_out, st));
   ph_fin.end();
   if (verify) HIP_TRY(launch_verify_point(d_out, &stats->bad_out, st));
-  HIP_TRY(hipEventRecord(ctx->done, st));
+  HIP_TRY(record_done());
   if (tl) ctx->runs++;
   if (verify) {
     HIP_TRY(hipMemcpyAsync(&ctx->host_stats->bad_out, &stats->bad_out, 4, hipMemcpyDeviceToHost, st));
@@ -463,7 +481,10 @@ int msm_ctx_create(int device, msm_ctx** out) {
     ctx->d_result = nullptr;
     rc = fail(MSM_ERR_OOM, "device allocation failed%s");
   } else if (hipEventCreateWithFlags(&ctx->plan_ready, hipEventDisableTiming) != hipSuccess ||
-             hipEventCreateWithFlags(&ctx->done, hipEventDisableTiming) != hipSuccess) {
+             // device-scope release: it orders later calls' kernels and tells the host
+             // the workspace is free, and nothing on the host reads what came before it
+             hipEventCreateWithFlags(&ctx->done, hipEventDisableTiming | hipEventReleaseToDevice) !=
+                 hipSuccess) {
     rc = fail(MSM_ERR_HIP, "event creation failed%s");
   } else {
     // set-up of msm_run_noalloc: this device's copy of its fixed workspace; a failed
