@@ -155,6 +155,21 @@ Layout plan(size_t n, int c, int S) {
   return L;
 }
 
+// plan() of the last shape asked for on this thread (planning takes microseconds, which a
+// run would otherwise spend before its first launch, twice).
+Layout plan_cached(size_t n, int c, int S) {
+  thread_local Layout L;
+  thread_local size_t kn = SIZE_MAX;
+  thread_local int kc = 0, kS = 0;
+  if (n != kn || c != kc || S != kS) {
+    L = plan(n, c, S);
+    kn = n;
+    kc = c;
+    kS = S;
+  }
+  return L;
+}
+
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 int check_run_args(const msm_g1_affine* pts, const uint32_t* sc, size_t n, int c, int S,
@@ -458,7 +473,7 @@ size_t msm_workspace_bytes(size_t n, int c, int S) {
   if (c < 1 || c > 16 || n > MSM_MAX_N) return 0;
   if ((uint64_t)2 * n * (uint64_t)num_windows(c) >= ((uint64_t)1 << 32)) return 0;
   if (S != 4 && S != 8 && S != 16 && S != 32) return 0;
-  return plan(n, c, S).total;
+  return plan_cached(n, c, S).total;
 }
 
 int msm_ctx_create(int device, msm_ctx** out) {
@@ -519,7 +534,7 @@ int msm_run(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t* d_scala
   if (!ctx) return fail(MSM_ERR_ARG, "ctx is NULL%s");
   int rc = check_run_args(d_points, d_scalars, n, c, S, sched, verify, d_out);
   if (rc) return rc;
-  const Layout L = plan(n, c, S);
+  const Layout L = plan_cached(n, c, S);
   if (d_workspace && (workspace_bytes < L.total || !aligned(d_workspace, 256)))
     return fail(MSM_ERR_ARG, "workspace smaller than msm_workspace_bytes() or not 256-byte aligned%s");
   hipStream_t st = (hipStream_t)stream;
@@ -552,7 +567,7 @@ int msm_run_noalloc(msm_ctx* ctx, const msm_g1_affine* d_points, const uint32_t*
   if (!ctx) return fail(MSM_ERR_ARG, "ctx is NULL%s");
   int rc = check_run_args(d_points, d_scalars, n, c, S, sched, verify, d_out);
   if (rc) return rc;
-  const Layout L = plan(n, c, S);
+  const Layout L = plan_cached(n, c, S);
   if (L.total > NOALLOC_MAX_BYTES)
     return fail(MSM_ERR_ARG,
                 "msm_workspace_bytes(n, c, S) exceeds the fixed workspace of msm_run_noalloc "

@@ -131,6 +131,7 @@ class Context:
         _check(lib().msm_ctx_create(self.device.index, ctypes.byref(h)))
         self._h = h
         self._ws = None
+        self._need = {}  # workspace bytes per (n, c, S)
 
     def close(self):
         if getattr(self, "_h", None):
@@ -172,9 +173,13 @@ class Context:
         return {name: getattr(t, name) for name, _ in Timing._fields_}
 
     def workspace(self, n: int, c: int, S: int) -> torch.Tensor:
-        need = workspace_bytes(n, c, S)
-        if need == 0:
-            raise MsmError(MSM_ERR_ARG, "invalid n or c")
+        key = (n, c, S)
+        need = self._need.get(key)
+        if need is None:
+            need = workspace_bytes(n, c, S)
+            if need == 0:
+                raise MsmError(MSM_ERR_ARG, "invalid n or c")
+            self._need[key] = need
         if self._ws is None or self._ws.numel() < need + 256:
             self._ws = None  # the old block returns to the allocator, guarded by record_stream
             self._ws = torch.empty(need + 256, dtype=torch.uint8, device=self.device)
