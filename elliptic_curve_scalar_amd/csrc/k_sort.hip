@@ -177,9 +177,12 @@ __device__ __forceinline__ void block_stats(uint32_t cnt, msm_stats* st) {
     red[wave][MAX_LEVELS] = mx;
     red[wave][MAX_LEVELS + 1] = tot;
   }
+  // level l has no pair in this wave once 2^l reaches the wave's largest count (every
+  // bucket is down to one entry): only the levels below need a reduction
 #pragma unroll
   for (int l = 0; l < MAX_LEVELS; l++) {
-    const uint32_t v = wave_sum(level_count(cnt, l) >> 1);
+    uint32_t v = 0;
+    if (((uint64_t)1 << l) < mx) v = wave_sum(level_count(cnt, l) >> 1);
     if (lead) red[wave][l] = v;
   }
   __syncthreads();
