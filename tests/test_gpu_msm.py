@@ -372,3 +372,19 @@ def test_two_streams_growing_n():
     finally:
         torch.cuda.synchronize()
         ctx.close()
+
+
+def test_alternating_shapes_one_context():
+    """Shapes that alternate on one context (the layout plan is kept per shape, the
+    workspace only grows): every run matches the oracle."""
+    M = _msm()
+    ctx = M.Context(0)
+    try:
+        for n, c in ((3000, 13), (700, 13), (3000, 13), (700, 9), (3000, 13)):
+            w = wl.generate("n65536_c13", n=n)
+            pts = oracle.g1_from_scalars(w["dlogs"])
+            say("alternating shapes n", n, "c", c)
+            out = ctx.run(to_dev(pts), to_dev(w["scalars"]), c, 8)
+            assert np.array_equal(to_host(out), oracle.msm_pippenger(pts, w["scalars"], c)), (n, c)
+    finally:
+        ctx.close()
